@@ -1,0 +1,207 @@
+/*
+ * sfi.h -- C ABI of the MI355X (gfx950) decode-attention path of
+ * Slow-Fast Inference (SFI).
+ *
+ * What the calls compute (pages cited by title and section):
+ *
+ *  - sfi_slow_step: the slow step, dense attention of each query head over the
+ *    whole KV history of its sequence, which also records how much softmax
+ *    mass every position received ("Training-Free LLM Inference Acceleration
+ *    by Exploiting Attention Stability Within Sentences", section "How SFI
+ *    Works: Two Gears for Decoding"; "Slow-Fast Inference: Training-Free
+ *    Inference Acceleration via Within-Sentence Support Stability",
+ *    gist.science technical summary, 2.A "Das Slow-Fast Paradigma").
+ *  - sfi_select: the Selector, which fuses that evidence with a prior as the
+ *    mixture s = (1 - lambda) f + lambda r and keeps the top-k positions per
+ *    KV head (same summary, 2.B "Der Training-Free Selector").
+ *  - sfi_fast_step: the fast step, attention restricted to the sparse state:
+ *    sink tokens, the recent window and the selected memory (2.A, items 1-3).
+ *  - sfi_kv_append: grows the history by one token per sequence.
+ *  - sfi_sched_*: the host-side boundary scheduler that opens every span with
+ *    a slow step and can force a refresh after t_max fast steps (2.C
+ *    "Trigger-Policy"); span lengths are drawn from splitmix64.
+ *
+ * Conventions
+ *  - Every function returns an sfi_status (0 = SFI_OK, negative = error)
+ *    unless stated otherwise.  All arguments are validated before anything is
+ *    enqueued: on an error nothing is launched and no output is touched;
+ *    sfi_last_error() then holds a message (per calling thread).
+ *  - Pointers documented as "device" must point to device memory of the
+ *    current HIP device; "host" pointers are read during the call only.
+ *    The caller owns every buffer.  The library allocates no device memory.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued; nothing synchronises.  Asynchronous device faults surface at
+ *    the caller's next synchronisation.
+ *  - KV cache layout: K and V are [B][Hkv][T_cap][D] row-major, element type
+ *    kv_dtype.  Query head h reads KV head h / (Hq / Hkv).
+ *  - Queries q are [B][Hq][D] in kv_dtype.  Outputs are float32.
+ *  - Only the batch rows named in seq_ids (host array, distinct values in
+ *    [0, B)) are read or written by a call.
+ *  - Supported shapes: head_dim 64 or 128; Hq / Hkv in {1, 2, 4, 8};
+ *    kv_dtype SFI_F32 or SFI_BF16; 1 <= ctx_len[b] <= kv_capacity.
+ */
+#ifndef SFI_H_
+#define SFI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFI_VERSION_MAJOR 0
+#define SFI_VERSION_MINOR 1
+
+typedef enum {
+  SFI_OK = 0,
+  SFI_ERR_INVALID_ARG = -1, /* null pointer, bad shape, out-of-range id ... */
+  SFI_ERR_UNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  SFI_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  SFI_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
+  SFI_ERR_INJECTED = -5     /* failure forced by SFI_FAULT_INJECT (testing) */
+} sfi_status;
+
+typedef enum { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
+
+typedef enum { SFI_OP_SLOW = 0, SFI_OP_SELECT = 1, SFI_OP_FAST = 2 } sfi_op;
+
+/* One layer's KV cache and the current context lengths. */
+typedef struct {
+  int32_t batch;               /* B */
+  int32_t n_q_heads;           /* Hq */
+  int32_t n_kv_heads;          /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;            /* D: 64 or 128 */
+  int32_t kv_dtype;            /* sfi_dtype of K, V and q */
+  int64_t kv_capacity;         /* T_cap: rows allocated per (b, kv head) */
+  void* k;                     /* device [B][Hkv][T_cap][D]; read-only except sfi_kv_append */
+  void* v;                     /* device [B][Hkv][T_cap][D]; read-only except sfi_kv_append */
+  const int32_t* ctx_len_host; /* host [B]: valid rows of each sequence (T_b) */
+  float scale;                 /* logit scale; 0 selects 1/sqrt(D) */
+} sfi_kv_desc;
+
+/* The sparse state kept for fast steps: n_sink sink tokens, a recent window
+ * of n_recent tokens, and top_k selected tokens chosen by the Selector with
+ * mixture weight lambda in [0, 1].  Sinks, window and selected memory are
+ * disjoint; top_k counts only the selected memory. */
+typedef struct {
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t top_k;
+  float lambda;
+} sfi_support_params;
+
+/* Bytes of workspace `op` needs for this cache shape (the maximum over all
+ * context lengths up to kv_capacity and all batch rows).  `sp` may be NULL
+ * for SFI_OP_SLOW.  Returns 0 and sets sfi_last_error() on invalid input. */
+size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp, int32_t op);
+
+/* Prepares a freshly allocated workspace (device, ws_bytes) for use: clears
+ * the completion counters the fast step keeps there.  Call once after
+ * allocation; the kernels leave the counters cleared when they finish.
+ * Workspaces must not be shared by calls that may run concurrently. */
+int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Slow step (dense decode attention over the whole history).
+ *   q    : device [B][Hq][D], kv_dtype
+ *   out  : device float32 [B][Hq][D]; out[b][h] = sum_j p_hj v_j with
+ *          p_h = softmax_j(scale * q_h . k_j) over j < ctx_len[b]
+ *   mass : device float32 [B][Hkv][T_cap] or NULL.  When non-NULL, row
+ *          [b][g][j] for j < ctx_len[b] receives the softmax mass of position
+ *          j averaged over the query heads of KV head g (each row sums to 1);
+ *          the Selector's evidence.  Entries j >= ctx_len[b] are not written.
+ *   ws   : device workspace of at least sfi_workspace_bytes(desc, NULL, SFI_OP_SLOW). */
+int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int32_t n_seq,
+                      const void* q, float* out, float* mass, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Selector.  For each listed sequence b (context T = ctx_len[b]) and KV head
+ * g: candidates are positions [n_sink, T - n_recent) (n of them); candidate
+ * at 1-based offset a from the sinks gets the prior
+ *   r = (1/a + 1/(n + 1 - a)) / (2 H_n),   H_n = 1 + 1/2 + ... + 1/n,
+ * and the score s = (1 - lambda) * mass[b][g][j] + lambda * r, computed in
+ * float32.  The min(top_k, n) highest scores are kept, ties going to the
+ * lower position.
+ *   mass    : device float32 [B][Hkv][T_cap] (as written by sfi_slow_step)
+ *   sel_idx : device int32 [B][Hkv][top_k]; the kept positions in ascending
+ *             order, then -1 up to top_k
+ *   sel_cnt : device int32 [B][Hkv]; min(top_k, n) (0 when T <= n_sink + n_recent)
+ *   ws      : at least sfi_workspace_bytes(desc, sp, SFI_OP_SELECT) bytes. */
+int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                   const int32_t* seq_ids_host, int32_t n_seq, const float* mass,
+                   int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes, void* stream);
+
+/* Fast step (attention over the sparse state).  For sequence b at context
+ * length t = ctx_len[b], KV head g attends to
+ *   [0, min(n_sink, t))  u  [max(n_sink, t - n_recent), t)  u  sel_idx[b][g][0 : sel_cnt[b][g]]
+ * with the softmax renormalised over that support.
+ *   q, out           : as for sfi_slow_step
+ *   sel_idx, sel_cnt : device, as written by sfi_select.  Entries outside
+ *                      [0, t) and counts above min(top_k, n) are ignored.
+ *   ws               : at least sfi_workspace_bytes(desc, sp, SFI_OP_FAST)
+ *                      bytes, prepared once by sfi_workspace_init. */
+int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                      const int32_t* seq_ids_host, int32_t n_seq, const void* q,
+                      const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Appends one token per listed sequence: writes k_new[b][g][:] and
+ * v_new[b][g][:] (device [B][Hkv][D], kv_dtype) into row ctx_len[b] of
+ * desc->k and desc->v.  Requires ctx_len[b] < kv_capacity.  The caller then
+ * increments its ctx_len[b]. */
+int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int32_t n_seq,
+                      const void* k_new, const void* v_new, void* stream);
+
+/* Debug: writes the positions the fast-step kernel enumerates for each
+ * listed (b, g), in its own order, into support_out (device int32
+ * [B][Hkv][cap_per_head]), and their count into support_cnt (device int32
+ * [B][Hkv]).  Uses the same device index function as sfi_fast_step. */
+int32_t sfi_debug_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                          const int32_t* seq_ids_host, int32_t n_seq, const int32_t* sel_idx,
+                          const int32_t* sel_cnt, int32_t* support_out, int32_t* support_cnt,
+                          int32_t cap_per_head, void* stream);
+
+/* ---- host-side boundary scheduler (no device work) -------------------- */
+typedef struct sfi_sched sfi_sched;
+typedef enum { SFI_SPAN_FIXED = 0, SFI_SPAN_GEOMETRIC = 1 } sfi_span_mode;
+
+/* batch sequences; sequence b draws from splitmix64 started at seed + b.
+ * FIXED: every span has span_param steps (a positive integer).
+ * GEOMETRIC: span length = index of the first draw x < floor(2^64 / span_param),
+ * span_param in [1, 2^52).  t_max > 0 forces a slow step after t_max
+ * consecutive fast steps (0 = off). */
+int32_t sfi_sched_create(int32_t batch, uint64_t seed, int32_t mode, double span_param,
+                         int32_t t_max, sfi_sched** out);
+/* Advances every sequence by one decode step.  slow_ids / fast_ids (host,
+ * capacity batch each) receive the sequence ids, in increasing order. */
+int32_t sfi_sched_step(sfi_sched* s, int32_t* slow_ids, int32_t* n_slow, int32_t* fast_ids,
+                       int32_t* n_fast);
+/* The next step of sequence `seq` will be slow (e.g. after a failed select). */
+int32_t sfi_sched_force_slow(sfi_sched* s, int32_t seq);
+void sfi_sched_destroy(sfi_sched* s);
+
+/* ---- errors, version, kernel timing ------------------------------------ */
+const char* sfi_status_str(int32_t status);
+const char* sfi_last_error(void);
+int32_t sfi_version(void); /* MAJOR * 100 + MINOR */
+
+/* Kernel timing with HIP events recorded on the launch stream around each
+ * launch of the named kernel (off by default).  sfi_profile_read waits for
+ * the recorded events and returns the summed milliseconds and launch count
+ * since the last reset. */
+typedef enum {
+  SFI_K_SLOW_PARTIAL = 0, /* split-K dense partials (+ logit scratch) */
+  SFI_K_SLOW_COMBINE = 1, /* split merge + per-position mass */
+  SFI_K_SELECT = 2,       /* Selector */
+  SFI_K_FAST = 3,         /* sparse gather attention (+ fused merge) */
+  SFI_K_APPEND = 4,
+  SFI_K_COUNT = 5
+} sfi_kernel_id;
+int32_t sfi_profile_enable(int32_t on);
+int32_t sfi_profile_reset(void);
+int32_t sfi_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFI_H_ */

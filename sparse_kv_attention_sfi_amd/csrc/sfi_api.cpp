@@ -1,0 +1,572 @@
+// Host runtime and C ABI of the SFI decode-attention library: argument
+// validation, launch planning (split-K sizes, workgroup tables), workspace
+// layout, error reporting and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sfi_internal.hpp"
+
+namespace sfi {
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(SFI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (s == nullptr || *s == '\0') return dflt;
+  return std::atoi(s);
+}
+
+bool fault_injected(const char* op) {
+  const char* s = std::getenv("SFI_FAULT_INJECT");
+  return s != nullptr && std::strcmp(s, op) == 0;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int elem_bytes(int dtype) { return dtype == SFI_BF16 ? 2 : 4; }
+
+// ---- validation -------------------------------------------------------------
+int32_t check_desc(const sfi_kv_desc* d) {
+  if (d == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1) return fail(SFI_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(SFI_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(SFI_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SFI_ERR_UNSUPPORTED, "query group size %d not supported (1, 2, 4 or 8)", G);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SFI_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->kv_dtype != SFI_F32 && d->kv_dtype != SFI_BF16)
+    return fail(SFI_ERR_UNSUPPORTED, "kv_dtype %d not supported", d->kv_dtype);
+  if (d->kv_capacity < 1 || d->kv_capacity > (int64_t{1} << 30))
+    return fail(SFI_ERR_INVALID_ARG, "kv_capacity %lld out of range [1, 2^30]",
+                static_cast<long long>(d->kv_capacity));
+  if (!(std::isfinite(d->scale)) || d->scale < 0.f)
+    return fail(SFI_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  return SFI_OK;
+}
+
+int32_t check_kv(const sfi_kv_desc* d) {
+  if (d->k == nullptr || d->v == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->k / desc->v is NULL");
+  if (d->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
+  return SFI_OK;
+}
+
+int32_t check_seqs(const sfi_kv_desc* d, const int32_t* ids, int32_t n, bool need_ctx, int32_t min_ctx,
+                   int64_t max_ctx) {
+  if (n < 0) return fail(SFI_ERR_INVALID_ARG, "n_seq must be >= 0 (got %d)", n);
+  if (n == 0) return SFI_OK;
+  if (ids == nullptr) return fail(SFI_ERR_INVALID_ARG, "seq_ids_host is NULL");
+  std::vector<char> seen(static_cast<size_t>(d->batch), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = ids[i];
+    if (b < 0 || b >= d->batch) return fail(SFI_ERR_INVALID_ARG, "seq id %d out of range [0, %d)", b, d->batch);
+    if (seen[b]) return fail(SFI_ERR_INVALID_ARG, "seq id %d listed twice", b);
+    seen[b] = 1;
+    if (need_ctx) {
+      const int32_t t = d->ctx_len_host[b];
+      if (t < min_ctx || t > max_ctx)
+        return fail(SFI_ERR_INVALID_ARG, "ctx_len[%d] = %d out of range [%d, %lld]", b, t, min_ctx,
+                    static_cast<long long>(max_ctx));
+    }
+  }
+  return SFI_OK;
+}
+
+int32_t check_params(const sfi_support_params* sp) {
+  if (sp == nullptr) return fail(SFI_ERR_INVALID_ARG, "support params are NULL");
+  if (sp->n_sink < 0 || sp->n_recent < 0 || sp->top_k < 0)
+    return fail(SFI_ERR_INVALID_ARG, "n_sink, n_recent and top_k must be >= 0");
+  if (sp->top_k > (1 << 24)) return fail(SFI_ERR_INVALID_ARG, "top_k %d too large", sp->top_k);
+  if (!(sp->lambda >= 0.f && sp->lambda <= 1.f))
+    return fail(SFI_ERR_INVALID_ARG, "lambda must lie in [0, 1]");
+  return SFI_OK;
+}
+
+float logit_scale(const sfi_kv_desc* d) {
+  const float s = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
+  return s * 1.4426950408889634f;  // log2(e): the kernels use exp2
+}
+
+// ---- workspace layout -----------------------------------------------------
+// [ fast-step arrival counters | op scratch ]  The counter block sits at a
+// fixed offset so that slow, select and fast calls may share one workspace.
+size_t counter_bytes(const sfi_kv_desc* d) {
+  return align_up(static_cast<size_t>(d->batch) * d->n_kv_heads * sizeof(int32_t));
+}
+
+int slow_unit_rows(const sfi_kv_desc* d) {
+  return (kSlowThreads / 64) * block_rows(d->head_dim * elem_bytes(d->kv_dtype));
+}
+
+int slow_part_stride(const sfi_kv_desc* d) {
+  return static_cast<int>(ceil_div(d->kv_capacity, slow_unit_rows(d)));
+}
+
+struct SlowLayout {
+  size_t logits, part_ml, part_o, end;
+};
+SlowLayout slow_layout(const sfi_kv_desc* d) {
+  SlowLayout L;
+  const size_t heads = static_cast<size_t>(d->batch) * d->n_q_heads;
+  const size_t stride = static_cast<size_t>(slow_part_stride(d));
+  L.logits = counter_bytes(d);
+  L.part_ml = L.logits + align_up(heads * d->kv_capacity * sizeof(float));
+  L.part_o = L.part_ml + align_up(heads * stride * 2 * sizeof(float));
+  L.end = L.part_o + align_up(heads * stride * d->head_dim * sizeof(float));
+  return L;
+}
+
+int fast_part_stride(const sfi_support_params* sp) {
+  const int64_t rows = static_cast<int64_t>(sp->n_sink) + sp->n_recent + sp->top_k;
+  return static_cast<int>(std::max<int64_t>(1, ceil_div(rows, fast_chunk_rows())));
+}
+
+struct FastLayout {
+  size_t part_ml, part_o, end;
+};
+FastLayout fast_layout(const sfi_kv_desc* d, const sfi_support_params* sp) {
+  FastLayout L;
+  const size_t heads = static_cast<size_t>(d->batch) * d->n_q_heads;
+  const size_t stride = static_cast<size_t>(fast_part_stride(sp));
+  L.part_ml = counter_bytes(d);
+  L.part_o = L.part_ml + align_up(heads * stride * 2 * sizeof(float));
+  L.end = L.part_o + align_up(heads * stride * d->head_dim * sizeof(float));
+  return L;
+}
+
+int32_t check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return SFI_OK;
+  if (ws == nullptr) return fail(SFI_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (have < need) return fail(SFI_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return SFI_OK;
+}
+
+// ---- event timing ---------------------------------------------------------
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[SFI_K_COUNT];
+  std::vector<hipEvent_t> pool;
+  double ms[SFI_K_COUNT] = {};
+  int64_t launches[SFI_K_COUNT] = {};
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+
+hipEvent_t take_event(Prof& p) {
+  if (!p.pool.empty()) {
+    hipEvent_t e = p.pool.back();
+    p.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returning hipError_t) between two recorded events when timing is on.
+template <typename F>
+hipError_t timed(int kid, hipStream_t s, F&& launch) {
+  Prof& p = prof();
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(p.mu);
+    on = p.on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(p.mu);
+    a = take_event(p);
+    b = take_event(p);
+  }
+  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.pending[kid].emplace_back(a, b);
+  return hipSuccess;
+}
+
+// ---- launch tables --------------------------------------------------------
+// Splits the id list into groups of at most kMaxSeqPerLaunch.
+template <typename F>
+int32_t for_each_group(const int32_t* ids, int32_t n, F&& f) {
+  for (int32_t i0 = 0; i0 < n; i0 += kMaxSeqPerLaunch) {
+    const int32_t cnt = std::min<int32_t>(kMaxSeqPerLaunch, n - i0);
+    const int32_t st = f(ids + i0, cnt);
+    if (st != SFI_OK) return st;
+  }
+  return SFI_OK;
+}
+
+}  // namespace
+}  // namespace sfi
+
+using namespace sfi;
+
+extern "C" {
+
+int32_t sfi_version(void) { return SFI_VERSION_MAJOR * 100 + SFI_VERSION_MINOR; }
+
+const char* sfi_status_str(int32_t st) {
+  switch (st) {
+    case SFI_OK: return "SFI_OK";
+    case SFI_ERR_INVALID_ARG: return "SFI_ERR_INVALID_ARG";
+    case SFI_ERR_UNSUPPORTED: return "SFI_ERR_UNSUPPORTED";
+    case SFI_ERR_WORKSPACE: return "SFI_ERR_WORKSPACE";
+    case SFI_ERR_HIP: return "SFI_ERR_HIP";
+    case SFI_ERR_INJECTED: return "SFI_ERR_INJECTED";
+    default: return "SFI_ERR_UNKNOWN";
+  }
+}
+
+const char* sfi_last_error(void) { return g_last_error.c_str(); }
+
+size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp, int32_t op) {
+  if (check_desc(desc) != SFI_OK) return 0;
+  switch (op) {
+    case SFI_OP_SLOW: return slow_layout(desc).end;
+    case SFI_OP_SELECT:
+      if (check_params(sp) != SFI_OK) return 0;
+      return counter_bytes(desc);
+    case SFI_OP_FAST:
+      if (check_params(sp) != SFI_OK) return 0;
+      return fast_layout(desc, sp).end;
+    default: fail(SFI_ERR_INVALID_ARG, "unknown op %d", op); return 0;
+  }
+}
+
+int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws == nullptr || ws_bytes == 0) return SFI_OK;
+  const hipError_t e = launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SFI_OK : hip_fail(e, "workspace init");
+}
+
+int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n_seq, const void* q, float* out,
+                      float* mass, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_kv(desc)) != SFI_OK) return st;
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (n_seq == 0) return SFI_OK;
+  if (q == nullptr || out == nullptr) return fail(SFI_ERR_INVALID_ARG, "q / out is NULL");
+  const SlowLayout L = slow_layout(desc);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int unit = slow_unit_rows(desc);
+  const int target = std::max(64, env_int("SFI_SLOW_TARGET_WGS", 1024));
+  char* w = static_cast<char*>(ws);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    SlowArgs a{};
+    a.k = desc->k;
+    a.v = desc->v;
+    a.q = q;
+    a.logits = mass ? reinterpret_cast<float*>(w + L.logits) : nullptr;
+    a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+    a.part_o = reinterpret_cast<float*>(w + L.part_o);
+    a.out = out;
+    a.mass = mass;
+    a.t_cap = desc->kv_capacity;
+    a.n_q_heads = desc->n_q_heads;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.part_stride = slow_part_stride(desc);
+    a.scale_log2 = logit_scale(desc);
+    int64_t rows = 0;
+    for (int i = 0; i < cnt; ++i) rows += static_cast<int64_t>(desc->ctx_len_host[ids[i]]) * desc->n_kv_heads;
+    const int64_t per = ceil_div(rows, target);
+    a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
+    CombineArgs c{};
+    a.tab.n = cnt;
+    a.tab.wg_begin[0] = 0;
+    c.tab.wg_begin[0] = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const int b = ids[i];
+      const int T = desc->ctx_len_host[b];
+      a.tab.seq[i] = b;
+      a.tab.ctx[i] = T;
+      a.tab.nsplit[i] = static_cast<int32_t>(ceil_div(T, a.split_rows));
+      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+      c.mass_blocks[i] = mass ? static_cast<int32_t>(ceil_div(T, kMassChunk)) : 0;
+      c.tab.seq[i] = b;
+      c.tab.ctx[i] = T;
+      c.tab.nsplit[i] = a.tab.nsplit[i];
+      c.tab.wg_begin[i + 1] = c.tab.wg_begin[i] + desc->n_kv_heads * (c.mass_blocks[i] + G);
+    }
+    c.tab.n = cnt;
+    c.logits = a.logits;
+    c.part_ml = a.part_ml;
+    c.part_o = a.part_o;
+    c.out = out;
+    c.mass = mass;
+    c.t_cap = a.t_cap;
+    c.n_q_heads = a.n_q_heads;
+    c.n_kv_heads = a.n_kv_heads;
+    c.part_stride = a.part_stride;
+    hipError_t e = timed(SFI_K_SLOW_PARTIAL, s, [&] {
+      return launch_slow_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "slow partial launch");
+    e = timed(SFI_K_SLOW_COMBINE, s,
+              [&] { return launch_slow_combine(c, desc->head_dim, G, c.tab.wg_begin[cnt], s); });
+    if (e != hipSuccess) return hip_fail(e, "slow combine launch");
+    return SFI_OK;
+  });
+}
+
+int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids, int32_t n_seq,
+                   const float* mass, int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_params(sp)) != SFI_OK) return st;
+  if (desc->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (fault_injected("select")) return fail(SFI_ERR_INJECTED, "select failure forced by SFI_FAULT_INJECT");
+  if (n_seq == 0) return SFI_OK;
+  if (mass == nullptr || sel_idx == nullptr || sel_cnt == nullptr)
+    return fail(SFI_ERR_INVALID_ARG, "mass / sel_idx / sel_cnt is NULL");
+  (void)ws;
+  (void)ws_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    SelectArgs a{};
+    a.mass = mass;
+    a.sel_idx = sel_idx;
+    a.sel_cnt = sel_cnt;
+    a.t_cap = desc->kv_capacity;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.n_sink = sp->n_sink;
+    a.n_recent = sp->n_recent;
+    a.top_k = sp->top_k;
+    a.lambda = sp->lambda;
+    a.tab.n = cnt;
+    for (int i = 0; i < cnt; ++i) {
+      a.tab.seq[i] = ids[i];
+      a.tab.ctx[i] = desc->ctx_len_host[ids[i]];
+      a.tab.nsplit[i] = 1;
+      a.tab.wg_begin[i] = i * desc->n_kv_heads;
+    }
+    a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;
+    const hipError_t e = timed(SFI_K_SELECT, s, [&] { return launch_select(a, cnt * desc->n_kv_heads, s); });
+    return e == hipSuccess ? SFI_OK : hip_fail(e, "select launch");
+  });
+}
+
+int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids, int32_t n_seq,
+                      const void* q, const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_kv(desc)) != SFI_OK) return st;
+  if ((st = check_params(sp)) != SFI_OK) return st;
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (n_seq == 0) return SFI_OK;
+  if (q == nullptr || out == nullptr || sel_idx == nullptr || sel_cnt == nullptr)
+    return fail(SFI_ERR_INVALID_ARG, "q / out / sel_idx / sel_cnt is NULL");
+  if (sp->n_sink == 0 && sp->n_recent == 0 && sp->top_k == 0)
+    return fail(SFI_ERR_INVALID_ARG, "the support is empty (n_sink = n_recent = top_k = 0)");
+  const FastLayout L = fast_layout(desc, sp);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int crow = fast_chunk_rows();
+  char* w = static_cast<char*>(ws);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    FastArgs a{};
+    a.k = desc->k;
+    a.v = desc->v;
+    a.q = q;
+    a.sel_idx = sel_idx;
+    a.sel_cnt = sel_cnt;
+    a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+    a.part_o = reinterpret_cast<float*>(w + L.part_o);
+    a.counter = reinterpret_cast<int32_t*>(w);
+    a.out = out;
+    a.t_cap = desc->kv_capacity;
+    a.n_q_heads = desc->n_q_heads;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.n_sink = sp->n_sink;
+    a.n_recent = sp->n_recent;
+    a.top_k = sp->top_k;
+    a.chunk_rows = crow;
+    a.part_stride = fast_part_stride(sp);
+    a.scale_log2 = logit_scale(desc);
+    a.tab.n = cnt;
+    a.tab.wg_begin[0] = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const int b = ids[i];
+      const int64_t t = desc->ctx_len_host[b];
+      const int64_t ns_eff = std::min<int64_t>(sp->n_sink, t);
+      const int64_t w_lo = std::max<int64_t>(sp->n_sink, t - sp->n_recent);
+      const int64_t w_eff = std::max<int64_t>(0, t - w_lo);
+      const int64_t n = std::max<int64_t>(0, t - sp->n_sink - sp->n_recent);
+      const int64_t smax = ns_eff + w_eff + std::min<int64_t>(sp->top_k, n);
+      a.tab.seq[i] = b;
+      a.tab.ctx[i] = static_cast<int32_t>(t);
+      a.tab.nsplit[i] = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(smax, crow)));
+      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+    }
+    const hipError_t e = timed(SFI_K_FAST, s, [&] {
+      return launch_fast(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
+    });
+    return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
+  });
+}
+
+int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n_seq, const void* k_new,
+                      const void* v_new, void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_kv(desc)) != SFI_OK) return st;
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 0, desc->kv_capacity - 1)) != SFI_OK) return st;
+  if (n_seq == 0) return SFI_OK;
+  if (k_new == nullptr || v_new == nullptr) return fail(SFI_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    AppendArgs a{};
+    a.k = desc->k;
+    a.v = desc->v;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.t_cap = desc->kv_capacity;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.tab.n = cnt;
+    for (int i = 0; i < cnt; ++i) {
+      a.tab.seq[i] = ids[i];
+      a.tab.ctx[i] = desc->ctx_len_host[ids[i]];
+      a.tab.nsplit[i] = 1;
+      a.tab.wg_begin[i] = i * desc->n_kv_heads;
+    }
+    a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;
+    const hipError_t e = timed(SFI_K_APPEND, s, [&] {
+      return launch_append(a, desc->kv_dtype, desc->head_dim, cnt * desc->n_kv_heads, s);
+    });
+    return e == hipSuccess ? SFI_OK : hip_fail(e, "append launch");
+  });
+}
+
+int32_t sfi_debug_support(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                          int32_t n_seq, const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* support_out,
+                          int32_t* support_cnt, int32_t cap_per_head, void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_params(sp)) != SFI_OK) return st;
+  if (desc->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (n_seq == 0) return SFI_OK;
+  if (sel_idx == nullptr || sel_cnt == nullptr || support_out == nullptr || support_cnt == nullptr)
+    return fail(SFI_ERR_INVALID_ARG, "NULL buffer");
+  if (cap_per_head < 1) return fail(SFI_ERR_INVALID_ARG, "cap_per_head must be >= 1");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    SupportArgs a{};
+    a.sel_idx = sel_idx;
+    a.sel_cnt = sel_cnt;
+    a.support_out = support_out;
+    a.support_cnt = support_cnt;
+    a.t_cap = desc->kv_capacity;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.n_sink = sp->n_sink;
+    a.n_recent = sp->n_recent;
+    a.top_k = sp->top_k;
+    a.cap_per_head = cap_per_head;
+    a.tab.n = cnt;
+    for (int i = 0; i < cnt; ++i) {
+      a.tab.seq[i] = ids[i];
+      a.tab.ctx[i] = desc->ctx_len_host[ids[i]];
+      a.tab.nsplit[i] = 1;
+      a.tab.wg_begin[i] = i * desc->n_kv_heads;
+    }
+    a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;
+    const hipError_t e = launch_support(a, cnt * desc->n_kv_heads, s);
+    return e == hipSuccess ? SFI_OK : hip_fail(e, "support launch");
+  });
+}
+
+int32_t sfi_profile_enable(int32_t on) {
+  Prof& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = on != 0;
+  return SFI_OK;
+}
+
+static int32_t drain_profile(Prof& p) {
+  for (int k = 0; k < SFI_K_COUNT; ++k) {
+    for (auto& pr : p.pending[k]) {
+      hipError_t e = hipEventSynchronize(pr.second);
+      if (e != hipSuccess) return hip_fail(e, "profile event sync");
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, pr.first, pr.second);
+      if (e != hipSuccess) return hip_fail(e, "profile elapsed time");
+      p.ms[k] += ms;
+      p.launches[k] += 1;
+      p.pool.push_back(pr.first);
+      p.pool.push_back(pr.second);
+    }
+    p.pending[k].clear();
+  }
+  return SFI_OK;
+}
+
+int32_t sfi_profile_reset(void) {
+  Prof& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  const int32_t st = drain_profile(p);
+  for (int k = 0; k < SFI_K_COUNT; ++k) {
+    p.ms[k] = 0.0;
+    p.launches[k] = 0;
+  }
+  return st;
+}
+
+int32_t sfi_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= SFI_K_COUNT) return fail(SFI_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+  if (total_ms == nullptr || launches == nullptr) return fail(SFI_ERR_INVALID_ARG, "NULL output");
+  Prof& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  const int32_t st = drain_profile(p);
+  if (st != SFI_OK) return st;
+  *total_ms = p.ms[kernel];
+  *launches = p.launches[kernel];
+  return SFI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,732 @@
+// Decode-attention kernels of the SFI path for gfx950 (CDNA4).
+//
+//  * slow_partial: split-K flash-decode over the whole KV history (the slow
+//    step's dense attention: "Slow-Fast Inference ...", gist.science
+//    technical summary, 2.A).  Each workgroup streams one contiguous chunk of
+//    K and V rows of one KV head exactly once and keeps the online-softmax
+//    state (running max, running sum, un-normalised output) of the G query
+//    heads that share the KV head.  It also stores the scaled logits so the
+//    merge kernel can turn them into per-position softmax mass.
+//  * slow_combine: merges the split partials into the output and writes the
+//    Selector's evidence, the softmax mass averaged over the query group
+//    (2.B "Der Training-Free Selector").
+//  * fast: attention restricted to sinks + recent window + selected memory
+//    (2.A, items 1-3), gathering K/V rows by index; the last workgroup of each
+//    (sequence, KV head) merges the chunk partials.
+//
+// Work layout inside a wave (64 lanes), per 16-row tile of K:
+//   logits   S[h][j] = q_h . k_j come from MFMA 16x16 (bf16: 16x16x32,
+//            fp32: 16x16x4) with the query heads on M (padded to 16) and the
+//            16 rows on N.  Lane l loads 16 bytes of row (l % 16) at byte
+//            offset 64 * kk + 16 * (l / 16); lanes 0..15 receive the G <= 4
+//            logits of their row (lanes 16..31 heads 4..7 when G = 8).
+//   softmax  per-head block max over the tile rows with DPP row reductions,
+//            exp2 in the log2 domain, probabilities staged in LDS.
+//   P.V      VALU FMAs: lane l owns one 16-byte piece of V rows
+//            (l / PPR) + RPL * i, so every V load instruction reads whole
+//            rows contiguously; partial outputs are reduced across lanes once
+//            at the end.
+#include <math.h>
+
+#include <algorithm>
+
+#include "sfi_device.hpp"
+#include "sfi_internal.hpp"
+
+namespace sfi {
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename E, int D, int G>
+struct Attn {
+  static constexpr int kEsz = Elem<E>::kBytes;
+  static constexpr int kEpp = Elem<E>::kPerPiece;  // elements per 16-byte piece
+  static constexpr int kRowBytes = D * kEsz;
+  static constexpr int kNL = kRowBytes / 64;       // K pieces per lane per tile
+  static constexpr int kPPR = kRowBytes / 16;      // pieces per row
+  static constexpr int kRPL = 64 / kPPR;           // rows per V load instruction
+  static constexpr int kGroups = (G + 3) / 4;      // 16-lane groups holding logits
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  static_assert(kNL >= 1 && kRPL >= 1, "row size");
+
+  float m_run[G];     // running max per head (wave-uniform), log2 domain
+  float l_lane[4];    // per-lane partial softmax sums, head 4 * (lane / 16) + e
+  float acc[G][kEpp]; // per-lane un-normalised output piece
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m_run[h] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kEpp; ++i) acc[h][i] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l_lane[e] = 0.f;
+  }
+
+  // Value of per-head array x for the head this lane's item e belongs to.
+  __device__ __forceinline__ static float for_item(const float (&x)[G], int lane, int e) {
+    if constexpr (G <= 4) {
+      return x[e < G ? e : 0];
+    } else {
+      return (lane & 16) ? x[4 + e] : x[e];
+    }
+  }
+
+  // Consume one block of TILES * 16 rows.
+  //   kb[t][kk] : K pieces in MFMA layout (row 16 t + lane % 16)
+  //   vb[i]     : V pieces in row layout (row lane / PPR + RPL * i)
+  //   kvalid[t] : row 16 t + lane % 16 exists
+  //   Pw        : this wave's LDS staging area, TILES * 16 * G floats
+  //   logit_row : if non-null, logits of row 16 t + lane % 16 of head h go to
+  //               logit_row[h * head_stride + 16 t]
+  template <int TILES>
+  __device__ __forceinline__ void consume(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
+                                          const uint4 (&vb)[TILES * 16 / kRPL],
+                                          const bool (&kvalid)[TILES], float* Pw, float scale_log2,
+                                          float* logit_row, int64_t head_stride, int lane) {
+    constexpr int NV = TILES * 16 / kRPL;
+    // logits
+    float x[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kNL; ++kk) c = mfma_piece(E(), qa[kk], kb[t][kk], c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[t][e] = kvalid[t] ? c[e] * scale_log2 : -INFINITY;
+    }
+    const int grp = lane >> 4;
+    if (logit_row != nullptr && grp < kGroups) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        if (!kvalid[t]) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = 4 * grp + e;
+          if (h < G) logit_row[h * head_stride + 16 * t] = x[t][e];
+        }
+      }
+    }
+    // block max per head, new running max, rescale factors (wave-uniform)
+    float mx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = x[0][e];
+#pragma unroll
+      for (int t = 1; t < TILES; ++t) v = fmaxf(v, x[t][e]);
+      mx[e] = row16_max(v);
+    }
+    float m_new[G], alpha[G];
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float bm = lane_bcast(mx[h & 3], 16 * (h >> 2));
+      m_new[h] = fmaxf(m_run[h], bm);
+      alpha[h] = (m_new[h] == m_run[h]) ? 1.f : fast_exp2(m_run[h] - m_new[h]);
+      rescale |= (alpha[h] != 1.f);
+    }
+    // probabilities relative to the new max
+    float p[TILES][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mn = for_item(m_new, lane, e);
+      const float al = for_item(alpha, lane, e);
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        p[t][e] = fast_exp2(x[t][e] - mn);
+        s += p[t][e];
+      }
+      l_lane[e] = l_lane[e] * al + s;
+    }
+    // stage P in LDS: row r, head h at Pw[r * G + h]
+    wave_sync();
+    if (grp < kGroups) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        float* dst = Pw + (16 * t + (lane & 15)) * G;
+        if constexpr (G >= 4) {
+          *reinterpret_cast<float4*>(dst + 4 * grp) = make_float4(p[t][0], p[t][1], p[t][2], p[t][3]);
+        } else if constexpr (G == 2) {
+          *reinterpret_cast<float2*>(dst) = make_float2(p[t][0], p[t][1]);
+        } else {
+          dst[0] = p[t][0];
+        }
+      }
+    }
+    wave_sync();
+    if (rescale) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < kEpp; ++i) acc[h][i] *= alpha[h];
+    }
+    // P.V
+    const int rr = lane / kPPR;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float* src = Pw + (rr + kRPL * i) * G;
+      float pr[G];
+      if constexpr (G >= 4) {
+#pragma unroll
+        for (int h4 = 0; h4 < G; h4 += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(src + h4);
+          pr[h4] = v4.x; pr[h4 + 1] = v4.y; pr[h4 + 2] = v4.z; pr[h4 + 3] = v4.w;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) pr[h] = src[h];
+      }
+      float vf[kEpp];
+      widen(E(), vb[i], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int d = 0; d < kEpp; ++d) acc[h][d] = fmaf(pr[h], vf[d], acc[h][d]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_run[h] = m_new[h];
+  }
+
+  // Reduce this wave's state and store it in LDS slot `w`:
+  //   sm[w * G + h], sl[w * G + h], so[(w * G + h) * D + d].
+  __device__ __forceinline__ void finish_wave(float* sm, float* sl, float* so, int w, int lane) {
+    float lt[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = row16_sum(l_lane[h & 3]);
+      lt[h] = lane_bcast(v, 16 * (h >> 2));
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int d = 0; d < kEpp; ++d) {
+        float v = acc[h][d];
+#pragma unroll
+        for (int m = kPPR; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+        acc[h][d] = v;
+      }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm[w * G + h] = m_run[h];
+        sl[w * G + h] = lt[h];
+      }
+    }
+    if (lane < kPPR) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int d = 0; d < kEpp; ++d) so[(w * G + h) * D + lane * kEpp + d] = acc[h][d];
+    }
+  }
+};
+
+// Merge NW wave states from LDS into one (max, sum, output) per head and store
+// it to the global partial slot: ml[h * ml_stride] = (m, l),
+// o[h * o_stride + d].  Called by all threads of the workgroup after a barrier.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_waves_to_global(const float* sm, const float* sl, const float* so,
+                                                      float* ml, int64_t ml_stride, float* o,
+                                                      int64_t o_stride, int tid, int nthreads) {
+  for (int idx = tid; idx < G * D; idx += nthreads) {
+    const int h = idx / D, d = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * G + h]);
+    float acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm[w * G + h];
+        if (mw != -INFINITY) acc += so[(w * G + h) * D + d] * fast_exp2(mw - M);
+      }
+    }
+    o[h * o_stride + d] = acc;
+    if (d == 0) {
+      float L = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float mw = sm[w * G + h];
+          if (mw != -INFINITY) L += sl[w * G + h] * fast_exp2(mw - M);
+        }
+      }
+      ml[h * ml_stride] = M;
+      ml[h * ml_stride + 1] = L;
+    }
+  }
+}
+
+// Load the query pieces of KV head g's query group in MFMA operand-A layout.
+template <typename E, int D, int G>
+__device__ __forceinline__ void load_q(const void* q, int64_t q_row0, int lane,
+                                       uint4 (&qa)[Attn<E, D, G>::kNL]) {
+  using A = Attn<E, D, G>;
+  const int h = lane & 15;
+  const char* base = static_cast<const char*>(q) + (q_row0 + (h < G ? h : 0)) * A::kRowBytes;
+#pragma unroll
+  for (int kk = 0; kk < A::kNL; ++kk) {
+    if (h < G) {
+      qa[kk] = ld16(base + 64 * kk + 16 * (lane >> 4));
+    } else {
+      qa[kk] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// slow step, kernel 1: split-K partials
+// ---------------------------------------------------------------------------
+template <typename E, int D, int G>
+__global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) {
+  using A = Attn<E, D, G>;
+  constexpr int RB = A::kRowBytes;
+  constexpr int ROWS = block_rows(RB);
+  constexpr int TILES = ROWS / 16;
+  constexpr int NV = ROWS / A::kRPL;
+  constexpr int NW = kSlowThreads / 64;
+
+  __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
+  __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
+  __shared__ float s_m[NW * G], s_l[NW * G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wg = blockIdx.x;
+  const int e = find_entry(a.tab, wg);
+  const int local = wg - a.tab.wg_begin[e];
+  const int nsplit = a.tab.nsplit[e];
+  const int g = local / nsplit;
+  const int split = local - g * nsplit;
+  const int b = a.tab.seq[e];
+  const int T = a.tab.ctx[e];
+  const int r_begin = split * a.split_rows;
+  const int r_end = min(T, r_begin + a.split_rows);
+
+  const int64_t kv_row0 = (static_cast<int64_t>(b) * a.n_kv_heads + g) * a.t_cap;
+  const char* Kb = static_cast<const char*>(a.k) + kv_row0 * RB;
+  const char* Vb = static_cast<const char*>(a.v) + kv_row0 * RB;
+  const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
+
+  uint4 qa[A::kNL];
+  load_q<E, D, G>(a.q, qh0, lane, qa);
+
+  A st;
+  st.init();
+  float* Pw = s_p + wave * ROWS * G;
+  const int kr = lane & 15, kg = lane >> 4;
+  const int vr = lane / A::kPPR, vp = lane % A::kPPR;
+
+  for (int r0 = r_begin + wave * ROWS; r0 < r_end; r0 += NW * ROWS) {
+    uint4 kb[TILES][A::kNL];
+    uint4 vb[NV];
+    bool kvalid[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int row = r0 + 16 * t + kr;
+      kvalid[t] = row < r_end;
+      const char* src = Kb + static_cast<int64_t>(kvalid[t] ? row : r_end - 1) * RB + 16 * kg;
+#pragma unroll
+      for (int kk = 0; kk < A::kNL; ++kk) kb[t][kk] = ld16(src + 64 * kk);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int row = min(r0 + vr + A::kRPL * i, r_end - 1);
+      vb[i] = ld16(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
+    }
+    float* lrow = a.logits ? a.logits + qh0 * a.t_cap + r0 + kr : nullptr;
+    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lrow, a.t_cap, lane);
+  }
+  st.finish_wave(s_m, s_l, s_o, wave, lane);
+  __syncthreads();
+  const int64_t slot = qh0 * a.part_stride + split;
+  merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
+                                  static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
+                                  static_cast<int64_t>(a.part_stride) * D, threadIdx.x, kSlowThreads);
+}
+
+// ---------------------------------------------------------------------------
+// slow step, kernel 2: merge partials; per-position softmax mass
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineArgs a) {
+  constexpr int NW = kCombineThreads / 64;
+  __shared__ float s_M[G], s_invL[G];
+  __shared__ float s_red[kCombineThreads];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wg = blockIdx.x;
+  const int e = find_entry(a.tab, wg);
+  const int local = wg - a.tab.wg_begin[e];
+  const int mblocks = a.mass_blocks[e];
+  const int per_g = mblocks + G;
+  const int g = local / per_g;
+  const int r = local - g * per_g;
+  const int b = a.tab.seq[e];
+  const int T = a.tab.ctx[e];
+  const int nsplit = a.tab.nsplit[e];
+  const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
+
+  // global max and sum of each head of the group over all splits
+  for (int h = wave; h < G; h += NW) {
+    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
+    float m = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, ml[2 * s]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float ms = ml[2 * s];
+      if (ms != -INFINITY) l += ml[2 * s + 1] * fast_exp2(ms - m);
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      s_M[h] = m;
+      s_invL[h] = 1.f / l;
+    }
+  }
+  __syncthreads();
+
+  if (r < mblocks) {
+    const int j0 = r * kMassChunk;
+    const int j1 = min(T, j0 + kMassChunk);
+    const float* lg = a.logits + qh0 * a.t_cap;
+    float* mrow = a.mass + (static_cast<int64_t>(b) * a.n_kv_heads + g) * a.t_cap;
+    const float invG = 1.f / static_cast<float>(G);
+    for (int j = j0 + tid; j < j1; j += kCombineThreads) {
+      float f = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) f += fast_exp2(lg[h * a.t_cap + j] - s_M[h]) * s_invL[h];
+      mrow[j] = f * invG;
+    }
+  } else {
+    const int h = r - mblocks;
+    constexpr int NSUB = kCombineThreads / D;
+    const int d = tid % D, sub = tid / D;
+    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
+    const float* po = a.part_o + (qh0 + h) * a.part_stride * D;
+    const float M = s_M[h];
+    float acc = 0.f;
+    for (int s = sub; s < nsplit; s += NSUB) {
+      const float ms = ml[2 * s];
+      if (ms != -INFINITY) acc += po[static_cast<int64_t>(s) * D + d] * fast_exp2(ms - M);
+    }
+    s_red[tid] = acc;
+    __syncthreads();
+    if (sub == 0) {
+      float o = 0.f;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) o += s_red[u * D + d];
+      a.out[(qh0 + h) * D + d] = o * s_invL[h];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fast step: gathered sparse attention with a last-workgroup merge
+// ---------------------------------------------------------------------------
+struct SupportGeom {
+  int ns_eff, w_lo, w_eff, cnt, size;
+};
+
+// Support of KV head row `bg` at context t: [0, ns_eff) sinks, then the window
+// [w_lo, w_lo + w_eff), then sel_idx[0 : cnt].
+__device__ __forceinline__ SupportGeom support_geom(int t, int n_sink, int n_recent, int top_k,
+                                                    const int32_t* sel_cnt, int64_t bg) {
+  SupportGeom s;
+  s.ns_eff = min(n_sink, t);
+  s.w_lo = max(n_sink, t - n_recent);
+  s.w_eff = max(0, t - s.w_lo);
+  const int n = max(0, t - n_sink - n_recent);
+  const int kmax = min(top_k, n);
+  s.cnt = min(max(sel_cnt[bg], 0), kmax);
+  s.size = s.ns_eff + s.w_eff + s.cnt;
+  return s;
+}
+
+// Position of support element p, or -1 when the stored index is not a
+// position of the current context.
+__device__ __forceinline__ int support_pos(const SupportGeom& s, int p, int t,
+                                           const int32_t* sel_row) {
+  if (p < s.ns_eff) return p;
+  if (p < s.ns_eff + s.w_eff) return s.w_lo + (p - s.ns_eff);
+  if (p < s.size) {
+    const int j = sel_row[p - s.ns_eff - s.w_eff];
+    return (j >= 0 && j < t) ? j : -1;
+  }
+  return -1;
+}
+
+template <typename E, int D, int G, int TILES>
+__global__ __launch_bounds__(kFastThreads) void fast_kernel(FastArgs a) {
+  using A = Attn<E, D, G>;
+  constexpr int RB = A::kRowBytes;
+  constexpr int ROWS = TILES * 16;  // rows per wave
+  constexpr int NW = kFastThreads / 64;
+  constexpr int CH = NW * ROWS;     // rows per workgroup
+  constexpr int NV = ROWS / A::kRPL;
+
+  __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
+  __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
+  __shared__ float s_m[NW * G], s_l[NW * G];
+  __shared__ int s_pos[CH];
+  __shared__ int s_last;
+  __shared__ float s_M[G], s_invL[G];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wg = blockIdx.x;
+  const int e = find_entry(a.tab, wg);
+  const int local = wg - a.tab.wg_begin[e];
+  const int nchunk = a.tab.nsplit[e];
+  const int g = local / nchunk;
+  const int chunk = local - g * nchunk;
+  const int b = a.tab.seq[e];
+  const int t = a.tab.ctx[e];
+  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  const SupportGeom sg = support_geom(t, a.n_sink, a.n_recent, a.top_k, a.sel_cnt, bg);
+  const int32_t* sel_row = a.sel_idx + bg * a.top_k;
+  const int c0 = chunk * CH;
+
+  for (int i = tid; i < CH; i += kFastThreads) s_pos[i] = support_pos(sg, c0 + i, t, sel_row);
+  __syncthreads();
+
+  const int64_t kv_row0 = bg * a.t_cap;
+  const char* Kb = static_cast<const char*>(a.k) + kv_row0 * RB;
+  const char* Vb = static_cast<const char*>(a.v) + kv_row0 * RB;
+  const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
+
+  uint4 qa[A::kNL];
+  load_q<E, D, G>(a.q, qh0, lane, qa);
+  A st;
+  st.init();
+  {
+    const int kr = lane & 15, kg = lane >> 4;
+    const int vr = lane / A::kPPR, vp = lane % A::kPPR;
+    const int w0 = wave * ROWS;  // first row of this wave inside the chunk
+    uint4 kb[TILES][A::kNL];
+    uint4 vb[NV];
+    bool kvalid[TILES];
+    bool any = false;
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) {
+      const int pos = s_pos[w0 + 16 * tt + kr];
+      kvalid[tt] = pos >= 0;
+      any |= kvalid[tt];
+      const char* src = Kb + static_cast<int64_t>(pos >= 0 ? pos : 0) * RB + 16 * kg;
+#pragma unroll
+      for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16(src + 64 * kk);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int pos = s_pos[w0 + vr + A::kRPL * i];
+      vb[i] = ld16(Vb + static_cast<int64_t>(pos >= 0 ? pos : 0) * RB + 16 * vp);
+    }
+    // a wave whose rows are all outside the support keeps the empty state
+    if (__ballot(any) != 0) {
+      st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr,
+                                 0, lane);
+    }
+  }
+  st.finish_wave(s_m, s_l, s_o, wave, lane);
+  __syncthreads();
+  const int64_t slot = qh0 * a.part_stride + chunk;
+  merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
+                                  static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
+                                  static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
+
+  // arrival: the last workgroup of this (sequence, KV head) merges the chunks
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(a.counter + bg, 1);
+    s_last = (prev == nchunk - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  for (int h = wave; h < G; h += NW) {
+    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
+    float m = -INFINITY;
+    for (int s = lane; s < nchunk; s += 64) m = fmaxf(m, ml[2 * s]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int s = lane; s < nchunk; s += 64) {
+      const float ms = ml[2 * s];
+      if (ms != -INFINITY) l += ml[2 * s + 1] * fast_exp2(ms - m);
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      s_M[h] = m;
+      s_invL[h] = 1.f / l;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kFastThreads) {
+    const int h = idx / D, d = idx - h * D;
+    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
+    const float* po = a.part_o + (qh0 + h) * a.part_stride * D;
+    const float M = s_M[h];
+    float acc = 0.f;
+    for (int s = 0; s < nchunk; ++s) {
+      const float ms = ml[2 * s];
+      if (ms != -INFINITY) acc += po[static_cast<int64_t>(s) * D + d] * fast_exp2(ms - M);
+    }
+    a.out[(qh0 + h) * D + d] = acc * s_invL[h];
+  }
+  if (tid == 0) a.counter[bg] = 0;  // ready for the next launch
+}
+
+// ---------------------------------------------------------------------------
+// debug: materialise the fast-step support
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void support_kernel(SupportArgs a) {
+  const int e = blockIdx.x / a.n_kv_heads;
+  const int g = blockIdx.x - e * a.n_kv_heads;
+  const int b = a.tab.seq[e];
+  const int t = a.tab.ctx[e];
+  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  const SupportGeom sg = support_geom(t, a.n_sink, a.n_recent, a.top_k, a.sel_cnt, bg);
+  const int32_t* sel_row = a.sel_idx + bg * a.top_k;
+  int32_t* out = a.support_out + bg * a.cap_per_head;
+  for (int p = threadIdx.x; p < a.cap_per_head; p += blockDim.x)
+    out[p] = p < sg.size ? support_pos(sg, p, t, sel_row) : -1;
+  if (threadIdx.x == 0) a.support_cnt[bg] = sg.size;
+}
+
+// ---------------------------------------------------------------------------
+// KV append and workspace clearing
+// ---------------------------------------------------------------------------
+template <int RB>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  const int e = blockIdx.x / a.n_kv_heads;
+  const int g = blockIdx.x - e * a.n_kv_heads;
+  const int b = a.tab.seq[e];
+  const int t = a.tab.ctx[e];
+  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  constexpr int NP = RB / 16;
+  for (int i = threadIdx.x; i < 2 * NP; i += 64) {
+    const bool isv = i >= NP;
+    const int pc = isv ? i - NP : i;
+    const char* src = static_cast<const char*>(isv ? a.v_new : a.k_new) + bg * RB + 16 * pc;
+    char* dst = static_cast<char*>(isv ? a.v : a.k) + (bg * a.t_cap + t) * RB + 16 * pc;
+    *reinterpret_cast<uint4*>(dst) = ld16(src);
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < words; i += gridDim.x * 256ull) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+static hipError_t slow_partial_g(const SlowArgs& a, int group, int grid, hipStream_t s) {
+  switch (group) {
+    case 1: slow_partial_kernel<E, D, 1><<<grid, kSlowThreads, 0, s>>>(a); break;
+    case 2: slow_partial_kernel<E, D, 2><<<grid, kSlowThreads, 0, s>>>(a); break;
+    case 4: slow_partial_kernel<E, D, 4><<<grid, kSlowThreads, 0, s>>>(a); break;
+    case 8: slow_partial_kernel<E, D, 8><<<grid, kSlowThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_slow_partial(const SlowArgs& a, int dtype, int head_dim, int group, int grid,
+                               hipStream_t s) {
+  if (dtype == SFI_BF16) {
+    return head_dim == 128 ? slow_partial_g<BF16, 128>(a, group, grid, s)
+                           : slow_partial_g<BF16, 64>(a, group, grid, s);
+  }
+  return head_dim == 128 ? slow_partial_g<F32, 128>(a, group, grid, s)
+                         : slow_partial_g<F32, 64>(a, group, grid, s);
+}
+
+template <int D>
+static hipError_t slow_combine_g(const CombineArgs& a, int group, int grid, hipStream_t s) {
+  switch (group) {
+    case 1: slow_combine_kernel<D, 1><<<grid, kCombineThreads, 0, s>>>(a); break;
+    case 2: slow_combine_kernel<D, 2><<<grid, kCombineThreads, 0, s>>>(a); break;
+    case 4: slow_combine_kernel<D, 4><<<grid, kCombineThreads, 0, s>>>(a); break;
+    case 8: slow_combine_kernel<D, 8><<<grid, kCombineThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_slow_combine(const CombineArgs& a, int head_dim, int group, int grid,
+                               hipStream_t s) {
+  return head_dim == 128 ? slow_combine_g<128>(a, group, grid, s)
+                         : slow_combine_g<64>(a, group, grid, s);
+}
+
+// Fast-step rows per wave: one 16-row tile keeps many small workgroups in
+// flight, which is what a latency-bound gather of ~10 MB needs.
+constexpr int kFastTiles = 1;
+
+template <typename E, int D>
+static hipError_t fast_g(const FastArgs& a, int group, int grid, hipStream_t s) {
+  switch (group) {
+    case 1: fast_kernel<E, D, 1, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
+    case 2: fast_kernel<E, D, 2, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
+    case 4: fast_kernel<E, D, 4, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
+    case 8: fast_kernel<E, D, 8, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fast(const FastArgs& a, int dtype, int head_dim, int group, int grid,
+                       hipStream_t s) {
+  if (dtype == SFI_BF16) {
+    return head_dim == 128 ? fast_g<BF16, 128>(a, group, grid, s) : fast_g<BF16, 64>(a, group, grid, s);
+  }
+  return head_dim == 128 ? fast_g<F32, 128>(a, group, grid, s) : fast_g<F32, 64>(a, group, grid, s);
+}
+
+int fast_chunk_rows() { return (kFastThreads / 64) * kFastTiles * 16; }
+
+hipError_t launch_support(const SupportArgs& a, int grid, hipStream_t s) {
+  support_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, int dtype, int head_dim, int grid, hipStream_t s) {
+  const int rb = head_dim * (dtype == SFI_BF16 ? 2 : 4);
+  switch (rb) {
+    case 128: append_kernel<128><<<grid, 64, 0, s>>>(a); break;
+    case 256: append_kernel<256><<<grid, 64, 0, s>>>(a); break;
+    case 512: append_kernel<512><<<grid, 64, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  const int grid = static_cast<int>(std::min<size_t>((words + 255) / 256, 1024));
+  fill_zero_kernel<<<grid, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+}  // namespace sfi

@@ -1,0 +1,106 @@
+// Device helpers for the gfx950 kernels: element traits, 16-byte loads,
+// bf16 widening, the 16x16 MFMA logit tile and 16-lane DPP reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfi {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+struct BF16 {};
+struct F32 {};
+
+template <typename E> struct Elem;
+template <> struct Elem<BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerPiece = 8;  // elements in a 16-byte piece
+};
+template <> struct Elem<F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerPiece = 4;
+};
+
+// 16-byte global load (global_load_dwordx4).
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Widen a 16-byte piece to floats.  bf16 -> f32 is exact (shift into the
+// high half of the word).
+__device__ __forceinline__ void widen(BF16, const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void widen(F32, const uint4& u, float* f) {
+  f[0] = __uint_as_float(u.x);
+  f[1] = __uint_as_float(u.y);
+  f[2] = __uint_as_float(u.z);
+  f[3] = __uint_as_float(u.w);
+}
+
+// One 16-byte piece of K (operand B, 16 rows x 32 or 4x4 k-values) times the
+// matching piece of Q (operand A, 16 head rows), accumulated into c.
+//   lane l supplies row (l % 16) and k-group (l / 16) of both operands;
+//   c item e of lane l is C[head 4 * (l / 16) + e][row l % 16].
+__device__ __forceinline__ f32x4_t mfma_piece(BF16, const uint4& q, const uint4& k, f32x4_t c) {
+  bf16x8_t a, b;
+  __builtin_memcpy(&a, &q, 16);
+  __builtin_memcpy(&b, &k, 16);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_piece(F32, const uint4& q, const uint4& k, f32x4_t c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.x), __uint_as_float(k.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.y), __uint_as_float(k.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.z), __uint_as_float(k.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.w), __uint_as_float(k.w), c, 0, 0, 0);
+  return c;
+}
+
+// DPP lane exchanges inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Max / sum over the 16 lanes of a row; every lane of the row gets the result.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kDppQuadSwap1>(x);
+  x += dpp<kDppQuadSwap2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float lane_bcast(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Locate the table entry owning workgroup `wg` (tables are short).
+template <typename Table>
+__device__ __forceinline__ int find_entry(const Table& t, int wg) {
+  int e = 0;
+  while (e + 1 < t.n && t.wg_begin[e + 1] <= wg) ++e;
+  return e;
+}
+
+}  // namespace sfi

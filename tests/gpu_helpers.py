@@ -1,0 +1,78 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the
+binding and compare with the CPU oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import sparse_kv_attention_sfi_amd as S
+
+OUT_TOL = 2e-3        # max-abs error of attention outputs against fp64
+MASS_REL_TOL = 1e-5   # mass: max-abs error relative to the row's max mass
+MASS_SUM_TOL = 1e-5
+GAP_REL = 1e-5        # support: relative k-th/(k+1)-th score gap for exactness
+
+
+def np64(t):
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return torch.device("cuda:0")
+
+
+def random_cache(B, Hq, Hkv, cap, D, dtype, ctx, seed, q_scale=1.0):
+    dev = device()
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    K = torch.randn(B, Hkv, cap, D, generator=g, device=dev).to(dtype)
+    V = torch.randn(B, Hkv, cap, D, generator=g, device=dev).to(dtype)
+    q = (q_scale * torch.randn(B, Hq, D, generator=g, device=dev)).to(dtype)
+    kv = S.KVDesc(K, V, ctx, Hq)
+    return kv, q
+
+
+def run_slow(kv, q, ids, with_mass=True, ws=None):
+    dev = kv.k.device
+    out = torch.full((kv.batch, kv.n_q_heads, kv.head_dim), float("nan"), device=dev)
+    mass = torch.full((kv.batch, kv.n_kv_heads, kv.capacity), -1.0, device=dev) if with_mass else None
+    if ws is None:
+        ws = S.alloc_workspace(kv)
+    S.sfi_slow_step(kv, ids, q, out, mass, ws)
+    torch.cuda.synchronize()
+    return out, mass
+
+
+def oracle_slow(kv, q, b):
+    T = int(kv.ctx[b])
+    K = np64(kv.k[b, :, :T]); V = np64(kv.v[b, :, :T])
+    out, P = O.dense_attention(np64(q[b]), K, V)
+    return out, O.group_mass(P, kv.n_kv_heads)
+
+
+def check_support(gpu_sel, f_row, T, ns, W, k, lam, where=""):
+    """Support parity: exact when the oracle's k-th / (k+1)-th scores are
+    separated by more than GAP_REL relative, tie-tolerant otherwise."""
+    sel, score, cand = O.select(f_row, T, ns, W, k, lam)
+    gpu = sorted(int(x) for x in gpu_sel)
+    ora = sel.tolist()
+    assert len(gpu) == len(ora), (where, len(gpu), len(ora))
+    assert len(set(gpu)) == len(gpu), where
+    assert all(ns <= j < T - W for j in gpu), where
+    n = len(cand)
+    if n <= k:
+        assert gpu == ora, where
+        return "all"
+    order = np.sort(score)[::-1]
+    sk, sk1 = order[k - 1], order[k]
+    if sk > 0 and (sk - sk1) / sk > GAP_REL:
+        assert gpu == ora, (where, sk, sk1)
+        return "exact"
+    sc = dict(zip(cand.tolist(), score.tolist()))
+    for j in set(gpu) - set(ora):
+        assert sc[j] >= sk * (1 - GAP_REL), (where, j, sc[j], sk)
+    for j in set(ora) - set(gpu):
+        assert sc[j] <= sk * (1 + GAP_REL), (where, j, sc[j], sk)
+    return "tolerant"

@@ -1,0 +1,243 @@
+"""GPU parity of each kernel against the CPU oracle on small seeded inputs that
+span several tiles and splits with ragged tails, plus edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_kv_attention_sfi_amd as S
+from tests.gpu_helpers import (MASS_REL_TOL, MASS_SUM_TOL, OUT_TOL, check_support, np64,
+                               oracle_slow, random_cache, run_slow)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_slow_step_shapes(dtype, D, G):
+    Hkv = 2
+    ctx = [1000, 3001, 17]
+    kv, q = random_cache(3, G * Hkv, Hkv, 3072, D, DT[dtype], ctx, seed=100 + D + G, q_scale=2.0)
+    out, mass = run_slow(kv, q, [0, 1, 2])
+    for b in range(3):
+        o_ref, f_ref = oracle_slow(kv, q, b)
+        T = ctx[b]
+        assert np.max(np.abs(np64(out[b]) - o_ref)) < OUT_TOL
+        f = np64(mass[b, :, :T])
+        assert np.max(np.abs(f - f_ref)) <= MASS_REL_TOL * f_ref.max()
+        assert np.max(np.abs(f.sum(axis=1) - 1.0)) < MASS_SUM_TOL
+        assert torch.all(mass[b, :, T:] == -1.0)          # beyond ctx untouched
+
+
+@pytest.mark.parametrize("T", [1, 2, 255, 256, 257, 4097])
+def test_slow_step_context_edges(T):
+    kv, q = random_cache(1, 8, 2, 4200, 128, torch.bfloat16, [T], seed=T, q_scale=3.0)
+    out, mass = run_slow(kv, q, [0])
+    o_ref, f_ref = oracle_slow(kv, q, 0)
+    assert np.max(np.abs(np64(out[0]) - o_ref)) < OUT_TOL
+    assert np.max(np.abs(np64(mass[0, :, :T]) - f_ref)) <= MASS_REL_TOL * f_ref.max()
+    if T == 1:
+        assert np.max(np.abs(np64(out[0]) - np.repeat(np64(kv.v[0, :, 0]), 4, axis=0))) < 1e-6
+
+
+def test_slow_without_mass_and_subset_rows():
+    kv, q = random_cache(4, 32, 8, 2048, 128, torch.bfloat16, [2048, 1500, 999, 64], seed=7)
+    dev = kv.k.device
+    out = torch.full((4, 32, 128), 7.0, device=dev)
+    ws = S.alloc_workspace(kv)
+    S.sfi_slow_step(kv, [2, 0], q, out, None, ws)
+    torch.cuda.synchronize()
+    for b in (0, 2):
+        o_ref, _ = oracle_slow(kv, q, b)
+        assert np.max(np.abs(np64(out[b]) - o_ref)) < OUT_TOL
+    assert torch.all(out[1] == 7.0) and torch.all(out[3] == 7.0)    # unlisted rows untouched
+
+
+def test_slow_deterministic():
+    kv, q = random_cache(1, 32, 8, 40000, 128, torch.bfloat16, [39999], seed=3)
+    a_out, a_mass = run_slow(kv, q, [0])
+    b_out, b_mass = run_slow(kv, q, [0])
+    assert torch.equal(a_out, b_out) and torch.equal(a_mass, b_mass)
+
+
+# ------------------------------------------------------------------ select
+def _select_gpu(kv, sp, ids, mass):
+    dev = kv.k.device
+    sel = torch.full((kv.batch, kv.n_kv_heads, sp.top_k), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((kv.batch, kv.n_kv_heads), -7, dtype=torch.int32, device=dev)
+    S.sfi_select(kv, sp, ids, mass, sel, cnt)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), cnt.cpu().numpy()
+
+
+def _mass_cache(B, Hkv, cap, ctx):
+    dev = torch.device("cuda:0")
+    K = torch.zeros(B, Hkv, cap, 64, device=dev)
+    kv = S.KVDesc(K, K.clone(), ctx, Hkv * 4)
+    return kv
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.1, 0.5, 1.0])
+@pytest.mark.parametrize("T,ns,W,k", [(5000, 4, 64, 256), (5000, 16, 256, 2048), (300, 4, 16, 1),
+                                      (100, 4, 16, 200), (20, 4, 16, 5), (10, 4, 16, 5), (70000, 16, 256, 2048)])
+def test_select_random_mass(lam, T, ns, W, k):
+    rng = np.random.default_rng(T + k)
+    Hkv, cap = 3, T + 5
+    f = rng.gamma(0.3, size=(1, Hkv, cap)).astype(np.float32)
+    f /= f[..., :T].sum(axis=-1, keepdims=True)
+    kv = _mass_cache(1, Hkv, cap, [T])
+    mass = torch.from_numpy(f).cuda()
+    sp = S.support_params(ns, W, k, lam)
+    sel, cnt = _select_gpu(kv, sp, [0], mass)
+    n = max(0, T - ns - W)
+    for g in range(Hkv):
+        c = int(cnt[0, g])
+        assert c == min(k, n)
+        assert np.all(sel[0, g, c:] == -1)
+        assert np.all(np.diff(sel[0, g, :c]) > 0)            # ascending
+        check_support(sel[0, g, :c], f[0, g].astype(np.float64), T, ns, W, k, lam, f"g{g}")
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 1000])
+def test_select_ties_exact(k):
+    """Evidence with heavy exact ties and lambda = 0: the fp32 and fp64 scores
+    coincide, so the lowest-index rule must match bit for bit."""
+    rng = np.random.default_rng(k)
+    T, ns, W, Hkv = 6000, 4, 64, 2
+    f = (rng.integers(0, 4, size=(1, Hkv, T)).astype(np.float32) / 8.0)
+    kv = _mass_cache(1, Hkv, T, [T])
+    sel, cnt = _select_gpu(kv, S.support_params(ns, W, k, 0.0), [0], torch.from_numpy(f).cuda())
+    for g in range(Hkv):
+        ora = O.select(f[0, g].astype(np.float64), T, ns, W, k, 0.0)[0]
+        assert sel[0, g, :cnt[0, g]].tolist() == ora.tolist()
+
+
+def test_select_all_equal_and_prior_closed_form():
+    """Uniform evidence: with lambda > 0 the choice follows the prior (both ends
+    of the candidate range); with lambda = 0 every score ties and the lowest k
+    positions win.  Exercises the deepest radix path (no early LDS copy)."""
+    T, ns, W, k, Hkv = 20000, 16, 256, 2048, 1
+    f = np.full((1, Hkv, T), 1.0 / T, dtype=np.float32)
+    kv = _mass_cache(1, Hkv, T, [T])
+    n = T - ns - W
+    sel, cnt = _select_gpu(kv, S.support_params(ns, W, k, 0.0), [0], torch.from_numpy(f).cuda())
+    assert sel[0, 0].tolist() == list(range(ns, ns + k))
+    sel, cnt = _select_gpu(kv, S.support_params(ns, W, k, 1.0), [0], torch.from_numpy(f).cuda())
+    a = sel[0, 0] - ns + 1
+    assert a.tolist() == list(range(1, k // 2 + 1)) + list(range(n - k // 2 + 1, n + 1))
+
+
+# ------------------------------------------------------------------ fast step
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_fast_step_with_oracle_support(dtype, D, G):
+    Hkv, ns, W, k = 2, 4, 64, 200
+    ctx = [3000, 700, 50]
+    kv, q = random_cache(3, G * Hkv, Hkv, 3000, D, DT[dtype], ctx, seed=G * D, q_scale=2.0)
+    dev = kv.k.device
+    sel = torch.full((3, Hkv, k), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(3, Hkv, dtype=torch.int32, device=dev)
+    sels = {}
+    for b in range(3):
+        T = ctx[b]
+        _, f = oracle_slow(kv, q, b)
+        for g in range(Hkv):
+            s = O.select(f[g], T, ns, W, k, 0.1)[0]
+            sels[(b, g)] = s
+            sel[b, g, :len(s)] = torch.from_numpy(s.astype(np.int32))
+            cnt[b, g] = len(s)
+    sp = S.support_params(ns, W, k, 0.1)
+    out = torch.full((3, G * Hkv, D), float("nan"), device=dev)
+    ws = S.alloc_workspace(kv, sp)
+    S.sfi_fast_step(kv, sp, [0, 1, 2], q, sel, cnt, out, ws)
+    S.sfi_fast_step(kv, sp, [0, 1, 2], q, sel, cnt, out, ws)   # counters reset by the first call
+    torch.cuda.synchronize()
+    for b in range(3):
+        T = ctx[b]
+        ref = O.fast_step(np64(q[b]), np64(kv.k[b, :, :T]), np64(kv.v[b, :, :T]), T, ns, W,
+                          [sels[(b, g)] for g in range(Hkv)])
+        assert np.max(np.abs(np64(out[b]) - ref)) < OUT_TOL
+
+
+def test_fast_equals_slow_when_support_covers_context():
+    kv, q = random_cache(2, 32, 8, 2500, 128, torch.bfloat16, [2500, 1234], seed=5, q_scale=2.0)
+    sp = S.support_params(16, 256, 4096, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    dev = kv.k.device
+    out_s, mass = run_slow(kv, q, [0, 1], ws=ws)
+    sel = torch.empty(2, 8, 4096, dtype=torch.int32, device=dev)
+    cnt = torch.empty(2, 8, dtype=torch.int32, device=dev)
+    S.sfi_select(kv, sp, [0, 1], mass, sel, cnt, ws)
+    out_f = torch.empty_like(out_s)
+    S.sfi_fast_step(kv, sp, [0, 1], q, sel, cnt, out_f, ws)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(out_f - out_s)).item() < OUT_TOL
+
+
+def test_fast_ignores_out_of_range_indices_and_counts():
+    kv, q = random_cache(1, 8, 2, 1000, 64, torch.float32, [900], seed=9)
+    dev = kv.k.device
+    ns, W, k = 4, 16, 8
+    sp = S.support_params(ns, W, k, 0.1)
+    good = np.array([10, 20, 30, 40], dtype=np.int32)
+    sel = torch.full((1, 2, k), -1, dtype=torch.int32, device=dev)
+    sel[0, :, :4] = torch.from_numpy(good)
+    sel[0, :, 4] = 950          # beyond the context: ignored
+    sel[0, :, 5] = -5           # negative: ignored
+    cnt = torch.tensor([[6, 4]], dtype=torch.int32, device=dev)
+    out = torch.empty(1, 8, 64, device=dev)
+    S.sfi_fast_step(kv, sp, [0], q, sel, cnt, out, S.alloc_workspace(kv, sp))
+    torch.cuda.synchronize()
+    ref = O.fast_step(np64(q[0]), np64(kv.k[0, :, :900]), np64(kv.v[0, :, :900]), 900, ns, W, [good, good])
+    assert np.max(np.abs(np64(out[0]) - ref)) < OUT_TOL
+
+
+def test_debug_support_matches_oracle_sets():
+    T, ns, W, k, Hkv = 5000, 16, 256, 100, 2
+    kv = _mass_cache(1, Hkv, T, [T])
+    rng = np.random.default_rng(1)
+    f = rng.random((1, Hkv, T)).astype(np.float32)
+    sp = S.support_params(ns, W, k, 0.1)
+    sel, cnt = _select_gpu(kv, sp, [0], torch.from_numpy(f).cuda())
+    dev = torch.device("cuda:0")
+    sup = torch.full((1, Hkv, 512), -9, dtype=torch.int32, device=dev)
+    scnt = torch.zeros(1, Hkv, dtype=torch.int32, device=dev)
+    S.sfi_debug_support(kv, sp, [0], torch.from_numpy(sel).cuda(), torch.from_numpy(cnt).cuda(), sup, scnt)
+    torch.cuda.synchronize()
+    for g in range(Hkv):
+        c = int(scnt[0, g])
+        got = sup[0, g, :c].cpu().numpy()
+        assert sorted(got.tolist()) == O.support(T, ns, W, sel[0, g, :cnt[0, g]]).tolist()
+
+
+# ------------------------------------------------------------------ append
+def test_kv_append_then_slow_step():
+    kv, q = random_cache(2, 8, 2, 600, 128, torch.bfloat16, [500, 300], seed=11)
+    dev = kv.k.device
+    kn = torch.randn(2, 2, 128, device=dev).to(torch.bfloat16)
+    vn = torch.randn(2, 2, 128, device=dev).to(torch.bfloat16)
+    S.sfi_kv_append(kv, [0, 1], kn, vn)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.k[0, :, 500], kn[0]) and torch.equal(kv.v[1, :, 300], vn[1])
+    kv.ctx[:] = [501, 301]
+    out, _ = run_slow(kv, q, [0, 1])
+    for b in range(2):
+        o_ref, _ = oracle_slow(kv, q, b)
+        assert np.max(np.abs(np64(out[b]) - o_ref)) < OUT_TOL
+
+
+# ------------------------------------------------------------------ errors
+def test_invalid_arguments_raise_before_launch():
+    kv, q = random_cache(1, 8, 2, 100, 64, torch.float32, [100], seed=1)
+    out = torch.empty(1, 8, 64, device=kv.k.device)
+    with pytest.raises(S.SFIError):
+        S.sfi_slow_step(kv, [1], q, out, None, S.alloc_workspace(kv))   # id out of range
+    with pytest.raises(S.SFIError):
+        S.sfi_slow_step(kv, [0], q, out, None, None)                       # no workspace
+    kv.ctx[0] = 101
+    with pytest.raises(S.SFIError):
+        S.sfi_slow_step(kv, [0], q, out, None, S.alloc_workspace(kv))    # ctx beyond capacity

@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Decode-attention throughput of the SFI path on one MI355X.
+
+Workload (default): the 8B-shaped layer at 128K context, batch 1, bf16 KV,
+32 query / 8 KV heads, head_dim 128, 16 sinks + 256 recent + top-2048,
+lambda 0.1, spans geometric with mean 18 drawn by the boundary scheduler.
+Every decode step runs that layer shape over ``--layers`` independent
+caches (32 by default, as a decoder stack would), so a layer's KV rows and
+support are not reused from L2/MALL between two of its own steps.
+
+A "step" is one decode step over all layers: for every layer either the slow
+path (dense split-K attention + mass + Selector) or the fast path (gathered
+sparse attention), as the scheduler says.  ``value`` = K * layers / wall
+time of K steps (decode steps per second per layer), with inputs resident in
+HBM.  Each step's queries are staged into fixed buffers and the step is
+replayed as a HIP graph (one for slow steps, one for fast steps).
+
+Also reported: per-kernel average durations from HIP events recorded by the
+library around its launches (eager pass over the same steps), the roofline
+of the dominant kernel, the dense-every-step baseline, and the CPU oracle on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn steps/sec/layer (slow, fast, blended) + HBM GB/s frac @128K ctx"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1024)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", default="C3")
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--dense-steps", type=int, default=64)
+    p.add_argument("--eager-steps", type=int, default=128)
+    p.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path shards by KV head or "
+                          "sequence with no per-step communication, but no multi-GPU run is built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_kv_attention_sfi_amd as S
+    import synth
+    from synth import gen
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    S.lib()  # fail loudly when the library is missing
+    dev = torch.device("cuda:0")
+    w = {"C1": synth.C1, "C2": synth.C2, "C3": synth.C3, "C4": synth.C4}[args.workload]
+    if w.batch != 1:
+        raise SystemExit("bench.py times batch-1 workloads")
+    L, K, W = args.layers, args.steps, args.warmup
+    n_steps = W + K
+
+    # schedule (host scheduler) and the span index of every step
+    sched = S.Scheduler(1, w.seed, w.span_mode, w.span_param)
+    flags = [bool(sched.step()[0]) for _ in range(n_steps)]
+    sched.close()
+    span_ids = [gen.span_ids_from_flags(flags)]
+    n_spans = span_ids[0][-1] + 1
+
+    # inputs: L layer caches, per-step queries, all resident in HBM
+    t0 = time.time()
+    kvs, q_steps = [], torch.empty(n_steps, L, 1, w.n_q_heads, w.head_dim, dtype=gen.torch_dtype(w.dtype),
+                                   device=dev)
+    for l in range(L):
+        c = gen.build_cache(w, dev, layer=l, n_spans=n_spans)
+        kvs.append(S.KVDesc(c["K"], c["V"], c["ctx_len"], w.n_q_heads))
+        q_steps[:, l].copy_(gen.build_queries(w, dev, span_ids, c, layer=l))
+        del c
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: {L} layers x {w.ctx} ctx")
+
+    sp = S.support_params(w.n_sink, w.n_recent, w.top_k, w.lam)
+    ws = S.alloc_workspace(kvs[0], sp)
+    q_buf = torch.empty(L, 1, w.n_q_heads, w.head_dim, dtype=q_steps.dtype, device=dev)
+    out_buf = torch.empty(L, 1, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    mass = torch.empty(1, w.n_kv_heads, kvs[0].capacity, dtype=torch.float32, device=dev)
+    sel = torch.empty(L, 1, w.n_kv_heads, w.top_k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(L, 1, w.n_kv_heads, dtype=torch.int32, device=dev)
+
+    def slow_layers():
+        for l in range(L):
+            S.sfi_slow_step(kvs[l], [0], q_buf[l], out_buf[l], mass, ws)
+            S.sfi_select(kvs[l], sp, [0], mass, sel[l], cnt[l], ws)
+
+    def fast_layers():
+        for l in range(L):
+            S.sfi_fast_step(kvs[l], sp, [0], q_buf[l], sel[l], cnt[l], out_buf[l], ws)
+
+    def dense_layers():
+        for l in range(L):
+            S.sfi_slow_step(kvs[l], [0], q_buf[l], out_buf[l], None, ws)
+
+    # eager warm-up (also primes the selection used by the first fast step)
+    q_buf.copy_(q_steps[0])
+    slow_layers()
+    fast_layers()
+    dense_layers()
+    torch.cuda.synchronize()
+
+    if args.mode == "graph":
+        graphs = {}
+        for name, fn in (("slow", slow_layers), ("fast", fast_layers), ("dense", dense_layers)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs[name] = g
+        run = {"slow": graphs["slow"].replay, "fast": graphs["fast"].replay, "dense": graphs["dense"].replay}
+    else:
+        run = {"slow": slow_layers, "fast": fast_layers, "dense": dense_layers}
+
+    def step(t, kind=None):
+        q_buf.copy_(q_steps[t])
+        run[kind or ("slow" if flags[t] else "fast")]()
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for t in range(W, W + K):
+        step(t)
+    torch.cuda.synchronize()
+    t_blend = time.perf_counter() - t_start
+    n_slow_timed = sum(flags[W:W + K])
+    log(f"blended: {K} steps ({n_slow_timed} slow) x {L} layers in {t_blend * 1e3:.1f} ms")
+
+    # dense-every-step baseline (same queries)
+    kd = min(args.dense_steps, n_steps)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for t in range(kd):
+        step(t, "dense")
+    torch.cuda.synchronize()
+    t_dense = time.perf_counter() - t_start
+
+    # per-kernel durations: library HIP events around each launch, eager
+    S.sfi_profile_reset()
+    S.sfi_profile_enable(True)
+    ke = min(args.eager_steps, n_steps)
+    for t in range(ke):
+        q_buf.copy_(q_steps[t])
+        (slow_layers if flags[t] else fast_layers)()
+    torch.cuda.synchronize()
+    S.sfi_profile_enable(False)
+    kern = {}
+    for kid, name in S.KERNEL_NAMES.items():
+        ms, n = S.sfi_profile_read(kid)
+        if n:
+            kern[name] = {"launches": n, "avg_us": 1e3 * ms / n}
+    T = w.ctx
+    kv_bytes_slow = 2 * w.n_kv_heads * T * w.head_dim * 2 if w.dtype == "bf16" else 2 * w.n_kv_heads * T * w.head_dim * 4
+    esz = 2 if w.dtype == "bf16" else 4
+    supp = w.n_sink + w.n_recent + min(w.top_k, T - w.n_sink - w.n_recent)
+    alg = {
+        "slow_partial": kv_bytes_slow + w.n_q_heads * w.head_dim * esz,
+        "slow_combine": 4 * w.n_kv_heads * T + 4 * w.n_q_heads * w.head_dim,
+        "select": 4 * w.n_kv_heads * (T - w.n_sink - w.n_recent) + 4 * w.n_kv_heads * w.top_k,
+        "fast": 2 * w.n_kv_heads * supp * w.head_dim * esz + 4 * w.n_kv_heads * w.top_k
+                + w.n_q_heads * w.head_dim * esz,
+    }
+    for name, k in kern.items():
+        if name in alg:
+            k["alg_bytes"] = alg[name]
+            k["GBps"] = alg[name] / (k["avg_us"] * 1e-6) / 1e9
+            k["frac"] = k["GBps"] / HBM_PEAK_GBS
+    total_time = {n: k["avg_us"] * k["launches"] for n, k in kern.items()}
+    dominant = max(total_time, key=total_time.get)
+
+    def us(name):
+        return kern.get(name, {}).get("avg_us", 0.0)
+
+    slow_us = us("slow_partial") + us("slow_combine") + us("select")
+    fast_us = us("fast")
+    value = K * L / t_blend
+    dense_rate = kd * L / t_dense
+    d = kern[dominant]
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "decode steps/s/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": 1e3 * t_blend / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B=1, {w.n_q_heads}q/{w.n_kv_heads}kv heads, D={w.head_dim}, "
+                               f"ctx {w.ctx}, {w.dtype} KV, sinks {w.n_sink}, recent {w.n_recent}, "
+                               f"top-k {w.top_k}, lambda {w.lam}, geometric spans mean {w.span_param}; "
+                               f"{L} independent layer caches per decode step",
+                   "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode,
+                   "slow_steps_timed": n_slow_timed},
+        "slow_steps_per_s_layer": 1e6 / slow_us if slow_us else None,
+        "fast_steps_per_s_layer": 1e6 / fast_us if fast_us else None,
+        "blended_steps_per_s_layer": value,
+        "dense_steps_per_s_layer": dense_rate,
+        "speedup_vs_dense": value / dense_rate,
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d.get("frac"), "traffic": None,
+                     "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, sp, args.cpu_budget)
+    print(json.dumps(result))
+
+
+def cpu_baseline(w, kv, q_steps, flags, sp, budget):
+    """The CPU oracle, as it stands, on the first steps of layer 0's schedule
+    until ``budget`` seconds of oracle work have run."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    T = int(kv.ctx[0])
+    K = kv.k[0, :, :T].float().cpu().numpy().astype(np.float64)
+    V = kv.v[0, :, :T].float().cpu().numpy().astype(np.float64)
+    qs = q_steps[:, 0].float().cpu().numpy().astype(np.float64)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    done, sels, spent = 0, None, 0.0
+    while spent < budget and done < len(flags):
+        t0 = time.perf_counter()
+        if flags[done] or sels is None:
+            _, _, sels = O.slow_step(qs[done], K, V, T, w.n_sink, w.n_recent, w.top_k, w.lam)
+        else:
+            O.fast_step(qs[done], K, V, T, w.n_sink, w.n_recent, sels)
+        spent += time.perf_counter() - t0
+        done += 1
+    n_slow = sum(flags[:done])
+    return {"value": done / spent, "unit": "decode steps/s/layer", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} decode steps ({n_slow} slow) of layer 0 of the same workload, "
+                      f"numpy float64, {spent:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

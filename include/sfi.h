@@ -97,8 +97,9 @@ typedef struct {
 size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp, int32_t op);
 
 /* Prepares a freshly allocated workspace (device, ws_bytes) for use: clears
- * the completion counters the fast step keeps there.  Call once after
- * allocation; the kernels leave the counters cleared when they finish.
+ * the bookkeeping the Selector keeps at its start (a per-head histogram and a
+ * list counter).  Call once after allocation, before the first sfi_select;
+ * the Selector's kernels leave that bookkeeping cleared when they finish.
  * Workspaces must not be shared by calls that may run concurrently. */
 int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
@@ -126,7 +127,8 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int3
  *   sel_idx : device int32 [B][Hkv][top_k]; the kept positions in ascending
  *             order, then -1 up to top_k
  *   sel_cnt : device int32 [B][Hkv]; min(top_k, n) (0 when T <= n_sink + n_recent)
- *   ws      : at least sfi_workspace_bytes(desc, sp, SFI_OP_SELECT) bytes. */
+ *   ws      : at least sfi_workspace_bytes(desc, sp, SFI_OP_SELECT) bytes,
+ *             prepared once by sfi_workspace_init. */
 int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp,
                    const int32_t* seq_ids_host, int32_t n_seq, const float* mass,
                    int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes, void* stream);
@@ -138,12 +140,34 @@ int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp,
  *   q, out           : as for sfi_slow_step
  *   sel_idx, sel_cnt : device, as written by sfi_select.  Entries outside
  *                      [0, t) and counts above min(top_k, n) are ignored.
- *   ws               : at least sfi_workspace_bytes(desc, sp, SFI_OP_FAST)
- *                      bytes, prepared once by sfi_workspace_init. */
+ *   ws               : at least sfi_workspace_bytes(desc, sp, SFI_OP_FAST) bytes.
+ * An empty support (possible only with n_sink = n_recent = 0 and a zero count)
+ * yields a zero output. */
 int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp,
                       const int32_t* seq_ids_host, int32_t n_seq, const void* q,
                       const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* Memory-coalesced layout of the selected memory ("Slow-Fast Inference ...",
+ * gist.science technical summary, 3 "Systemdesign und Kernel-Optimierung":
+ * after each slow step the selected tokens are packed into a contiguous
+ * buffer, while sinks and the recent window are read from the cache).
+ *
+ * sfi_pack_support copies, for each listed (b, g), the rows
+ * K[b][g][sel_idx[b][g][i]] and V[...] for i < sel_cnt[b][g] into
+ * packed_k[b][g][i] and packed_v[b][g][i] (device [B][Hkv][top_k][D],
+ * kv_dtype).  Indices outside [0, ctx_len[b]) are skipped. */
+int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                         const int32_t* seq_ids_host, int32_t n_seq, const int32_t* sel_idx,
+                         const int32_t* sel_cnt, void* packed_k, void* packed_v, void* stream);
+
+/* Fast step over a packed support: the same result as sfi_fast_step with the
+ * sel_idx that filled packed_k / packed_v; the selected rows are read
+ * contiguously from the packed buffers (no index lookups). */
+int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                             const int32_t* seq_ids_host, int32_t n_seq, const void* q,
+                             const void* packed_k, const void* packed_v, const int32_t* sel_cnt,
+                             float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Appends one token per listed sequence: writes k_new[b][g][:] and
  * v_new[b][g][:] (device [B][Hkv][D], kv_dtype) into row ctx_len[b] of
@@ -192,10 +216,11 @@ int32_t sfi_version(void); /* MAJOR * 100 + MINOR */
 typedef enum {
   SFI_K_SLOW_PARTIAL = 0, /* split-K dense partials (+ logit scratch) */
   SFI_K_SLOW_COMBINE = 1, /* split merge + per-position mass */
-  SFI_K_SELECT = 2,       /* Selector */
-  SFI_K_FAST = 3,         /* sparse gather attention (+ fused merge) */
+  SFI_K_SELECT = 2,       /* Selector (its four kernels together) */
+  SFI_K_FAST = 3,         /* sparse gather attention + chunk merge */
   SFI_K_APPEND = 4,
-  SFI_K_COUNT = 5
+  SFI_K_PACK = 5,         /* packing of the selected rows */
+  SFI_K_COUNT = 6
 } sfi_kernel_id;
 int32_t sfi_profile_enable(int32_t on);
 int32_t sfi_profile_reset(void);

@@ -20,9 +20,9 @@ SFI_OK, SFI_ERR_INVALID_ARG, SFI_ERR_UNSUPPORTED, SFI_ERR_WORKSPACE, SFI_ERR_HIP
 SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST = 0, 1, 2
 SFI_SPAN_FIXED, SFI_SPAN_GEOMETRIC = 0, 1
-SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND = 0, 1, 2, 3, 4
+SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK = 0, 1, 2, 3, 4, 5
 KERNEL_NAMES = {SFI_K_SLOW_PARTIAL: "slow_partial", SFI_K_SLOW_COMBINE: "slow_combine",
-                SFI_K_SELECT: "select", SFI_K_FAST: "fast", SFI_K_APPEND: "append"}
+                SFI_K_SELECT: "select", SFI_K_FAST: "fast", SFI_K_APPEND: "append", SFI_K_PACK: "pack"}
 
 
 class SFIError(RuntimeError):
@@ -66,6 +66,8 @@ def lib():
             "sfi_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, SZ, VP]),
             "sfi_fast_step": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, SZ, VP]),
             "sfi_kv_append": (I32, [D, P(I32), I32, VP, VP, VP]),
+            "sfi_pack_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP]),
+            "sfi_fast_step_packed": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "sfi_debug_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, I32, VP]),
             "sfi_sched_create": (I32, [I32, C.c_uint64, I32, C.c_double, I32, P(VP)]),
             "sfi_sched_step": (I32, [VP, P(I32), P(I32), P(I32), P(I32)]),
@@ -226,6 +228,33 @@ def sfi_fast_step(kv: KVDesc, sp, seq_ids, q, sel_idx, sel_cnt, out, ws, stream=
                                _ptr(out), _ptr(ws), nbytes, _stream(stream)), "sfi_fast_step")
 
 
+def sfi_pack_support(kv: KVDesc, sp, seq_ids, sel_idx, sel_cnt, packed_k, packed_v, stream=None):
+    import torch
+    B, Hkv, D = kv.batch, kv.n_kv_heads, kv.head_dim
+    _need(sel_idx, torch.int32, (B, Hkv, sp.top_k), "sel_idx")
+    _need(sel_cnt, torch.int32, (B, Hkv), "sel_cnt")
+    _need(packed_k, kv.dtype, (B, Hkv, sp.top_k, D), "packed_k")
+    _need(packed_v, kv.dtype, (B, Hkv, sp.top_k, D), "packed_v")
+    _, ids, n = _ids(seq_ids)
+    _check(lib().sfi_pack_support(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(sel_idx), _ptr(sel_cnt),
+                                  _ptr(packed_k), _ptr(packed_v), _stream(stream)), "sfi_pack_support")
+
+
+def sfi_fast_step_packed(kv: KVDesc, sp, seq_ids, q, packed_k, packed_v, sel_cnt, out, ws, stream=None):
+    import torch
+    B, Hq, Hkv, D = kv.batch, kv.n_q_heads, kv.n_kv_heads, kv.head_dim
+    _need(q, kv.dtype, (B, Hq, D), "q")
+    _need(out, torch.float32, (B, Hq, D), "out")
+    _need(packed_k, kv.dtype, (B, Hkv, sp.top_k, D), "packed_k")
+    _need(packed_v, kv.dtype, (B, Hkv, sp.top_k, D), "packed_v")
+    _need(sel_cnt, torch.int32, (B, Hkv), "sel_cnt")
+    _, ids, n = _ids(seq_ids)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sfi_fast_step_packed(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(packed_k),
+                                      _ptr(packed_v), _ptr(sel_cnt), _ptr(out), _ptr(ws), nbytes,
+                                      _stream(stream)), "sfi_fast_step_packed")
+
+
 def sfi_kv_append(kv: KVDesc, seq_ids, k_new, v_new, stream=None):
     B, Hkv, D = kv.batch, kv.n_kv_heads, kv.head_dim
     _need(k_new, kv.dtype, (B, Hkv, D), "k_new")
@@ -256,7 +285,10 @@ class Scheduler:
 
     def __init__(self, batch, seed, mode, span_param, t_max=0):
         self._h = C.c_void_p()
-        m = {"fixed": SFI_SPAN_FIXED, "geometric": SFI_SPAN_GEOMETRIC}.get(mode, mode)
+        modes = {"fixed": SFI_SPAN_FIXED, "geometric": SFI_SPAN_GEOMETRIC}
+        if mode not in modes and mode not in modes.values():
+            raise ValueError(f"unknown span mode {mode!r}")
+        m = modes.get(mode, mode)
         _check(lib().sfi_sched_create(int(batch), C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(m),
                                       float(span_param), int(t_max), C.byref(self._h)), "sfi_sched_create")
         self.batch = int(batch)

@@ -118,10 +118,35 @@ float logit_scale(const sfi_kv_desc* d) {
 }
 
 // ---- workspace layout -----------------------------------------------------
-// [ fast-step arrival counters | op scratch ]  The counter block sits at a
-// fixed offset so that slow, select and fast calls may share one workspace.
-size_t counter_bytes(const sfi_kv_desc* d) {
-  return align_up(static_cast<size_t>(d->batch) * d->n_kv_heads * sizeof(int32_t));
+// [ persistent header | op scratch ].  The header holds the Selector's
+// bookkeeping (top-digit histogram, list counter), which its kernels leave
+// cleared when they finish; it sits at a fixed offset so slow, select and fast
+// calls may share one workspace.
+struct Header {
+  size_t sel_hist, sel_list_n, end;
+};
+Header header_layout(const sfi_kv_desc* d) {
+  const size_t bh = static_cast<size_t>(d->batch) * d->n_kv_heads;
+  Header H;
+  H.sel_hist = 0;
+  H.sel_list_n = H.sel_hist + align_up(bh * 4096 * sizeof(uint32_t));
+  H.end = H.sel_list_n + align_up(bh * sizeof(int32_t));
+  return H;
+}
+size_t header_bytes(const sfi_kv_desc* d) { return header_layout(d).end; }
+
+struct SelectLayout {
+  size_t list, chunk_above, chunk_off, kstar, end;
+};
+SelectLayout select_layout(const sfi_kv_desc* d) {
+  const size_t bh = static_cast<size_t>(d->batch) * d->n_kv_heads;
+  SelectLayout L;
+  L.list = header_bytes(d);
+  L.chunk_above = L.list + align_up(bh * kSelListCap * sizeof(uint64_t));
+  L.chunk_off = L.chunk_above + align_up(bh * kSelMaxChunks * sizeof(int32_t));
+  L.kstar = L.chunk_off + align_up(bh * kSelMaxChunks * sizeof(int32_t));
+  L.end = L.kstar + align_up(bh * sizeof(uint64_t));
+  return L;
 }
 
 int slow_unit_rows(const sfi_kv_desc* d) {
@@ -132,6 +157,8 @@ int slow_part_stride(const sfi_kv_desc* d) {
   return static_cast<int>(ceil_div(d->kv_capacity, slow_unit_rows(d)));
 }
 
+int64_t logit_pitch(const sfi_kv_desc* d) { return (d->kv_capacity + 63) / 64 * 64; }
+
 struct SlowLayout {
   size_t logits, part_ml, part_o, end;
 };
@@ -139,8 +166,8 @@ SlowLayout slow_layout(const sfi_kv_desc* d) {
   SlowLayout L;
   const size_t heads = static_cast<size_t>(d->batch) * d->n_q_heads;
   const size_t stride = static_cast<size_t>(slow_part_stride(d));
-  L.logits = counter_bytes(d);
-  L.part_ml = L.logits + align_up(heads * d->kv_capacity * sizeof(float));
+  L.logits = header_bytes(d);
+  L.part_ml = L.logits + align_up(heads * static_cast<size_t>(logit_pitch(d)) * sizeof(float));
   L.part_o = L.part_ml + align_up(heads * stride * 2 * sizeof(float));
   L.end = L.part_o + align_up(heads * stride * d->head_dim * sizeof(float));
   return L;
@@ -158,7 +185,7 @@ FastLayout fast_layout(const sfi_kv_desc* d, const sfi_support_params* sp) {
   FastLayout L;
   const size_t heads = static_cast<size_t>(d->batch) * d->n_q_heads;
   const size_t stride = static_cast<size_t>(fast_part_stride(sp));
-  L.part_ml = counter_bytes(d);
+  L.part_ml = header_bytes(d);
   L.part_o = L.part_ml + align_up(heads * stride * 2 * sizeof(float));
   L.end = L.part_o + align_up(heads * stride * d->head_dim * sizeof(float));
   return L;
@@ -265,7 +292,7 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp
     case SFI_OP_SLOW: return slow_layout(desc).end;
     case SFI_OP_SELECT:
       if (check_params(sp) != SFI_OK) return 0;
-      return counter_bytes(desc);
+      return select_layout(desc).end;
     case SFI_OP_FAST:
       if (check_params(sp) != SFI_OK) return 0;
       return fast_layout(desc, sp).end;
@@ -309,9 +336,13 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
     a.n_kv_heads = desc->n_kv_heads;
     a.part_stride = slow_part_stride(desc);
     a.scale_log2 = logit_scale(desc);
+    a.logit_pitch = logit_pitch(desc);
     int64_t rows = 0;
     for (int i = 0; i < cnt; ++i) rows += static_cast<int64_t>(desc->ctx_len_host[ids[i]]) * desc->n_kv_heads;
-    const int64_t per = ceil_div(rows, target);
+    int64_t t_max = 1;
+    for (int i = 0; i < cnt; ++i) t_max = std::max<int64_t>(t_max, desc->ctx_len_host[ids[i]]);
+    // at most kMaxMergeSlots splits per head (the merge stages them in LDS)
+    const int64_t per = std::max(ceil_div(rows, target), ceil_div(t_max, kMaxMergeSlots));
     a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
     CombineArgs c{};
     a.tab.n = cnt;
@@ -340,6 +371,7 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
     c.n_q_heads = a.n_q_heads;
     c.n_kv_heads = a.n_kv_heads;
     c.part_stride = a.part_stride;
+    c.logit_pitch = a.logit_pitch;
     hipError_t e = timed(SFI_K_SLOW_PARTIAL, s, [&] {
       return launch_slow_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
     });
@@ -363,62 +395,87 @@ int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const 
   if (n_seq == 0) return SFI_OK;
   if (mass == nullptr || sel_idx == nullptr || sel_cnt == nullptr)
     return fail(SFI_ERR_INVALID_ARG, "mass / sel_idx / sel_cnt is NULL");
-  (void)ws;
-  (void)ws_bytes;
+  const SelectLayout L = select_layout(desc);
+  const Header H = header_layout(desc);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SelectArgs a{};
     a.mass = mass;
     a.sel_idx = sel_idx;
     a.sel_cnt = sel_cnt;
+    a.hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
+    a.list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
+    a.list = reinterpret_cast<uint64_t*>(w + L.list);
+    a.chunk_above = reinterpret_cast<int32_t*>(w + L.chunk_above);
+    a.chunk_off = reinterpret_cast<int32_t*>(w + L.chunk_off);
+    a.kstar = reinterpret_cast<uint64_t*>(w + L.kstar);
     a.t_cap = desc->kv_capacity;
     a.n_kv_heads = desc->n_kv_heads;
     a.n_sink = sp->n_sink;
     a.n_recent = sp->n_recent;
     a.top_k = sp->top_k;
     a.lambda = sp->lambda;
+    int64_t n_max = 0;
+    for (int i = 0; i < cnt; ++i)
+      n_max = std::max<int64_t>(n_max, desc->ctx_len_host[ids[i]] - static_cast<int64_t>(sp->n_sink) - sp->n_recent);
+    const int64_t chunk = std::max<int64_t>(kSelMinChunk, ceil_div(ceil_div(n_max, kSelMaxChunks), 512) * 512);
+    a.chunk = static_cast<int32_t>(chunk);
     a.tab.n = cnt;
+    a.tab.wg_begin[0] = 0;
     for (int i = 0; i < cnt; ++i) {
+      const int64_t T = desc->ctx_len_host[ids[i]];
+      const int64_t n = std::max<int64_t>(0, T - sp->n_sink - sp->n_recent);
+      const bool keep_all = n <= sp->top_k || sp->top_k == 0;
+      const int64_t M = keep_all ? std::max<int64_t>(1, ceil_div(sp->top_k, chunk)) : ceil_div(n, chunk);
       a.tab.seq[i] = ids[i];
-      a.tab.ctx[i] = desc->ctx_len_host[ids[i]];
-      a.tab.nsplit[i] = 1;
-      a.tab.wg_begin[i] = i * desc->n_kv_heads;
+      a.tab.ctx[i] = static_cast<int32_t>(T);
+      a.tab.nsplit[i] = static_cast<int32_t>(M);
+      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
     }
-    a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;
-    const hipError_t e = timed(SFI_K_SELECT, s, [&] { return launch_select(a, cnt * desc->n_kv_heads, s); });
+    const int grid = a.tab.wg_begin[cnt];
+    const hipError_t e = timed(SFI_K_SELECT, s, [&] { return launch_select(a, grid, s); });
     return e == hipSuccess ? SFI_OK : hip_fail(e, "select launch");
   });
 }
 
-int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids, int32_t n_seq,
-                      const void* q, const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
-                      size_t ws_bytes, void* stream) {
+static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                              int32_t n_seq, const void* q, const int32_t* sel_idx, const void* packed_k,
+                              const void* packed_v, const int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes,
+                              void* stream) {
   int32_t st;
   if ((st = check_desc(desc)) != SFI_OK) return st;
   if ((st = check_kv(desc)) != SFI_OK) return st;
   if ((st = check_params(sp)) != SFI_OK) return st;
   if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
   if (n_seq == 0) return SFI_OK;
-  if (q == nullptr || out == nullptr || sel_idx == nullptr || sel_cnt == nullptr)
-    return fail(SFI_ERR_INVALID_ARG, "q / out / sel_idx / sel_cnt is NULL");
+  if (q == nullptr || out == nullptr || sel_cnt == nullptr)
+    return fail(SFI_ERR_INVALID_ARG, "q / out / sel_cnt is NULL");
+  if (sel_idx == nullptr && (packed_k == nullptr || packed_v == nullptr))
+    return fail(SFI_ERR_INVALID_ARG, "sel_idx (or packed_k / packed_v) is NULL");
   if (sp->n_sink == 0 && sp->n_recent == 0 && sp->top_k == 0)
     return fail(SFI_ERR_INVALID_ARG, "the support is empty (n_sink = n_recent = top_k = 0)");
+  const int crow = fast_chunk_rows();
+  if (static_cast<int64_t>(sp->n_sink) + sp->n_recent + sp->top_k > static_cast<int64_t>(crow) * kMaxMergeSlots)
+    return fail(SFI_ERR_UNSUPPORTED, "support of %lld rows exceeds %d",
+                static_cast<long long>(sp->n_sink) + sp->n_recent + sp->top_k, crow * kMaxMergeSlots);
   const FastLayout L = fast_layout(desc, sp);
   if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = desc->n_q_heads / desc->n_kv_heads;
-  const int crow = fast_chunk_rows();
   char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     FastArgs a{};
     a.k = desc->k;
     a.v = desc->v;
+    a.packed_k = packed_k;
+    a.packed_v = packed_v;
     a.q = q;
     a.sel_idx = sel_idx;
     a.sel_cnt = sel_cnt;
     a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
     a.part_o = reinterpret_cast<float*>(w + L.part_o);
-    a.counter = reinterpret_cast<int32_t*>(w);
     a.out = out;
     a.t_cap = desc->kv_capacity;
     a.n_q_heads = desc->n_q_heads;
@@ -448,6 +505,63 @@ int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp, con
       return launch_fast(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
     });
     return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
+  });
+}
+
+int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids, int32_t n_seq,
+                      const void* q, const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (sel_idx == nullptr) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
+  return fast_step_impl(desc, sp, seq_ids, n_seq, q, sel_idx, nullptr, nullptr, sel_cnt, out, ws, ws_bytes, stream);
+}
+
+int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                             int32_t n_seq, const void* q, const void* packed_k, const void* packed_v,
+                             const int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (packed_k == nullptr || packed_v == nullptr) return fail(SFI_ERR_INVALID_ARG, "packed_k / packed_v is NULL");
+  return fast_step_impl(desc, sp, seq_ids, n_seq, q, nullptr, packed_k, packed_v, sel_cnt, out, ws, ws_bytes,
+                        stream);
+}
+
+int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                         int32_t n_seq, const int32_t* sel_idx, const int32_t* sel_cnt, void* packed_k,
+                         void* packed_v, void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_kv(desc)) != SFI_OK) return st;
+  if ((st = check_params(sp)) != SFI_OK) return st;
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (n_seq == 0 || sp->top_k == 0) return SFI_OK;
+  if (sel_idx == nullptr || sel_cnt == nullptr || packed_k == nullptr || packed_v == nullptr)
+    return fail(SFI_ERR_INVALID_ARG, "sel_idx / sel_cnt / packed_k / packed_v is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    PackArgs a{};
+    a.k = desc->k;
+    a.v = desc->v;
+    a.packed_k = packed_k;
+    a.packed_v = packed_v;
+    a.sel_idx = sel_idx;
+    a.sel_cnt = sel_cnt;
+    a.t_cap = desc->kv_capacity;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.n_sink = sp->n_sink;
+    a.n_recent = sp->n_recent;
+    a.top_k = sp->top_k;
+    a.tab.n = cnt;
+    a.tab.wg_begin[0] = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const int64_t t = desc->ctx_len_host[ids[i]];
+      const int64_t kmax = std::min<int64_t>(sp->top_k, std::max<int64_t>(0, t - sp->n_sink - sp->n_recent));
+      a.tab.seq[i] = ids[i];
+      a.tab.ctx[i] = static_cast<int32_t>(t);
+      a.tab.nsplit[i] = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(kmax, kPackRows)));
+      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+    }
+    const hipError_t e = timed(SFI_K_PACK, s, [&] {
+      return launch_pack(a, desc->kv_dtype, desc->head_dim, a.tab.wg_begin[cnt], s);
+    });
+    return e == hipSuccess ? SFI_OK : hip_fail(e, "pack launch");
   });
 }
 

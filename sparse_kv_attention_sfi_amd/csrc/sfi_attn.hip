@@ -10,9 +10,13 @@
 //  * slow_combine: merges the split partials into the output and writes the
 //    Selector's evidence, the softmax mass averaged over the query group
 //    (2.B "Der Training-Free Selector").
-//  * fast: attention restricted to sinks + recent window + selected memory
-//    (2.A, items 1-3), gathering K/V rows by index; the last workgroup of each
-//    (sequence, KV head) merges the chunk partials.
+//  * fast_partial / fast_merge: attention restricted to sinks + recent window
+//    + selected memory (2.A, items 1-3), gathering K/V rows by index in
+//    chunks, then merging the chunk partials of each (sequence, KV head).
+//
+// Workgroups never hand data to each other inside a kernel: on gfx950 a
+// device-scope fence writes back and invalidates the XCD's L2, which is far
+// more expensive than the kernel boundary between a partial and a merge pass.
 //
 // Work layout inside a wave (64 lanes), per 16-row tile of K:
 //   logits   S[h][j] = q_h . k_j come from MFMA 16x16 (bf16: 16x16x32,
@@ -29,6 +33,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "sfi_device.hpp"
 #include "sfi_internal.hpp"
@@ -340,8 +345,8 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
       const int row = min(r0 + vr + A::kRPL * i, r_end - 1);
       vb[i] = ld16(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
     }
-    float* lrow = a.logits ? a.logits + qh0 * a.t_cap + r0 + kr : nullptr;
-    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lrow, a.t_cap, lane);
+    float* lrow = a.logits ? a.logits + qh0 * a.logit_pitch + r0 + kr : nullptr;
+    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lrow, a.logit_pitch, lane);
   }
   st.finish_wave(s_m, s_l, s_o, wave, lane);
   __syncthreads();
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// slow step, kernel 2: merge partials; per-position softmax mass
+// merging partial (max, sum, output) slots
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
   v = row16_max(v);
@@ -367,13 +372,154 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int kMaxSlots = kMaxMergeSlots;
+
+// Global max M_h and 1 / L_h of NH heads over n slots; ml of head h is at
+// ml + h * ml_hstride as (m, l) pairs.  Ends with a barrier.
+template <int NH, int NW>
+__device__ __forceinline__ void head_max_sum(const float* ml, int64_t ml_hstride, int n, float* sM,
+                                             float* sInvL) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int h = wave; h < NH; h += NW) {
+    const float* p = ml + h * ml_hstride;
+    float m = -INFINITY;
+    for (int s = lane; s < n; s += 64) m = fmaxf(m, p[2 * s]);
+    m = wave_max(m);
+    float l = 0.f;
+    if (m != -INFINITY) {
+      for (int s = lane; s < n; s += 64) {
+        const float ms = p[2 * s];
+        if (ms != -INFINITY) l += p[2 * s + 1] * fast_exp2(ms - m);
+      }
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      sM[h] = m;
+      sInvL[h] = l > 0.f ? 1.f / l : 0.f;
+    }
+  }
+  __syncthreads();
+}
+
+template <int NH, int NT>
+struct MergeSmem {
+  float m[NH * kMaxSlots];
+  float l[NH * kMaxSlots];
+  float M[NH];
+  float invL[NH];
+  float4 red[NT];
+};
+
+// out[h * D + d] = sum_s exp2(m_hs - M_h) / L_h * o_hs[d] for NH heads over
+// n <= kMaxSlots partial slots.  Each thread owns one float4 column of one
+// head for a strided subset of the slots.  Its first kPrefetch output loads
+// are issued together with the (m, l) loads, so a merge of up to
+// kPrefetch * NSUB slots costs a single round trip to memory.
+template <int D, int NH, int NT>
+__device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_hstride, const float* po,
+                                               int64_t po_hstride, int n, float* out,
+                                               MergeSmem<NH, NT>& sm) {
+  constexpr int C4 = D / 4;
+  constexpr int NC = NH * C4;
+  static_assert(NC <= NT, "one column per thread at least");
+  constexpr int NSUB = NT / NC;
+  constexpr int NW = NT / 64;
+  constexpr int kPrefetch = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = tid % NC, sub = tid / NC;
+  const int h = col / C4, c4 = col - h * C4;
+  const bool active = sub < NSUB;
+  const float* base = po + h * po_hstride + 4 * c4;
+  float4 v[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) {
+    const int s = sub + u * NSUB;
+    v[u] = (active && s < n) ? *reinterpret_cast<const float4*>(base + static_cast<int64_t>(s) * D)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int i = tid; i < NH * n; i += NT) {
+    const int hh = i / n, s = i - hh * n;
+    const float2 p = *reinterpret_cast<const float2*>(ml + hh * ml_hstride + 2 * s);
+    sm.m[hh * kMaxSlots + s] = p.x;
+    sm.l[hh * kMaxSlots + s] = p.y;
+  }
+  __syncthreads();
+  for (int hh = wave; hh < NH; hh += NW) {
+    float m = -INFINITY;
+    for (int s = lane; s < n; s += 64) m = fmaxf(m, sm.m[hh * kMaxSlots + s]);
+    m = wave_max(m);
+    float l = 0.f;
+    if (m != -INFINITY) {
+      for (int s = lane; s < n; s += 64) {
+        const float ms = sm.m[hh * kMaxSlots + s];
+        if (ms != -INFINITY) l += sm.l[hh * kMaxSlots + s] * fast_exp2(ms - m);
+      }
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      sm.M[hh] = m;
+      sm.invL[hh] = l > 0.f ? 1.f / l : 0.f;
+    }
+  }
+  __syncthreads();
+  const float M = sm.M[h], il = sm.invL[h];
+  const float* mh = sm.m + h * kMaxSlots;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int s = sub + u * NSUB;
+      if (s < n && mh[s] != -INFINITY) {
+        const float w = fast_exp2(mh[s] - M) * il;
+        acc.x += w * v[u].x; acc.y += w * v[u].y; acc.z += w * v[u].z; acc.w += w * v[u].w;
+      }
+    }
+    for (int s0 = sub + kPrefetch * NSUB; s0 < n; s0 += kPrefetch * NSUB) {
+      float4 x[kPrefetch];
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        const int s = s0 + u * NSUB;
+        x[u] = s < n ? *reinterpret_cast<const float4*>(base + static_cast<int64_t>(s) * D)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        const int s = s0 + u * NSUB;
+        if (s < n && mh[s] != -INFINITY) {
+          const float w = fast_exp2(mh[s] - M) * il;
+          acc.x += w * x[u].x; acc.y += w * x[u].y; acc.z += w * x[u].z; acc.w += w * x[u].w;
+        }
+      }
+    }
+  }
+  if constexpr (NSUB > 1) {
+    sm.red[tid] = acc;
+    __syncthreads();
+    if (sub == 0) {
+      float4 t = acc;
+#pragma unroll
+      for (int u = 1; u < NSUB; ++u) {
+        const float4 x = sm.red[u * NC + col];
+        t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+      }
+      *reinterpret_cast<float4*>(out + h * D + 4 * c4) = t;
+    }
+  } else {
+    if (active) *reinterpret_cast<float4*>(out + h * D + 4 * c4) = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// slow step, kernel 2: merge partials; per-position softmax mass
+// ---------------------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineArgs a) {
   constexpr int NW = kCombineThreads / 64;
+  constexpr int PER = kMassChunk / (4 * kCombineThreads);  // float4 groups per thread
   __shared__ float s_M[G], s_invL[G];
-  __shared__ float s_red[kCombineThreads];
+  __shared__ MergeSmem<1, kCombineThreads> s_merge;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int wg = blockIdx.x;
   const int e = find_entry(a.tab, wg);
   const int local = wg - a.tab.wg_begin[e];
@@ -385,58 +531,50 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
   const int T = a.tab.ctx[e];
   const int nsplit = a.tab.nsplit[e];
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
-
-  // global max and sum of each head of the group over all splits
-  for (int h = wave; h < G; h += NW) {
-    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
-    float m = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, ml[2 * s]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float ms = ml[2 * s];
-      if (ms != -INFINITY) l += ml[2 * s + 1] * fast_exp2(ms - m);
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      s_M[h] = m;
-      s_invL[h] = 1.f / l;
-    }
-  }
-  __syncthreads();
+  const int64_t ml_hstride = static_cast<int64_t>(a.part_stride) * 2;
+  const float* ml = a.part_ml + qh0 * ml_hstride;
 
   if (r < mblocks) {
+    // f_j = (1/G) sum_h exp2(x_hj - M_h) / L_h, four positions per thread; the
+    // logit loads are issued before the (m, l) loads so both share a round trip
     const int j0 = r * kMassChunk;
     const int j1 = min(T, j0 + kMassChunk);
-    const float* lg = a.logits + qh0 * a.t_cap;
+    const float* lg = a.logits + qh0 * a.logit_pitch;
     float* mrow = a.mass + (static_cast<int64_t>(b) * a.n_kv_heads + g) * a.t_cap;
-    const float invG = 1.f / static_cast<float>(G);
-    for (int j = j0 + tid; j < j1; j += kCombineThreads) {
-      float f = 0.f;
+    float4 x[PER][G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) f += fast_exp2(lg[h * a.t_cap + j] - s_M[h]) * s_invL[h];
-      mrow[j] = f * invG;
+    for (int it = 0; it < PER; ++it) {
+      const int j = j0 + 4 * (it * kCombineThreads + tid);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        x[it][h] = j < j1 ? *reinterpret_cast<const float4*>(lg + h * a.logit_pitch + j)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    head_max_sum<G, NW>(ml, ml_hstride, nsplit, s_M, s_invL);
+    const float invG = 1.f / static_cast<float>(G);
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int j = j0 + 4 * (it * kCombineThreads + tid);
+      if (j >= j1) continue;
+      float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float M = s_M[h], il = s_invL[h];
+        f[0] += fast_exp2(x[it][h].x - M) * il;
+        f[1] += fast_exp2(x[it][h].y - M) * il;
+        f[2] += fast_exp2(x[it][h].z - M) * il;
+        f[3] += fast_exp2(x[it][h].w - M) * il;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j + u < j1) mrow[j + u] = f[u] * invG;
     }
   } else {
     const int h = r - mblocks;
-    constexpr int NSUB = kCombineThreads / D;
-    const int d = tid % D, sub = tid / D;
-    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
-    const float* po = a.part_o + (qh0 + h) * a.part_stride * D;
-    const float M = s_M[h];
-    float acc = 0.f;
-    for (int s = sub; s < nsplit; s += NSUB) {
-      const float ms = ml[2 * s];
-      if (ms != -INFINITY) acc += po[static_cast<int64_t>(s) * D + d] * fast_exp2(ms - M);
-    }
-    s_red[tid] = acc;
-    __syncthreads();
-    if (sub == 0) {
-      float o = 0.f;
-#pragma unroll
-      for (int u = 0; u < NSUB; ++u) o += s_red[u * D + d];
-      a.out[(qh0 + h) * D + d] = o * s_invL[h];
-    }
+    merge_partials<D, 1, kCombineThreads>(ml + h * ml_hstride, ml_hstride,
+                                          a.part_o + (qh0 + h) * a.part_stride * D,
+                                          static_cast<int64_t>(a.part_stride) * D, nsplit,
+                                          a.out + (qh0 + h) * D, s_merge);
   }
 }
 
@@ -476,7 +614,7 @@ __device__ __forceinline__ int support_pos(const SupportGeom& s, int p, int t,
 }
 
 template <typename E, int D, int G, int TILES>
-__global__ __launch_bounds__(kFastThreads) void fast_kernel(FastArgs a) {
+__global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
   constexpr int ROWS = TILES * 16;  // rows per wave
@@ -488,8 +626,6 @@ __global__ __launch_bounds__(kFastThreads) void fast_kernel(FastArgs a) {
   __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
   __shared__ float s_m[NW * G], s_l[NW * G];
   __shared__ int s_pos[CH];
-  __shared__ int s_last;
-  __shared__ float s_M[G], s_invL[G];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
@@ -551,48 +687,167 @@ __global__ __launch_bounds__(kFastThreads) void fast_kernel(FastArgs a) {
   merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
                                   static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
                                   static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
+}
 
-  // arrival: the last workgroup of this (sequence, KV head) merges the chunks
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(a.counter + bg, 1);
-    s_last = (prev == nchunk - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+// Fast step over the packed support: the selected rows were copied into a
+// contiguous buffer after the slow step (the memory-coalesced sparse layout
+// of "Slow-Fast Inference ...", gist.science technical summary, 3
+// "Systemdesign und Kernel-Optimierung"); sinks and the recent window are
+// read from the cache.  Every row address follows from host-known lengths,
+// so all K/V loads are issued at once with no index lookups; only the end of
+// the selected rows (sel_cnt) masks the tail.
+template <typename E, int D, int G, int TILES>
+__global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
+  using A = Attn<E, D, G>;
+  constexpr int RB = A::kRowBytes;
+  constexpr int ROWS = TILES * 16;
+  constexpr int NW = kFastThreads / 64;
+  constexpr int NV = ROWS / A::kRPL;
 
-  for (int h = wave; h < G; h += NW) {
-    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
-    float m = -INFINITY;
-    for (int s = lane; s < nchunk; s += 64) m = fmaxf(m, ml[2 * s]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int s = lane; s < nchunk; s += 64) {
-      const float ms = ml[2 * s];
-      if (ms != -INFINITY) l += ml[2 * s + 1] * fast_exp2(ms - m);
+  __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
+  __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
+  __shared__ float s_m[NW * G], s_l[NW * G];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wg = blockIdx.x;
+  const int e = find_entry(a.tab, wg);
+  const int local = wg - a.tab.wg_begin[e];
+  const int nchunk = a.tab.nsplit[e];
+  const int g = local / nchunk;
+  const int chunk = local - g * nchunk;
+  const int b = a.tab.seq[e];
+  const int t = a.tab.ctx[e];
+  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  const int ns_eff = min(a.n_sink, t);
+  const int w_lo = max(a.n_sink, t - a.n_recent);
+  const int w_eff = max(0, t - w_lo);
+  const int kmax = min(a.top_k, max(0, t - a.n_sink - a.n_recent));
+  const int fixed = ns_eff + w_eff;
+  const char* Kc = static_cast<const char*>(a.k) + bg * a.t_cap * RB;
+  const char* Vc = static_cast<const char*>(a.v) + bg * a.t_cap * RB;
+  const char* Kp = static_cast<const char*>(a.packed_k) + bg * a.top_k * RB;
+  const char* Vp = static_cast<const char*>(a.packed_v) + bg * a.top_k * RB;
+  const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
+  // byte offset of support row p from the cache or packed base
+  auto row_off = [&](int p, bool& packed) -> int64_t {
+    packed = false;
+    if (p < ns_eff) return static_cast<int64_t>(p) * RB;
+    if (p < fixed) return static_cast<int64_t>(w_lo + p - ns_eff) * RB;
+    const int qrow = p - fixed;
+    if (qrow < kmax) {
+      packed = true;
+      return static_cast<int64_t>(qrow) * RB;
     }
-    l = wave_sum(l);
-    if (lane == 0) {
-      s_M[h] = m;
-      s_invL[h] = 1.f / l;
+    return 0;
+  };
+
+  uint4 qa[A::kNL];
+  load_q<E, D, G>(a.q, qh0, lane, qa);
+  A st;
+  st.init();
+  const int w0 = chunk * (NW * ROWS) + wave * ROWS;  // first support row of this wave
+  const int kr = lane & 15, kg = lane >> 4;
+  const int vr = lane / A::kPPR, vp = lane % A::kPPR;
+  uint4 kb[TILES][A::kNL];
+  uint4 vb[NV];
+#pragma unroll
+  for (int tt = 0; tt < TILES; ++tt) {
+    bool pk;
+    const int64_t off = row_off(w0 + 16 * tt + kr, pk);
+    const char* src = (pk ? Kp : Kc) + off + 16 * kg;
+#pragma unroll
+    for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16(src + 64 * kk);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    bool pk;
+    const int64_t off = row_off(w0 + vr + A::kRPL * i, pk);
+    vb[i] = ld16((pk ? Vp : Vc) + off + 16 * vp);
+  }
+  const int cnt = min(max(a.sel_cnt[bg], 0), kmax);
+  const int size = fixed + cnt;
+  bool kvalid[TILES];
+#pragma unroll
+  for (int tt = 0; tt < TILES; ++tt) kvalid[tt] = (w0 + 16 * tt + kr) < size;
+  if (w0 < size) {
+    st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, lane);
+  }
+  st.finish_wave(s_m, s_l, s_o, wave, lane);
+  __syncthreads();
+  const int64_t slot = qh0 * a.part_stride + chunk;
+  merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
+                                  static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
+                                  static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
+}
+
+// Copies the selected K/V rows of each (sequence, KV head) into the packed
+// buffers: packed[i] = cache[sel_idx[i]] for i < sel_cnt.
+template <int RB>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+  constexpr int NP = RB / 16;  // 16-byte pieces per row
+  __shared__ int s_row[kPackRows];
+  const int wg = blockIdx.x;
+  const int e = find_entry(a.tab, wg);
+  const int local = wg - a.tab.wg_begin[e];
+  const int nchunk = a.tab.nsplit[e];
+  const int g = local / nchunk;
+  const int chunk = local - g * nchunk;
+  const int b = a.tab.seq[e];
+  const int t = a.tab.ctx[e];
+  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  const int kmax = min(a.top_k, max(0, t - a.n_sink - a.n_recent));
+  const int cnt = min(max(a.sel_cnt[bg], 0), kmax);
+  const int r0 = chunk * kPackRows;
+  for (int i = threadIdx.x; i < kPackRows; i += 256) {
+    const int r = r0 + i;
+    int j = -1;
+    if (r < cnt) {
+      j = a.sel_idx[bg * a.top_k + r];
+      if (j < 0 || j >= t) j = -1;
     }
+    s_row[i] = j;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kFastThreads) {
-    const int h = idx / D, d = idx - h * D;
-    const float* ml = a.part_ml + (qh0 + h) * a.part_stride * 2;
-    const float* po = a.part_o + (qh0 + h) * a.part_stride * D;
-    const float M = s_M[h];
-    float acc = 0.f;
-    for (int s = 0; s < nchunk; ++s) {
-      const float ms = ml[2 * s];
-      if (ms != -INFINITY) acc += po[static_cast<int64_t>(s) * D + d] * fast_exp2(ms - M);
-    }
-    a.out[(qh0 + h) * D + d] = acc * s_invL[h];
+  const char* K = static_cast<const char*>(a.k) + bg * a.t_cap * RB;
+  const char* V = static_cast<const char*>(a.v) + bg * a.t_cap * RB;
+  char* PK = static_cast<char*>(a.packed_k) + bg * a.top_k * RB;
+  char* PV = static_cast<char*>(a.packed_v) + bg * a.top_k * RB;
+  constexpr int kItems = kPackRows * NP * 2;
+  constexpr int kPer = kItems / 256;
+  uint4 val[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int item = threadIdx.x + 256 * u;
+    const int isv = item >= kPackRows * NP;
+    const int rem = isv ? item - kPackRows * NP : item;
+    const int row = rem / NP, pc = rem - row * NP;
+    const int j = s_row[row];
+    val[u] = j >= 0 ? ld16((isv ? V : K) + static_cast<int64_t>(j) * RB + 16 * pc) : make_uint4(0u, 0u, 0u, 0u);
   }
-  if (tid == 0) a.counter[bg] = 0;  // ready for the next launch
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int item = threadIdx.x + 256 * u;
+    const int isv = item >= kPackRows * NP;
+    const int rem = isv ? item - kPackRows * NP : item;
+    const int row = rem / NP, pc = rem - row * NP;
+    if (s_row[row] >= 0)
+      *reinterpret_cast<uint4*>((isv ? PV : PK) + static_cast<int64_t>(r0 + row) * RB + 16 * pc) = val[u];
+  }
+}
+
+// Merge of the chunk partials of one (sequence, KV head): the output of its G
+// query heads, renormalised over the whole support.
+template <int D, int G>
+__global__ __launch_bounds__(kMergeThreads) void fast_merge_kernel(FastArgs a) {
+  __shared__ MergeSmem<G, kMergeThreads> s_merge;
+  const int e = blockIdx.x / a.n_kv_heads;
+  const int g = blockIdx.x - e * a.n_kv_heads;
+  const int b = a.tab.seq[e];
+  const int nchunk = a.tab.nsplit[e];
+  const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
+  const int64_t ml_hstride = static_cast<int64_t>(a.part_stride) * 2;
+  merge_partials<D, G, kMergeThreads>(a.part_ml + qh0 * ml_hstride, ml_hstride, a.part_o + qh0 * a.part_stride * D,
+                                      static_cast<int64_t>(a.part_stride) * D, nchunk, a.out + qh0 * D, s_merge);
 }
 
 // ---------------------------------------------------------------------------
@@ -679,20 +934,51 @@ hipError_t launch_slow_combine(const CombineArgs& a, int head_dim, int group, in
                          : slow_combine_g<64>(a, group, grid, s);
 }
 
-// Fast-step rows per wave: one 16-row tile keeps many small workgroups in
-// flight, which is what a latency-bound gather of ~10 MB needs.
-constexpr int kFastTiles = 1;
+// Fast-step rows per wave (16 per tile).  Small chunks keep many workgroups
+// in flight, which a latency-bound gather of ~10 MB needs; the count is a
+// launch parameter (1, 2 or 4 tiles per wave).
+int fast_tiles() {
+  static const int t = [] {
+    const char* s = std::getenv("SFI_FAST_TILES");
+    const int v = s ? std::atoi(s) : 1;
+    return (v == 2 || v == 4) ? v : 1;
+  }();
+  return t;
+}
+
+int fast_chunk_rows() { return (kFastThreads / 64) * fast_tiles() * 16; }
+
+template <typename E, int D, int G, int TILES>
+static void fast_partial_launch(const FastArgs& a, int grid, hipStream_t s) {
+  if (a.packed_k != nullptr) {
+    fast_packed_kernel<E, D, G, TILES><<<grid, kFastThreads, 0, s>>>(a);
+  } else {
+    fast_partial_kernel<E, D, G, TILES><<<grid, kFastThreads, 0, s>>>(a);
+  }
+}
+
+template <typename E, int D, int G>
+static hipError_t fast_pair(const FastArgs& a, int grid, hipStream_t s) {
+  switch (a.chunk_rows / ((kFastThreads / 64) * 16)) {
+    case 4: fast_partial_launch<E, D, G, 4>(a, grid, s); break;
+    case 2: fast_partial_launch<E, D, G, 2>(a, grid, s); break;
+    default: fast_partial_launch<E, D, G, 1>(a, grid, s); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  fast_merge_kernel<D, G><<<a.tab.n * a.n_kv_heads, kMergeThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 template <typename E, int D>
 static hipError_t fast_g(const FastArgs& a, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: fast_kernel<E, D, 1, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
-    case 2: fast_kernel<E, D, 2, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
-    case 4: fast_kernel<E, D, 4, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
-    case 8: fast_kernel<E, D, 8, kFastTiles><<<grid, kFastThreads, 0, s>>>(a); break;
+    case 1: return fast_pair<E, D, 1>(a, grid, s);
+    case 2: return fast_pair<E, D, 2>(a, grid, s);
+    case 4: return fast_pair<E, D, 4>(a, grid, s);
+    case 8: return fast_pair<E, D, 8>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_fast(const FastArgs& a, int dtype, int head_dim, int group, int grid,
@@ -703,10 +989,20 @@ hipError_t launch_fast(const FastArgs& a, int dtype, int head_dim, int group, in
   return head_dim == 128 ? fast_g<F32, 128>(a, group, grid, s) : fast_g<F32, 64>(a, group, grid, s);
 }
 
-int fast_chunk_rows() { return (kFastThreads / 64) * kFastTiles * 16; }
 
 hipError_t launch_support(const SupportArgs& a, int grid, hipStream_t s) {
   support_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const PackArgs& a, int dtype, int head_dim, int grid, hipStream_t s) {
+  const int rb = head_dim * (dtype == SFI_BF16 ? 2 : 4);
+  switch (rb) {
+    case 128: pack_kernel<128><<<grid, 256, 0, s>>>(a); break;
+    case 256: pack_kernel<256><<<grid, 256, 0, s>>>(a); break;
+    case 512: pack_kernel<512><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -15,10 +15,15 @@ constexpr int kMaxSeqPerLaunch = 64;
 
 // Workgroup shapes.
 constexpr int kSlowThreads = 256;    // 4 waves, split-K partial kernel
-constexpr int kCombineThreads = 256; // merge + mass kernel
-constexpr int kMassChunk = 4096;     // positions per mass workgroup
-constexpr int kSelectThreads = 1024; // one workgroup per (sequence, KV head)
+constexpr int kCombineThreads = 1024; // merge + mass kernel
+constexpr int kMassChunk = 8192;      // positions per mass workgroup
+constexpr int kSelThreads = 512;     // Selector workgroups
+constexpr int kSelListCap = 8192;    // threshold-bin keys resolved in LDS
+constexpr int kSelMaxChunks = 1024;  // candidate chunks per (sequence, KV head)
+constexpr int kSelMinChunk = 4096;   // candidates per chunk (at least)
 constexpr int kFastThreads = 256;    // 4 waves, gather kernel
+constexpr int kMergeThreads = 1024;  // fast-step chunk merge
+constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a merge accepts
 
 struct SeqTable {
   int32_t n;                              // entries used
@@ -33,7 +38,7 @@ struct SlowArgs {
   const void* k;
   const void* v;
   const void* q;
-  float* logits;   // [B][Hq][T_cap] scaled log2-domain logits, or nullptr
+  float* logits;   // [B][Hq][logit_pitch] scaled log2-domain logits, or nullptr
   float* part_ml;  // [B][Hq][part_stride][2]  (running max, running sum)
   float* part_o;   // [B][Hq][part_stride][D]  un-normalised output
   float* out;      // [B][Hq][D]
@@ -44,6 +49,7 @@ struct SlowArgs {
   int32_t split_rows;   // rows per split-K workgroup (multiple of 4 * block rows)
   int32_t part_stride;  // max splits per head (workspace pitch)
   float scale_log2;     // logit scale times log2(e)
+  int64_t logit_pitch;  // floats per logit row (multiple of 64)
   SeqTable tab;
 };
 
@@ -57,6 +63,7 @@ struct CombineArgs {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t part_stride;
+  int64_t logit_pitch;
   SeqTable tab;  // nsplit = split-K splits; wg_begin counts combine workgroups
   int32_t mass_blocks[kMaxSeqPerLaunch];  // per entry: mass workgroups per KV head
 };
@@ -66,25 +73,35 @@ struct SelectArgs {
   const float* mass;
   int32_t* sel_idx;
   int32_t* sel_cnt;
+  // persistent bookkeeping (zero between calls)
+  uint32_t* hist;        // [B * Hkv][4096] top-digit histogram
+  int32_t* list_n;       // [B * Hkv] keys appended to the threshold-bin list
+  // per-call scratch
+  uint64_t* list;        // [B * Hkv][kSelListCap]
+  int32_t* chunk_above;  // [B * Hkv][kSelMaxChunks]
+  int32_t* chunk_off;    // [B * Hkv][kSelMaxChunks]
+  uint64_t* kstar;       // [B * Hkv]
   int64_t t_cap;
   int32_t n_kv_heads;
   int32_t n_sink;
   int32_t n_recent;
   int32_t top_k;
+  int32_t chunk;         // candidates per workgroup
   float lambda;
-  SeqTable tab;  // wg_begin = entry * Hkv
+  SeqTable tab;          // nsplit = chunks per KV head
 };
 
 // ---- fast step -----------------------------------------------------------
 struct FastArgs {
   const void* k;
   const void* v;
+  const void* packed_k;  // [B][Hkv][top_k][D] selected rows, or nullptr (gather by index)
+  const void* packed_v;
   const void* q;
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
   float* part_ml;   // [B][Hq][part_stride][2]
   float* part_o;    // [B][Hq][part_stride][D]
-  int32_t* counter; // [B][Hkv] arrival counters (zero between launches)
   float* out;
   int64_t t_cap;
   int32_t n_q_heads;
@@ -112,6 +129,21 @@ struct SupportArgs {
   SeqTable tab;
 };
 
+struct PackArgs {
+  const void* k;
+  const void* v;
+  void* packed_k;        // [B][Hkv][top_k][D]
+  void* packed_v;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  int64_t t_cap;
+  int32_t n_kv_heads;
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t top_k;
+  SeqTable tab;          // nsplit = row chunks per KV head
+};
+
 struct AppendArgs {
   void* k;
   void* v;
@@ -132,12 +164,15 @@ hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s);
 hipError_t launch_fast(const FastArgs& a, int dtype, int head_dim, int group, int grid,
                        hipStream_t s);
 hipError_t launch_support(const SupportArgs& a, int grid, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, int dtype, int head_dim, int grid, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int head_dim, int grid,
                          hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
-// Support rows handled by one fast-step workgroup.
+// Support rows handled by one fast-step workgroup; selected rows copied per
+// pack workgroup.
 int fast_chunk_rows();
+constexpr int kPackRows = 64;
 
 // Rows handled per wave per pipeline block: 16 KiB of K (and of V) per block.
 __host__ __device__ constexpr int block_rows(int row_bytes) { return 16384 / row_bytes; }

@@ -1,19 +1,33 @@
-// Selector kernel of the SFI path for gfx950 ("Slow-Fast Inference ...",
+// Selector kernels of the SFI path for gfx950 ("Slow-Fast Inference ...",
 // gist.science technical summary, 2.B "Der Training-Free Selector").
 //
-// One workgroup of 1024 threads per (sequence, KV head).  For the n
-// candidate positions [n_sink, T - n_recent) it forms
+// For each (sequence, KV head) the n candidate positions [n_sink, T - n_recent)
+// get the fused score
 //     s = (1 - lambda) * f + lambda * r,   r(a) = (1/a + 1/(n+1-a)) / (2 H_n)
-// (the closed-form mixture of evidence f and prior r; a is the 1-based
-// offset from the sinks) and keeps the k best.  Exact top-k is found by
-// radix selection on a 64-bit key that makes every candidate distinct:
+// (the closed-form mixture of the slow step's mass f with the prior r; a is
+// the 1-based offset from the sinks), and the k best are kept.  Exact top-k
+// uses a 64-bit key that makes every candidate distinct:
 //     key = order-preserving bits of s  << 32  |  ~position
-// so "larger key" means "higher score, or equal score and lower position".
-// The k-th largest key K* is resolved 12 bits at a time: each level builds an
-// LDS histogram of the next digit over the candidates that still match the
-// resolved prefix.  As soon as those candidates fit in LDS they are copied
-// there and the remaining levels run on the copy.  A final ordered pass
-// writes every position with key >= K* in ascending order.
+// so "larger key" means "higher score, or equal score and lower position";
+// the kept set is {key >= K*} with K* the k-th largest key.
+//
+// The candidates of a head are cut into chunks handled by separate
+// workgroups, so the selection of one head spreads over many CUs:
+//   1. select_hist:   histogram of the top 12 key bits, added into a
+//                     per-head global histogram.
+//   2. select_gather: every workgroup finds the bin d1 holding K*, counts its
+//                     keys above d1 and appends its keys in d1 to a per-head
+//                     list (one atomic per workgroup reserves its range).
+//   3. select_finish: one workgroup per head resolves K* inside the list in
+//                     LDS (12 bits per level), derives how many keys each
+//                     chunk keeps, turns that into output offsets, and clears
+//                     the head's histogram and list counter.  If d1 holds more
+//                     keys than fit in LDS, it resolves K* by radix passes
+//                     over all candidates instead.
+//   4. select_emit:   every workgroup writes the kept positions of its chunk
+//                     in ascending order at its offset.
+// Workgroups never hand data to each other inside a kernel: on gfx950 a
+// device-scope fence writes back and invalidates the XCD's L2.
 #include <math.h>
 
 #include "sfi_device.hpp"
@@ -23,8 +37,7 @@ namespace sfi {
 
 constexpr int kSelDigitBits = 12;
 constexpr int kSelBins = 1 << kSelDigitBits;
-constexpr int kSelListCap = 4096;  // candidates kept in LDS once few enough
-constexpr int kSelWaves = kSelectThreads / 64;
+constexpr int kSelWaves = kSelThreads / 64;
 
 struct ScoreParams {
   const float* f;   // mass row, shifted so that f[i] is candidate i
@@ -40,7 +53,7 @@ __device__ __forceinline__ uint64_t cand_key(const ScoreParams& p, int i) {
 #pragma clang fp contract(off)
   const float a = static_cast<float>(i + 1);
   const float b = static_cast<float>(p.n - i);
-  const float r = (1.0f / a + 1.0f / b) * p.inv_2h;
+  const float r = (__builtin_amdgcn_rcpf(a) + __builtin_amdgcn_rcpf(b)) * p.inv_2h;
   const float s = __builtin_fmaf(p.lambda, r, p.one_minus_lambda * p.f[i]);
   uint32_t u = __float_as_uint(s);
   u ^= (u & 0x80000000u) ? 0xffffffffu : 0x80000000u;  // order-preserving
@@ -48,8 +61,11 @@ __device__ __forceinline__ uint64_t cand_key(const ScoreParams& p, int i) {
   return (static_cast<uint64_t>(u) << 32) | static_cast<uint64_t>(~pos);
 }
 
-// Exclusive prefix sum over the 1024 threads, in thread order.  Returns the
-// exclusive prefix; *total receives the sum.  Contains two barriers.
+__device__ __forceinline__ int key_position(uint64_t key) {
+  return static_cast<int>(~static_cast<uint32_t>(key & 0xffffffffull));
+}
+
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -85,126 +101,299 @@ __device__ double harmonic_number(int n) {
   return log(x) + 0.57721566490153286061 + 1.0 / (2.0 * x) - 1.0 / (12.0 * x2) + 1.0 / (120.0 * x2 * x2);
 }
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-  __shared__ uint32_t s_hist[kSelBins];
-  __shared__ uint64_t s_list[kSelListCap];
-  __shared__ int s_wave[kSelWaves];
-  __shared__ int s_list_n;
-  __shared__ int s_digit, s_above;
-  __shared__ float s_inv2h;
+struct HeadCtx {
+  int e, g, c, b, T, n, M;
+  int64_t bg;
+  bool keep_all;
+};
 
-  const int tid = threadIdx.x;
-  const int e = blockIdx.x / a.n_kv_heads;
-  const int g = blockIdx.x - e * a.n_kv_heads;
-  const int b = a.tab.seq[e];
-  const int T = a.tab.ctx[e];
-  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
-  const int lo = a.n_sink;
-  const int n = max(0, T - a.n_recent - a.n_sink);
-  const int K = a.top_k;
-  int32_t* out = a.sel_idx + bg * K;
+__device__ __forceinline__ HeadCtx head_ctx(const SelectArgs& a) {
+  HeadCtx h;
+  const int wg = blockIdx.x;
+  h.e = find_entry(a.tab, wg);
+  const int local = wg - a.tab.wg_begin[h.e];
+  h.M = a.tab.nsplit[h.e];
+  h.g = local / h.M;
+  h.c = local - h.g * h.M;
+  h.b = a.tab.seq[h.e];
+  h.T = a.tab.ctx[h.e];
+  h.bg = static_cast<int64_t>(h.b) * a.n_kv_heads + h.g;
+  h.n = max(0, h.T - a.n_recent - a.n_sink);
+  h.keep_all = h.n <= a.top_k || a.top_k == 0;
+  return h;
+}
 
-  if (n <= K) {  // every candidate is kept (also covers n == 0)
-    for (int i = tid; i < K; i += kSelectThreads) out[i] = i < n ? lo + i : -1;
-    if (tid == 0) a.sel_cnt[bg] = n;
-    return;
-  }
-
-  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(n)));
-  __syncthreads();
+__device__ __forceinline__ ScoreParams score_params(const SelectArgs& a, const HeadCtx& h, float inv2h) {
   ScoreParams sp;
-  sp.f = a.mass + bg * a.t_cap + lo;
-  sp.n = n;
-  sp.lo = lo;
+  sp.f = a.mass + h.bg * a.t_cap + a.n_sink;
+  sp.n = h.n;
+  sp.lo = a.n_sink;
   sp.lambda = a.lambda;
   sp.one_minus_lambda = 1.0f - a.lambda;
-  sp.inv_2h = s_inv2h;
+  sp.inv_2h = inv2h;
+  return sp;
+}
 
-  uint64_t prefix = 0, pmask = 0;
-  int need = K;     // rank of K* among the candidates matching the prefix
-  int shift = 64;
-  bool in_lds = false;
-  int list_n = 0;
+// Digit d of a histogram (highest bins first) with
+// (count in higher bins) < need <= (count in higher bins) + hist[d].
+// Writes the digit and the count above it to s_res[0], s_res[1].
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int need, int* s_wave,
+                                           int* s_res) {
+  const int tid = threadIdx.x;
+  const int per = (nbins + kSelThreads - 1) / kSelThreads;
+  const int b0 = (kSelThreads - 1 - tid) * per;  // thread 0 owns the highest bins
+  int local = 0;
+  for (int u = 0; u < per; ++u)
+    if (b0 + u < nbins) local += static_cast<int>(hist[b0 + u]);
+  int tot;
+  const int above_me = block_excl_scan(local, s_wave, &tot);
+  if (above_me < need && need <= above_me + local) {
+    int run = above_me;
+    for (int u = per - 1; u >= 0; --u) {
+      const int bin = b0 + u;
+      if (bin >= nbins) continue;
+      const int c = static_cast<int>(hist[bin]);
+      if (run + c >= need) {
+        s_res[0] = bin;
+        s_res[1] = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Resolves the remaining digits of K* (below `shift`) among keys that match
+// `prefix` on `pmask`.  Keys come from `src(i)` for i < count.
+template <typename Src>
+__device__ uint64_t radix_resolve(Src src, int count, uint64_t prefix, uint64_t pmask, int shift, int need,
+                                  uint32_t* s_hist, int* s_wave, int* s_res) {
+  const int tid = threadIdx.x;
   while (shift > 0) {
     const int width = shift >= kSelDigitBits ? kSelDigitBits : shift;
     shift -= width;
     const uint32_t dmask = (1u << width) - 1u;
     const int nbins = 1 << width;
-    for (int i = tid; i < nbins; i += kSelectThreads) s_hist[i] = 0u;
+    for (int i = tid; i < nbins; i += kSelThreads) s_hist[i] = 0u;
     __syncthreads();
-    if (!in_lds) {
-      for (int i = tid; i < n; i += kSelectThreads) {
-        const uint64_t key = cand_key(sp, i);
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dmask], 1u);
-      }
-    } else {
-      for (int i = tid; i < list_n; i += kSelectThreads) {
-        const uint64_t key = s_list[i];
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dmask], 1u);
-      }
+    for (int i = tid; i < count; i += kSelThreads) {
+      const uint64_t key = src(i);
+      if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    // digit d with (count above d) < need <= (count above d) + hist[d]
-    {
-      const int per = (nbins + kSelectThreads - 1) / kSelectThreads;
-      const int t_hi = kSelectThreads - 1 - tid;  // scan from the top bins down
-      const int b0 = t_hi * per;
-      int local = 0;
-      for (int u = 0; u < per; ++u)
-        if (b0 + u < nbins) local += static_cast<int>(s_hist[b0 + u]);
-      int tot;
-      // thread 0 owns the highest bins, so the exclusive scan in thread order
-      // is the count in higher bins
-      const int above_me = block_excl_scan(local, s_wave, &tot);
-      (void)tot;
-      if (above_me < need && need <= above_me + local) {
-        int run = above_me;
-        for (int u = per - 1; u >= 0; --u) {
-          const int bin = b0 + u;
-          if (bin >= nbins) continue;
-          const int c = static_cast<int>(s_hist[bin]);
-          if (run + c >= need) {
-            s_digit = bin;
-            s_above = run;
-            break;
-          }
-          run += c;
-        }
-      }
-    }
-    __syncthreads();
-    const int digit = s_digit;
-    const int cnt = static_cast<int>(s_hist[digit]);
-    need -= s_above;
+    find_digit(s_hist, nbins, need, s_wave, s_res);
+    const int digit = s_res[0];
+    need -= s_res[1];
     prefix |= static_cast<uint64_t>(digit) << shift;
     pmask |= static_cast<uint64_t>(dmask) << shift;
-    __syncthreads();  // s_digit / s_hist reused by the next level
-    if (shift > 0 && !in_lds && cnt <= kSelListCap) {
-      if (tid == 0) s_list_n = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelectThreads) {
-        const uint64_t key = cand_key(sp, i);
-        if ((key & pmask) == prefix) {
-          const int slot = atomicAdd(&s_list_n, 1);
-          if (slot < kSelListCap) s_list[slot] = key;
-        }
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// 1. histogram of the top digit
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a) {
+  __shared__ uint32_t s_hist[kSelBins];
+  __shared__ float s_inv2h;
+  const HeadCtx h = head_ctx(a);
+  if (h.keep_all) return;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
+  for (int i = tid; i < kSelBins; i += kSelThreads) s_hist[i] = 0u;
+  __syncthreads();
+  const ScoreParams sp = score_params(a, h, s_inv2h);
+  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  for (int i = i0 + tid; i < i1; i += kSelThreads)
+    atomicAdd(&s_hist[cand_key(sp, i) >> (64 - kSelDigitBits)], 1u);
+  __syncthreads();
+  uint32_t* gh = a.hist + h.bg * kSelBins;
+  for (int i = tid; i < kSelBins; i += kSelThreads)
+    if (s_hist[i] != 0u) atomicAdd(gh + i, s_hist[i]);
+}
+
+// ---------------------------------------------------------------------------
+// 2. collect the keys of the threshold bin
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a) {
+  __shared__ uint32_t s_hist[kSelBins];
+  __shared__ int s_wave[kSelWaves];
+  __shared__ int s_res[2];
+  __shared__ int s_base;
+  __shared__ float s_inv2h;
+  const HeadCtx h = head_ctx(a);
+  if (h.keep_all) return;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
+  const uint32_t* gh = a.hist + h.bg * kSelBins;
+  for (int i = tid; i < kSelBins; i += kSelThreads) s_hist[i] = gh[i];
+  __syncthreads();
+  find_digit(s_hist, kSelBins, a.top_k, s_wave, s_res);
+  const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+  const ScoreParams sp = score_params(a, h, s_inv2h);
+
+  // each thread handles a contiguous run of the chunk so that its keys in d1
+  // can be written without per-key atomics
+  constexpr int kRun = 8;
+  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  int gt = 0, eq = 0;
+  for (int t0 = i0; t0 < i1; t0 += kRun * kSelThreads) {
+    const int j0 = t0 + tid;
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) {
+      const int i = j0 + u * kSelThreads;
+      if (i < i1) {
+        const uint32_t dig = static_cast<uint32_t>(cand_key(sp, i) >> (64 - kSelDigitBits));
+        gt += dig > d1;
+        eq += dig == d1;
       }
-      __syncthreads();
-      list_n = min(s_list_n, kSelListCap);
-      in_lds = true;
     }
   }
-  const uint64_t kstar = prefix;
+  int gt_total, eq_total;
+  (void)block_excl_scan(gt, s_wave, &gt_total);
+  const int my = block_excl_scan(eq, s_wave, &eq_total);
+  if (tid == 0) {
+    a.chunk_above[h.bg * kSelMaxChunks + h.c] = gt_total;
+    s_base = eq_total > 0 ? atomicAdd(a.list_n + h.bg, eq_total) : 0;
+  }
+  __syncthreads();
+  if (eq == 0) return;
+  uint64_t* glist = a.list + h.bg * kSelListCap;
+  int slot = s_base + my;
+  for (int t0 = i0; t0 < i1; t0 += kRun * kSelThreads) {
+    const int j0 = t0 + tid;
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) {
+      const int i = j0 + u * kSelThreads;
+      if (i < i1) {
+        const uint64_t key = cand_key(sp, i);
+        if (static_cast<uint32_t>(key >> (64 - kSelDigitBits)) == d1) {
+          if (slot < kSelListCap) glist[slot] = key;
+          ++slot;
+        }
+      }
+    }
+  }
+}
 
-  // ordered emission: positions with key >= K*, ascending
-  int base = 0;
-  for (int t0 = 0; t0 < n; t0 += 4 * kSelectThreads) {
-    const int i0 = t0 + 4 * tid;
+// ---------------------------------------------------------------------------
+// 3. resolve K*, per-chunk output offsets; clear the head's bookkeeping
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void select_finish_kernel(SelectArgs a) {
+  __shared__ uint32_t s_hist[kSelBins];
+  __shared__ uint64_t s_list[kSelListCap];
+  __shared__ int s_cnt[kSelMaxChunks];
+  __shared__ int s_wave[kSelWaves];
+  __shared__ int s_res[2];
+  __shared__ float s_inv2h;
+  HeadCtx h;
+  {
+    const int e = blockIdx.x / a.n_kv_heads;
+    h.e = e;
+    h.g = blockIdx.x - e * a.n_kv_heads;
+    h.c = 0;
+    h.M = a.tab.nsplit[e];
+    h.b = a.tab.seq[e];
+    h.T = a.tab.ctx[e];
+    h.bg = static_cast<int64_t>(h.b) * a.n_kv_heads + h.g;
+    h.n = max(0, h.T - a.n_recent - a.n_sink);
+    h.keep_all = h.n <= a.top_k || a.top_k == 0;
+  }
+  if (h.keep_all) return;
+  const int tid = threadIdx.x;
+  const int K = a.top_k;
+  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
+  uint32_t* gh = a.hist + h.bg * kSelBins;
+  for (int i = tid; i < kSelBins; i += kSelThreads) s_hist[i] = gh[i];
+  __syncthreads();
+  find_digit(s_hist, kSelBins, K, s_wave, s_res);
+  const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+  const int above = s_res[1];
+  const int cnt_d1 = static_cast<int>(s_hist[d1]);
+  const int need = K - above;
+  const ScoreParams sp = score_params(a, h, s_inv2h);
+  const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
+  const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
+  for (int c = tid; c < kSelMaxChunks; c += kSelThreads) s_cnt[c] = 0;
+  uint64_t kstar;
+  if (cnt_d1 <= kSelListCap) {
+    const uint64_t* glist = a.list + h.bg * kSelListCap;
+    for (int i = tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
+    __syncthreads();
+    kstar = radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
+                          s_hist, s_wave, s_res);
+    for (int i = tid; i < cnt_d1; i += kSelThreads) {
+      const uint64_t key = s_list[i];
+      if (key >= kstar) atomicAdd(&s_cnt[(key_position(key) - a.n_sink) / a.chunk], 1);
+    }
+    __syncthreads();
+    for (int c = tid; c < h.M; c += kSelThreads) s_cnt[c] += a.chunk_above[h.bg * kSelMaxChunks + c];
+  } else {
+    // the threshold bin does not fit in LDS: radix passes over all candidates
+    kstar = radix_resolve([&](int i) { return cand_key(sp, i); }, h.n, pfx, pmask, 64 - kSelDigitBits, need,
+                          s_hist, s_wave, s_res);
+    for (int i = tid; i < h.n; i += kSelThreads)
+      if (cand_key(sp, i) >= kstar) atomicAdd(&s_cnt[i / a.chunk], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the per-chunk counts -> output offsets
+  {
+    constexpr int PER = kSelMaxChunks / kSelThreads;
+    int v[PER], loc = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid * PER + u;
+      v[u] = c < h.M ? s_cnt[c] : 0;
+      loc += v[u];
+    }
+    int tot;
+    int run = block_excl_scan(loc, s_wave, &tot);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid * PER + u;
+      if (c < h.M) a.chunk_off[h.bg * kSelMaxChunks + c] = run;
+      run += v[u];
+    }
+  }
+  if (tid == 0) {
+    a.kstar[h.bg] = kstar;
+    a.sel_cnt[h.bg] = K;
+    a.list_n[h.bg] = 0;
+  }
+  for (int i = tid; i < kSelBins; i += kSelThreads) gh[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// 4. ordered emission
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
+  __shared__ int s_wave[kSelWaves];
+  __shared__ float s_inv2h;
+  const HeadCtx h = head_ctx(a);
+  const int tid = threadIdx.x;
+  const int K = a.top_k;
+  int32_t* out = a.sel_idx + h.bg * K;
+  if (h.keep_all) {
+    const int i0 = h.c * a.chunk, i1 = min(K, i0 + a.chunk);
+    for (int i = i0 + tid; i < i1; i += kSelThreads) out[i] = i < h.n ? a.n_sink + i : -1;
+    if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = min(h.n, K);
+    return;
+  }
+  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
+  __syncthreads();
+  const ScoreParams sp = score_params(a, h, s_inv2h);
+  const uint64_t kstar = a.kstar[h.bg];
+  int base = a.chunk_off[h.bg * kSelMaxChunks + h.c];
+  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  for (int t0 = i0; t0 < i1; t0 += 4 * kSelThreads) {
+    const int j0 = t0 + 4 * tid;
     int flags = 0, c = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u;
-      if (i < n && cand_key(sp, i) >= kstar) {
+      const int i = j0 + u;
+      if (i < i1 && cand_key(sp, i) >= kstar) {
         flags |= 1 << u;
         ++c;
       }
@@ -213,14 +402,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     int pos = base + block_excl_scan(c, s_wave, &total);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if ((flags & (1 << u)) && pos < K) out[pos++] = lo + i0 + u;
+      if ((flags & (1 << u)) && pos < K) out[pos++] = a.n_sink + j0 + u;
     base += total;
   }
-  if (tid == 0) a.sel_cnt[bg] = K;
 }
 
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s) {
-  select_kernel<<<grid, kSelectThreads, 0, s>>>(a);
+  select_hist_kernel<<<grid, kSelThreads, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_gather_kernel<<<grid, kSelThreads, 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_finish_kernel<<<a.tab.n * a.n_kv_heads, kSelThreads, 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_emit_kernel<<<grid, kSelThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

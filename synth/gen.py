@@ -90,7 +90,6 @@ def build_cache(w: Workload, device, layer=0, n_spans=None, ctx_lens=None):
     B, Hkv, D = w.batch, w.n_kv_heads, w.head_dim
     cap = w.kv_capacity
     ctx = ctx_lens if ctx_lens is not None else context_lengths(w)
-    Kf = torch.empty(B, Hkv, cap, D, dtype=torch.float32, device=device)
     K = torch.empty(B, Hkv, cap, D, dtype=_DT[w.dtype], device=device)
     V = torch.empty_like(K)
     gk = generator(device, w.seed, layer, S_K)
@@ -133,7 +132,6 @@ def build_cache(w: Workload, device, layer=0, n_spans=None, ctx_lens=None):
                 kf[T:] = 0.0
                 V[b, g, T:] = 0
             K[b, g].copy_(kf)
-    del Kf
     return {"K": K, "V": V, **info}
 
 

@@ -68,7 +68,7 @@ def _select_gpu(kv, sp, ids, mass):
     dev = kv.k.device
     sel = torch.full((kv.batch, kv.n_kv_heads, sp.top_k), -7, dtype=torch.int32, device=dev)
     cnt = torch.full((kv.batch, kv.n_kv_heads), -7, dtype=torch.int32, device=dev)
-    S.sfi_select(kv, sp, ids, mass, sel, cnt)
+    S.sfi_select(kv, sp, ids, mass, sel, cnt, S.alloc_workspace(kv, sp))
     torch.cuda.synchronize()
     return sel.cpu().numpy(), cnt.cpu().numpy()
 
@@ -241,3 +241,72 @@ def test_invalid_arguments_raise_before_launch():
     kv.ctx[0] = 101
     with pytest.raises(S.SFIError):
         S.sfi_slow_step(kv, [0], q, out, None, S.alloc_workspace(kv))    # ctx beyond capacity
+
+
+# ------------------------------------------------------------------ packed support
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_packed_fast_equals_gather_and_oracle(dtype, D, G):
+    """Packing the selected rows and streaming them gives the gather kernel's
+    result bit for bit (same support order and chunking), and the oracle's
+    within tolerance; short contexts exercise the sink/window clipping."""
+    Hkv, ns, W, k = 2, 4, 64, 200
+    ctx = [3000, 700, 50, 3]
+    B = len(ctx)
+    kv, q = random_cache(B, G * Hkv, Hkv, 3000, D, DT[dtype], ctx, seed=3 * G + D, q_scale=2.0)
+    dev = kv.k.device
+    sp = S.support_params(ns, W, k, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    ids = list(range(B))
+    _, mass = run_slow(kv, q, ids, ws=ws)
+    sel = torch.full((B, Hkv, k), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(B, Hkv, dtype=torch.int32, device=dev)
+    S.sfi_select(kv, sp, ids, mass, sel, cnt, ws)
+    pk = torch.zeros(B, Hkv, k, D, dtype=DT[dtype], device=dev)
+    pv = torch.zeros_like(pk)
+    S.sfi_pack_support(kv, sp, ids, sel, cnt, pk, pv)
+    out_g = torch.full((B, G * Hkv, D), float("nan"), device=dev)
+    out_p = torch.full_like(out_g, float("nan"))
+    S.sfi_fast_step(kv, sp, ids, q, sel, cnt, out_g, ws)
+    S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out_p, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_g, out_p)
+    for b in range(B):
+        T = ctx[b]
+        c = cnt[b].cpu().numpy()
+        sels = [sel[b, g, :c[g]].cpu().numpy().astype(np.int64) for g in range(Hkv)]
+        for g in range(Hkv):
+            rows = torch.from_numpy(sels[g]).to(dev)
+            assert torch.equal(pk[b, g, :c[g]], kv.k[b, g].index_select(0, rows))
+            assert torch.equal(pv[b, g, :c[g]], kv.v[b, g].index_select(0, rows))
+        ref = O.fast_step(np64(q[b]), np64(kv.k[b, :, :T]), np64(kv.v[b, :, :T]), T, ns, W, sels)
+        assert np.max(np.abs(np64(out_p[b]) - ref)) < OUT_TOL
+
+
+def test_packed_with_growing_context():
+    """The window slides as tokens are appended after the pack; the packed
+    selected rows stay valid and the result matches the oracle."""
+    kv, q = random_cache(1, 32, 8, 5000, 128, torch.bfloat16, [4000], seed=21, q_scale=2.0)
+    dev = kv.k.device
+    sp = S.support_params(16, 256, 512, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    _, mass = run_slow(kv, q, [0], ws=ws)
+    sel = torch.empty(1, 8, 512, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, 8, dtype=torch.int32, device=dev)
+    S.sfi_select(kv, sp, [0], mass, sel, cnt, ws)
+    pk = torch.empty(1, 8, 512, 128, dtype=torch.bfloat16, device=dev)
+    pv = torch.empty_like(pk)
+    S.sfi_pack_support(kv, sp, [0], sel, cnt, pk, pv)
+    for _ in range(5):
+        kn = torch.randn(1, 8, 128, device=dev).to(torch.bfloat16)
+        S.sfi_kv_append(kv, [0], kn, kn)
+        kv.ctx += 1
+    out = torch.empty(1, 32, 128, device=dev)
+    S.sfi_fast_step_packed(kv, sp, [0], q, pk, pv, cnt, out, ws)
+    torch.cuda.synchronize()
+    T = int(kv.ctx[0])
+    c = cnt[0].cpu().numpy()
+    sels = [sel[0, g, :c[g]].cpu().numpy().astype(np.int64) for g in range(8)]
+    ref = O.fast_step(np64(q[0]), np64(kv.k[0, :, :T]), np64(kv.v[0, :, :T]), T, 16, 256, sels)
+    assert np.max(np.abs(np64(out[0]) - ref)) < OUT_TOL

@@ -46,8 +46,12 @@ def parse():
     p.add_argument("--dense-steps", type=int, default=64)
     p.add_argument("--eager-steps", type=int, default=128)
     p.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    p.add_argument("--fast", choices=["packed", "gather"], default="packed",
+                   help="fast step over the packed support (default) or gathering rows by index")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="end with one device copy of MIB MiB (calibrates memory-traffic counters)")
     return p.parse_args()
 
 
@@ -105,15 +109,24 @@ def main():
     mass = torch.empty(1, w.n_kv_heads, kvs[0].capacity, dtype=torch.float32, device=dev)
     sel = torch.empty(L, 1, w.n_kv_heads, w.top_k, dtype=torch.int32, device=dev)
     cnt = torch.empty(L, 1, w.n_kv_heads, dtype=torch.int32, device=dev)
+    packed = args.fast == "packed"
+    if packed:
+        pk = torch.empty(L, 1, w.n_kv_heads, w.top_k, w.head_dim, dtype=q_steps.dtype, device=dev)
+        pv = torch.empty_like(pk)
 
     def slow_layers():
         for l in range(L):
             S.sfi_slow_step(kvs[l], [0], q_buf[l], out_buf[l], mass, ws)
             S.sfi_select(kvs[l], sp, [0], mass, sel[l], cnt[l], ws)
+            if packed:
+                S.sfi_pack_support(kvs[l], sp, [0], sel[l], cnt[l], pk[l], pv[l])
 
     def fast_layers():
         for l in range(L):
-            S.sfi_fast_step(kvs[l], sp, [0], q_buf[l], sel[l], cnt[l], out_buf[l], ws)
+            if packed:
+                S.sfi_fast_step_packed(kvs[l], sp, [0], q_buf[l], pk[l], pv[l], cnt[l], out_buf[l], ws)
+            else:
+                S.sfi_fast_step(kvs[l], sp, [0], q_buf[l], sel[l], cnt[l], out_buf[l], ws)
 
     def dense_layers():
         for l in range(L):
@@ -161,7 +174,9 @@ def main():
     torch.cuda.synchronize()
     t_dense = time.perf_counter() - t_start
 
-    # per-kernel durations: library HIP events around each launch, eager
+    # Per-kernel durations: with timing on, the library launches each kernel
+    # with a HIP event pair stamped by the kernel's own dispatch packet (on the
+    # launch stream), over the same schedule steps, eager.
     S.sfi_profile_reset()
     S.sfi_profile_enable(True)
     ke = min(args.eager_steps, n_steps)
@@ -176,31 +191,40 @@ def main():
         if n:
             kern[name] = {"launches": n, "avg_us": 1e3 * ms / n}
     T = w.ctx
-    kv_bytes_slow = 2 * w.n_kv_heads * T * w.head_dim * 2 if w.dtype == "bf16" else 2 * w.n_kv_heads * T * w.head_dim * 4
     esz = 2 if w.dtype == "bf16" else 4
-    supp = w.n_sink + w.n_recent + min(w.top_k, T - w.n_sink - w.n_recent)
+    n_cand = T - w.n_sink - w.n_recent
+    kk = min(w.top_k, n_cand)
+    supp = min(w.n_sink, T) + min(w.n_recent, T) + kk
+    kv_row = w.head_dim * esz
+    q_bytes = w.n_q_heads * w.head_dim * esz
+    # algorithmic bytes per launch (what the method has to move)
     alg = {
-        "slow_partial": kv_bytes_slow + w.n_q_heads * w.head_dim * esz,
+        "slow_partial": 2 * w.n_kv_heads * T * kv_row + q_bytes,
         "slow_combine": 4 * w.n_kv_heads * T + 4 * w.n_q_heads * w.head_dim,
-        "select": 4 * w.n_kv_heads * (T - w.n_sink - w.n_recent) + 4 * w.n_kv_heads * w.top_k,
-        "fast": 2 * w.n_kv_heads * supp * w.head_dim * esz + 4 * w.n_kv_heads * w.top_k
-                + w.n_q_heads * w.head_dim * esz,
+        "select": 4 * w.n_kv_heads * n_cand + 4 * w.n_kv_heads * w.top_k,
+        "pack": 2 * 2 * w.n_kv_heads * kk * kv_row + 4 * w.n_kv_heads * w.top_k,
+        "fast_partial": 2 * w.n_kv_heads * supp * kv_row + q_bytes + (0 if packed else 4 * w.n_kv_heads * w.top_k),
+        "fast_merge": 4 * w.n_q_heads * w.head_dim,
     }
     for name, k in kern.items():
         if name in alg:
             k["alg_bytes"] = alg[name]
             k["GBps"] = alg[name] / (k["avg_us"] * 1e-6) / 1e9
             k["frac"] = k["GBps"] / HBM_PEAK_GBS
-    total_time = {n: k["avg_us"] * k["launches"] for n, k in kern.items()}
+    # GPU time of each kernel over the timed steps = launches there x average
+    n_fast_timed = K - n_slow_timed
+    per_step = {"slow_partial": n_slow_timed, "slow_combine": n_slow_timed, "select": n_slow_timed,
+                "pack": n_slow_timed if packed else 0, "fast_partial": n_fast_timed, "fast_merge": n_fast_timed}
+    total_time = {n: kern[n]["avg_us"] * per_step[n] * L for n in kern if n in per_step}
     dominant = max(total_time, key=total_time.get)
 
     def us(name):
         return kern.get(name, {}).get("avg_us", 0.0)
 
-    slow_us = us("slow_partial") + us("slow_combine") + us("select")
-    fast_us = us("fast")
+    slow_us = us("slow_partial") + us("slow_combine") + us("select") + us("pack")
+    fast_us = us("fast_partial") + us("fast_merge")
     value = K * L / t_blend
-    dense_rate = kd * L / t_dense
+    dense_rate = kd * L / t_dense if kd else None
     d = kern[dominant]
     result = {
         "metric": METRIC,
@@ -219,20 +243,31 @@ def main():
                                f"ctx {w.ctx}, {w.dtype} KV, sinks {w.n_sink}, recent {w.n_recent}, "
                                f"top-k {w.top_k}, lambda {w.lam}, geometric spans mean {w.span_param}; "
                                f"{L} independent layer caches per decode step",
-                   "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode,
+                   "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode, "fast_path": args.fast,
                    "slow_steps_timed": n_slow_timed},
         "slow_steps_per_s_layer": 1e6 / slow_us if slow_us else None,
         "fast_steps_per_s_layer": 1e6 / fast_us if fast_us else None,
         "blended_steps_per_s_layer": value,
         "dense_steps_per_s_layer": dense_rate,
-        "speedup_vs_dense": value / dense_rate,
+        "speedup_vs_dense": value / dense_rate if dense_rate else None,
         "kernels": kern,
+        "kernel_time_share": {n: t / sum(total_time.values()) for n, t in total_time.items()},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d.get("frac"), "traffic": None,
                      "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},
+        "roofline_slow_partial": {"bound": "hbm", "achieved": kern["slow_partial"]["GBps"], "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": kern["slow_partial"]["frac"],
+                                  "avg_launch_us": kern["slow_partial"]["avg_us"]},
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, sp, args.cpu_budget)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(result))
 
 

@@ -217,10 +217,11 @@ typedef enum {
   SFI_K_SLOW_PARTIAL = 0, /* split-K dense partials (+ logit scratch) */
   SFI_K_SLOW_COMBINE = 1, /* split merge + per-position mass */
   SFI_K_SELECT = 2,       /* Selector (its four kernels together) */
-  SFI_K_FAST = 3,         /* sparse gather attention + chunk merge */
+  SFI_K_FAST = 3,         /* sparse attention over support chunks (gather or packed) */
   SFI_K_APPEND = 4,
   SFI_K_PACK = 5,         /* packing of the selected rows */
-  SFI_K_COUNT = 6
+  SFI_K_FAST_MERGE = 6,   /* merge of the fast step's chunk partials */
+  SFI_K_COUNT = 7
 } sfi_kernel_id;
 int32_t sfi_profile_enable(int32_t on);
 int32_t sfi_profile_reset(void);

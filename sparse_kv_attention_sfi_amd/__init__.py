@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     sfi_profile_reset, sfi_select, sfi_slow_step, sfi_status_str, sfi_version,
     sfi_workspace_bytes, sfi_workspace_init,
     SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE,
-    SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK, KERNEL_NAMES,
+    SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK, SFI_K_FAST_MERGE, KERNEL_NAMES,
 )

@@ -20,9 +20,10 @@ SFI_OK, SFI_ERR_INVALID_ARG, SFI_ERR_UNSUPPORTED, SFI_ERR_WORKSPACE, SFI_ERR_HIP
 SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST = 0, 1, 2
 SFI_SPAN_FIXED, SFI_SPAN_GEOMETRIC = 0, 1
-SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK = 0, 1, 2, 3, 4, 5
+SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK, SFI_K_FAST_MERGE = range(7)
 KERNEL_NAMES = {SFI_K_SLOW_PARTIAL: "slow_partial", SFI_K_SLOW_COMBINE: "slow_combine",
-                SFI_K_SELECT: "select", SFI_K_FAST: "fast", SFI_K_APPEND: "append", SFI_K_PACK: "pack"}
+                SFI_K_SELECT: "select", SFI_K_FAST: "fast_partial", SFI_K_APPEND: "append",
+                SFI_K_PACK: "pack", SFI_K_FAST_MERGE: "fast_merge"}
 
 
 class SFIError(RuntimeError):

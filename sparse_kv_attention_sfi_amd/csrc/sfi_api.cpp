@@ -223,9 +223,13 @@ hipEvent_t take_event(Prof& p) {
   return e;
 }
 
-// Runs `launch` (returning hipError_t) between two recorded events when timing is on.
+thread_local LaunchTiming* g_timing = nullptr;
+
+// Runs `launch` (returning hipError_t); when timing is on, its kernels stamp a
+// fresh event pair from their own dispatch packets.
 template <typename F>
 hipError_t timed(int kid, hipStream_t s, F&& launch) {
+  (void)s;
   Prof& p = prof();
   bool on;
   {
@@ -233,18 +237,17 @@ hipError_t timed(int kid, hipStream_t s, F&& launch) {
     on = p.on;
   }
   if (!on) return launch();
-  hipEvent_t a, b;
+  LaunchTiming t;
   {
     std::lock_guard<std::mutex> lk(p.mu);
-    a = take_event(p);
-    b = take_event(p);
+    t.start = take_event(p);
+    t.stop = take_event(p);
   }
-  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, s);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, s);
+  if (t.start == nullptr || t.stop == nullptr) return hipErrorOutOfMemory;
+  const hipEvent_t a = t.start, b = t.stop;
+  g_timing = &t;
+  const hipError_t e = launch();
+  g_timing = nullptr;
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lk(p.mu);
   p.pending[kid].emplace_back(a, b);
@@ -264,6 +267,9 @@ int32_t for_each_group(const int32_t* ids, int32_t n, F&& f) {
 }
 
 }  // namespace
+
+LaunchTiming* launch_timing() { return g_timing; }
+
 }  // namespace sfi
 
 using namespace sfi;
@@ -501,9 +507,11 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
       a.tab.nsplit[i] = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(smax, crow)));
       a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
     }
-    const hipError_t e = timed(SFI_K_FAST, s, [&] {
-      return launch_fast(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
+    hipError_t e = timed(SFI_K_FAST, s, [&] {
+      return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
     });
+    if (e == hipSuccess)
+      e = timed(SFI_K_FAST_MERGE, s, [&] { return launch_fast_merge(a, desc->head_dim, G, s); });
     return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
   });
 }

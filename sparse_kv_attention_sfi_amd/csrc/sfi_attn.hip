@@ -230,6 +230,37 @@ struct Attn {
         for (int d = 0; d < kEpp; ++d) so[(w * G + h) * D + lane * kEpp + d] = acc[h][d];
     }
   }
+
+  // Row groups: lanes that own the same 16-byte piece of different rows.
+  static constexpr int kRowGroups = 64 / kPPR;
+
+  // Like finish_wave, but without the cross-lane reduction of the output:
+  // every lane stores its piece to so[((w * kRowGroups + rg) * G + h) * D + col]
+  // and the workgroup merge sums the row groups (for short per-wave work the
+  // shuffles would dominate).
+  __device__ __forceinline__ void finish_wave_lds(float* sm, float* sl, float* so, int w, int lane) {
+    float lt[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = row16_sum(l_lane[h & 3]);
+      lt[h] = lane_bcast(v, 16 * (h >> 2));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm[w * G + h] = m_run[h];
+        sl[w * G + h] = lt[h];
+      }
+    }
+    const int rg = lane / kPPR, pc = lane % kPPR;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = so + ((w * kRowGroups + rg) * G + h) * D + pc * kEpp;
+#pragma unroll
+      for (int d = 0; d < kEpp; d += 4)
+        *reinterpret_cast<float4*>(dst + d) = make_float4(acc[h][d], acc[h][d + 1], acc[h][d + 2], acc[h][d + 3]);
+    }
+  }
 };
 
 // Merge NW wave states from LDS into one (max, sum, output) per head and store
@@ -262,6 +293,39 @@ __device__ __forceinline__ void merge_waves_to_global(const float* sm, const flo
           if (mw != -INFINITY) L += sl[w * G + h] * fast_exp2(mw - M);
         }
       }
+      ml[h * ml_stride] = M;
+      ml[h * ml_stride + 1] = L;
+    }
+  }
+}
+
+// merge_waves_to_global for states stored by finish_wave_lds (RG row groups
+// per wave).
+template <int D, int G, int NW, int RG>
+__device__ __forceinline__ void merge_wave_groups_to_global(const float* sm, const float* sl, const float* so,
+                                                            float* ml, int64_t ml_stride, float* o,
+                                                            int64_t o_stride, int tid, int nthreads) {
+  for (int idx = tid; idx < G * D; idx += nthreads) {
+    const int h = idx / D, d = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * G + h]);
+    float acc = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm[w * G + h];
+        if (mw == -INFINITY) continue;
+        const float sc = fast_exp2(mw - M);
+        float part = 0.f;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) part += so[((w * RG + rg) * G + h) * D + d];
+        acc += part * sc;
+        L += sl[w * G + h] * sc;
+      }
+    }
+    o[h * o_stride + d] = acc;
+    if (d == 0) {
       ml[h * ml_stride] = M;
       ml[h * ml_stride + 1] = L;
     }
@@ -623,7 +687,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
   constexpr int NV = ROWS / A::kRPL;
 
   __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
-  __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
+  __shared__ __attribute__((aligned(16))) float s_o[NW * A::kRowGroups * G * D];
   __shared__ float s_m[NW * G], s_l[NW * G];
   __shared__ int s_pos[CH];
 
@@ -681,10 +745,10 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
                                  0, lane);
     }
   }
-  st.finish_wave(s_m, s_l, s_o, wave, lane);
+  st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
   __syncthreads();
   const int64_t slot = qh0 * a.part_stride + chunk;
-  merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
+  merge_wave_groups_to_global<D, G, NW, A::kRowGroups>(s_m, s_l, s_o, a.part_ml + slot * 2,
                                   static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
                                   static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
 }
@@ -705,7 +769,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   constexpr int NV = ROWS / A::kRPL;
 
   __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
-  __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
+  __shared__ __attribute__((aligned(16))) float s_o[NW * A::kRowGroups * G * D];
   __shared__ float s_m[NW * G], s_l[NW * G];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -772,10 +836,10 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   if (w0 < size) {
     st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, lane);
   }
-  st.finish_wave(s_m, s_l, s_o, wave, lane);
+  st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
   __syncthreads();
   const int64_t slot = qh0 * a.part_stride + chunk;
-  merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
+  merge_wave_groups_to_global<D, G, NW, A::kRowGroups>(s_m, s_l, s_o, a.part_ml + slot * 2,
                                   static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
                                   static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
 }
@@ -897,10 +961,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t word
 template <typename E, int D>
 static hipError_t slow_partial_g(const SlowArgs& a, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: slow_partial_kernel<E, D, 1><<<grid, kSlowThreads, 0, s>>>(a); break;
-    case 2: slow_partial_kernel<E, D, 2><<<grid, kSlowThreads, 0, s>>>(a); break;
-    case 4: slow_partial_kernel<E, D, 4><<<grid, kSlowThreads, 0, s>>>(a); break;
-    case 8: slow_partial_kernel<E, D, 8><<<grid, kSlowThreads, 0, s>>>(a); break;
+    case 1: launch(slow_partial_kernel<E, D, 1>, grid, kSlowThreads, s, a); break;
+    case 2: launch(slow_partial_kernel<E, D, 2>, grid, kSlowThreads, s, a); break;
+    case 4: launch(slow_partial_kernel<E, D, 4>, grid, kSlowThreads, s, a); break;
+    case 8: launch(slow_partial_kernel<E, D, 8>, grid, kSlowThreads, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -919,10 +983,10 @@ hipError_t launch_slow_partial(const SlowArgs& a, int dtype, int head_dim, int g
 template <int D>
 static hipError_t slow_combine_g(const CombineArgs& a, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: slow_combine_kernel<D, 1><<<grid, kCombineThreads, 0, s>>>(a); break;
-    case 2: slow_combine_kernel<D, 2><<<grid, kCombineThreads, 0, s>>>(a); break;
-    case 4: slow_combine_kernel<D, 4><<<grid, kCombineThreads, 0, s>>>(a); break;
-    case 8: slow_combine_kernel<D, 8><<<grid, kCombineThreads, 0, s>>>(a); break;
+    case 1: launch(slow_combine_kernel<D, 1>, grid, kCombineThreads, s, a); break;
+    case 2: launch(slow_combine_kernel<D, 2>, grid, kCombineThreads, s, a); break;
+    case 4: launch(slow_combine_kernel<D, 4>, grid, kCombineThreads, s, a); break;
+    case 8: launch(slow_combine_kernel<D, 8>, grid, kCombineThreads, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -936,12 +1000,13 @@ hipError_t launch_slow_combine(const CombineArgs& a, int head_dim, int group, in
 
 // Fast-step rows per wave (16 per tile).  Small chunks keep many workgroups
 // in flight, which a latency-bound gather of ~10 MB needs; the count is a
-// launch parameter (1, 2 or 4 tiles per wave).
+// launch parameter (1, 2 or 4 tiles per wave; 2 measured fastest on the 128K
+// layer).
 int fast_tiles() {
   static const int t = [] {
     const char* s = std::getenv("SFI_FAST_TILES");
-    const int v = s ? std::atoi(s) : 1;
-    return (v == 2 || v == 4) ? v : 1;
+    const int v = s ? std::atoi(s) : 2;
+    return (v == 1 || v == 4) ? v : 2;
   }();
   return t;
 }
@@ -951,56 +1016,71 @@ int fast_chunk_rows() { return (kFastThreads / 64) * fast_tiles() * 16; }
 template <typename E, int D, int G, int TILES>
 static void fast_partial_launch(const FastArgs& a, int grid, hipStream_t s) {
   if (a.packed_k != nullptr) {
-    fast_packed_kernel<E, D, G, TILES><<<grid, kFastThreads, 0, s>>>(a);
+    launch(fast_packed_kernel<E, D, G, TILES>, grid, kFastThreads, s, a);
   } else {
-    fast_partial_kernel<E, D, G, TILES><<<grid, kFastThreads, 0, s>>>(a);
+    launch(fast_partial_kernel<E, D, G, TILES>, grid, kFastThreads, s, a);
   }
-}
-
-template <typename E, int D, int G>
-static hipError_t fast_pair(const FastArgs& a, int grid, hipStream_t s) {
-  switch (a.chunk_rows / ((kFastThreads / 64) * 16)) {
-    case 4: fast_partial_launch<E, D, G, 4>(a, grid, s); break;
-    case 2: fast_partial_launch<E, D, G, 2>(a, grid, s); break;
-    default: fast_partial_launch<E, D, G, 1>(a, grid, s); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  fast_merge_kernel<D, G><<<a.tab.n * a.n_kv_heads, kMergeThreads, 0, s>>>(a);
-  return hipGetLastError();
 }
 
 template <typename E, int D>
-static hipError_t fast_g(const FastArgs& a, int group, int grid, hipStream_t s) {
-  switch (group) {
-    case 1: return fast_pair<E, D, 1>(a, grid, s);
-    case 2: return fast_pair<E, D, 2>(a, grid, s);
-    case 4: return fast_pair<E, D, 4>(a, grid, s);
-    case 8: return fast_pair<E, D, 8>(a, grid, s);
+static hipError_t fast_partial_g(const FastArgs& a, int group, int grid, hipStream_t s) {
+  const int tiles = a.chunk_rows / ((kFastThreads / 64) * 16);
+  switch (group * 8 + tiles) {
+    case 1 * 8 + 1: fast_partial_launch<E, D, 1, 1>(a, grid, s); break;
+    case 1 * 8 + 2: fast_partial_launch<E, D, 1, 2>(a, grid, s); break;
+    case 1 * 8 + 4: fast_partial_launch<E, D, 1, 4>(a, grid, s); break;
+    case 2 * 8 + 1: fast_partial_launch<E, D, 2, 1>(a, grid, s); break;
+    case 2 * 8 + 2: fast_partial_launch<E, D, 2, 2>(a, grid, s); break;
+    case 2 * 8 + 4: fast_partial_launch<E, D, 2, 4>(a, grid, s); break;
+    case 4 * 8 + 1: fast_partial_launch<E, D, 4, 1>(a, grid, s); break;
+    case 4 * 8 + 2: fast_partial_launch<E, D, 4, 2>(a, grid, s); break;
+    case 4 * 8 + 4: fast_partial_launch<E, D, 4, 4>(a, grid, s); break;
+    case 8 * 8 + 1: fast_partial_launch<E, D, 8, 1>(a, grid, s); break;
+    case 8 * 8 + 2: fast_partial_launch<E, D, 8, 2>(a, grid, s); break;
+    case 8 * 8 + 4: fast_partial_launch<E, D, 8, 4>(a, grid, s); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
-hipError_t launch_fast(const FastArgs& a, int dtype, int head_dim, int group, int grid,
-                       hipStream_t s) {
+hipError_t launch_fast_partial(const FastArgs& a, int dtype, int head_dim, int group, int grid,
+                               hipStream_t s) {
   if (dtype == SFI_BF16) {
-    return head_dim == 128 ? fast_g<BF16, 128>(a, group, grid, s) : fast_g<BF16, 64>(a, group, grid, s);
+    return head_dim == 128 ? fast_partial_g<BF16, 128>(a, group, grid, s)
+                           : fast_partial_g<BF16, 64>(a, group, grid, s);
   }
-  return head_dim == 128 ? fast_g<F32, 128>(a, group, grid, s) : fast_g<F32, 64>(a, group, grid, s);
+  return head_dim == 128 ? fast_partial_g<F32, 128>(a, group, grid, s)
+                         : fast_partial_g<F32, 64>(a, group, grid, s);
 }
 
+template <int D>
+static hipError_t fast_merge_g(const FastArgs& a, int group, hipStream_t s) {
+  const int grid = a.tab.n * a.n_kv_heads;
+  switch (group) {
+    case 1: launch(fast_merge_kernel<D, 1>, grid, kMergeThreads, s, a); break;
+    case 2: launch(fast_merge_kernel<D, 2>, grid, kMergeThreads, s, a); break;
+    case 4: launch(fast_merge_kernel<D, 4>, grid, kMergeThreads, s, a); break;
+    case 8: launch(fast_merge_kernel<D, 8>, grid, kMergeThreads, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_merge(const FastArgs& a, int head_dim, int group, hipStream_t s) {
+  return head_dim == 128 ? fast_merge_g<128>(a, group, s) : fast_merge_g<64>(a, group, s);
+}
 
 hipError_t launch_support(const SupportArgs& a, int grid, hipStream_t s) {
-  support_kernel<<<grid, 256, 0, s>>>(a);
+  launch(support_kernel, grid, 256, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pack(const PackArgs& a, int dtype, int head_dim, int grid, hipStream_t s) {
   const int rb = head_dim * (dtype == SFI_BF16 ? 2 : 4);
   switch (rb) {
-    case 128: pack_kernel<128><<<grid, 256, 0, s>>>(a); break;
-    case 256: pack_kernel<256><<<grid, 256, 0, s>>>(a); break;
-    case 512: pack_kernel<512><<<grid, 256, 0, s>>>(a); break;
+    case 128: launch(pack_kernel<128>, grid, 256, s, a); break;
+    case 256: launch(pack_kernel<256>, grid, 256, s, a); break;
+    case 512: launch(pack_kernel<512>, grid, 256, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1009,9 +1089,9 @@ hipError_t launch_pack(const PackArgs& a, int dtype, int head_dim, int grid, hip
 hipError_t launch_append(const AppendArgs& a, int dtype, int head_dim, int grid, hipStream_t s) {
   const int rb = head_dim * (dtype == SFI_BF16 ? 2 : 4);
   switch (rb) {
-    case 128: append_kernel<128><<<grid, 64, 0, s>>>(a); break;
-    case 256: append_kernel<256><<<grid, 64, 0, s>>>(a); break;
-    case 512: append_kernel<512><<<grid, 64, 0, s>>>(a); break;
+    case 128: launch(append_kernel<128>, grid, 64, s, a); break;
+    case 256: launch(append_kernel<256>, grid, 64, s, a); break;
+    case 512: launch(append_kernel<512>, grid, 64, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1021,7 +1101,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   const size_t words = bytes / 4;
   if (words == 0) return hipSuccess;
   const int grid = static_cast<int>(std::min<size_t>((words + 255) / 256, 1024));
-  fill_zero_kernel<<<grid, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+  launch(fill_zero_kernel, grid, 256, s, static_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }
 

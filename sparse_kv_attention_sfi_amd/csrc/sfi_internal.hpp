@@ -2,6 +2,7 @@
 // of the SFI decode-attention library (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -161,8 +162,9 @@ hipError_t launch_slow_partial(const SlowArgs& a, int dtype, int head_dim, int g
 hipError_t launch_slow_combine(const CombineArgs& a, int head_dim, int group, int grid,
                                hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s);
-hipError_t launch_fast(const FastArgs& a, int dtype, int head_dim, int group, int grid,
-                       hipStream_t s);
+hipError_t launch_fast_partial(const FastArgs& a, int dtype, int head_dim, int group, int grid,
+                               hipStream_t s);
+hipError_t launch_fast_merge(const FastArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_support(const SupportArgs& a, int grid, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int dtype, int head_dim, int grid, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int head_dim, int grid,
@@ -173,6 +175,26 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // pack workgroup.
 int fast_chunk_rows();
 constexpr int kPackRows = 64;
+
+// Kernel timing: while the host runtime times a launch group, launches stamp
+// HIP events from their own dispatch packets (the start event on the group's
+// first kernel, the stop event on every kernel, so the last one wins).
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchTiming* launch_timing();  // the calling thread's context, or nullptr
+
+template <typename Kern, typename... Args>
+inline void launch(Kern kern, int grid, int block, hipStream_t s, Args... args) {
+  LaunchTiming* t = launch_timing();
+  if (t == nullptr) {
+    kern<<<grid, block, 0, s>>>(args...);
+    return;
+  }
+  hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, s, t->start, t->stop, 0, args...);
+  t->start = nullptr;
+}
 
 // Rows handled per wave per pipeline block: 16 KiB of K (and of V) per block.
 __host__ __device__ constexpr int block_rows(int row_bytes) { return 16384 / row_bytes; }

@@ -19,7 +19,8 @@
 //                     keys above d1 and appends its keys in d1 to a per-head
 //                     list (one atomic per workgroup reserves its range).
 //   3. select_finish: one workgroup per head resolves K* inside the list in
-//                     LDS (12 bits per level), derives how many keys each
+//                     LDS (by direct ranking when the list is short, else 12
+//                     bits per level), derives how many keys each
 //                     chunk keeps, turns that into output offsets, and clears
 //                     the head's histogram and list counter.  If d1 holds more
 //                     keys than fit in LDS, it resolves K* by radix passes
@@ -282,6 +283,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
 // 3. resolve K*, per-chunk output offsets; clear the head's bookkeeping
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_finish_kernel(SelectArgs a) {
+  __shared__ uint64_t s_kstar;
   __shared__ uint32_t s_hist[kSelBins];
   __shared__ uint64_t s_list[kSelListCap];
   __shared__ int s_cnt[kSelMaxChunks];
@@ -322,8 +324,20 @@ __global__ __launch_bounds__(kSelThreads) void select_finish_kernel(SelectArgs a
     const uint64_t* glist = a.list + h.bg * kSelListCap;
     for (int i = tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
     __syncthreads();
-    kstar = radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
-                          s_hist, s_wave, s_res);
+    if (cnt_d1 <= kSelThreads) {
+      // few keys: K* is the key with exactly need - 1 larger keys (all distinct)
+      if (tid < cnt_d1) {
+        const uint64_t mine = s_list[tid];
+        int rank = 0;
+        for (int j = 0; j < cnt_d1; ++j) rank += s_list[j] > mine;
+        if (rank == need - 1) s_kstar = mine;
+      }
+      __syncthreads();
+      kstar = s_kstar;
+    } else {
+      kstar = radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
+                            s_hist, s_wave, s_res);
+    }
     for (int i = tid; i < cnt_d1; i += kSelThreads) {
       const uint64_t key = s_list[i];
       if (key >= kstar) atomicAdd(&s_cnt[(key_position(key) - a.n_sink) / a.chunk], 1);
@@ -408,16 +422,16 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
 }
 
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s) {
-  select_hist_kernel<<<grid, kSelThreads, 0, s>>>(a);
+  launch(select_hist_kernel, grid, kSelThreads, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_gather_kernel<<<grid, kSelThreads, 0, s>>>(a);
+  launch(select_gather_kernel, grid, kSelThreads, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_finish_kernel<<<a.tab.n * a.n_kv_heads, kSelThreads, 0, s>>>(a);
+  launch(select_finish_kernel, a.tab.n * a.n_kv_heads, kSelThreads, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_emit_kernel<<<grid, kSelThreads, 0, s>>>(a);
+  launch(select_emit_kernel, grid, kSelThreads, s, a);
   return hipGetLastError();
 }
 

@@ -310,3 +310,31 @@ def test_packed_with_growing_context():
     sels = [sel[0, g, :c[g]].cpu().numpy().astype(np.int64) for g in range(8)]
     ref = O.fast_step(np64(q[0]), np64(kv.k[0, :, :T]), np64(kv.v[0, :, :T]), T, 16, 256, sels)
     assert np.max(np.abs(np64(out[0]) - ref)) < OUT_TOL
+
+
+def test_kernel_timing_events():
+    """With timing on, every launch group records one event pair; the summed
+    durations are positive and the counts match the calls."""
+    kv, q = random_cache(1, 32, 8, 20000, 128, torch.bfloat16, [20000], seed=2)
+    dev = kv.k.device
+    sp = S.support_params(16, 256, 1024, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    out = torch.empty(1, 32, 128, device=dev)
+    mass = torch.empty(1, 8, 20000, device=dev)
+    sel = torch.empty(1, 8, 1024, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, 8, dtype=torch.int32, device=dev)
+    S.sfi_profile_reset()
+    S.sfi_profile_enable(True)
+    try:
+        for _ in range(3):
+            S.sfi_slow_step(kv, [0], q, out, mass, ws)
+            S.sfi_select(kv, sp, [0], mass, sel, cnt, ws)
+            S.sfi_fast_step(kv, sp, [0], q, sel, cnt, out, ws)
+    finally:
+        S.sfi_profile_enable(False)
+    torch.cuda.synchronize()
+    for kid in (S.SFI_K_SLOW_PARTIAL, S.SFI_K_SLOW_COMBINE, S.SFI_K_SELECT, S.SFI_K_FAST, S.SFI_K_FAST_MERGE):
+        ms, n = S.sfi_profile_read(kid)
+        assert n == 3 and ms > 0, (kid, ms, n)
+    S.sfi_profile_reset()
+    assert S.sfi_profile_read(S.SFI_K_FAST) == (0.0, 0)

@@ -33,6 +33,46 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3_128k_layer_traffic.json")
+
+
+def csrc_digest():
+    """Digest of the kernel sources; counter readings apply only to kernels
+    built from the sources they were taken on."""
+    import hashlib
+    d = os.path.join(ROOT, "sparse_kv_attention_sfi_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_group(name):
+    """Bench kernel name of a device kernel (the Selector's four kernels form one group)."""
+    for key, group in (("slow_partial", "slow_partial"), ("slow_combine", "slow_combine"), ("select_", "select"),
+                       ("pack_kernel", "pack"), ("fast_packed", "fast_partial"), ("fast_partial", "fast_partial"),
+                       ("fast_merge", "fast_merge")):
+        if key in name:
+            return group
+    return None
+
+
+def measured_traffic(group, workload_name):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of a kernel group, if
+    the committed counter summary matches the current kernel sources."""
+    if workload_name != "C3-8B-layer-128K" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    if t.get("csrc_digest") != csrc_digest():
+        return None
+    ks = [k for k in t["kernels"].values() if k.get("group") == group]
+    if not ks:
+        return None
+    return sum(k.get("fetch_bytes", 0.0) + k.get("write_bytes", 0.0) for k in ks)
 METRIC = "decode-attn steps/sec/layer (slow, fast, blended) + HBM GB/s frac @128K ctx"
 
 
@@ -253,10 +293,11 @@ def main():
         "kernels": kern,
         "kernel_time_share": {n: t / sum(total_time.values()) for n, t in total_time.items()},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": d.get("frac"), "traffic": None,
+                     "unit": "GB/s", "frac": d.get("frac"), "traffic": measured_traffic(dominant, w.name),
                      "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},
         "roofline_slow_partial": {"bound": "hbm", "achieved": kern["slow_partial"]["GBps"], "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": kern["slow_partial"]["frac"],
+                                  "traffic": measured_traffic("slow_partial", w.name),
                                   "avg_launch_us": kern["slow_partial"]["avg_us"]},
     }
     if not args.no_cpu:

@@ -37,6 +37,8 @@
  *  - Queries q are [B][Hq][D] in kv_dtype.  Outputs are float32.
  *  - Only the batch rows named in seq_ids (host array, distinct values in
  *    [0, B)) are read or written by a call.
+ *  - Arrays with a top_k extent (sel_idx, packed_k, packed_v) may be NULL
+ *    when top_k = 0.
  *  - Supported shapes: head_dim 64 or 128; Hq / Hkv in {1, 2, 4, 8};
  *    kv_dtype SFI_F32 or SFI_BF16; 1 <= ctx_len[b] <= kv_capacity.
  */
@@ -64,7 +66,7 @@ typedef enum {
 
 typedef enum { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
 
-typedef enum { SFI_OP_SLOW = 0, SFI_OP_SELECT = 1, SFI_OP_FAST = 2 } sfi_op;
+typedef enum { SFI_OP_SLOW = 0, SFI_OP_SELECT = 1, SFI_OP_FAST = 2, SFI_OP_SLOW_SELECT = 3 } sfi_op;
 
 /* One layer's KV cache and the current context lengths. */
 typedef struct {
@@ -98,7 +100,8 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp
 
 /* Prepares a freshly allocated workspace (device, ws_bytes) for use: clears
  * the bookkeeping the Selector keeps at its start (a per-head histogram and a
- * list counter).  Call once after allocation, before the first sfi_select;
+ * list counter).  Call once after allocation, before the first sfi_select
+ * or sfi_slow_step_select;
  * the Selector's kernels leave that bookkeeping cleared when they finish.
  * Workspaces must not be shared by calls that may run concurrently. */
 int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream);
@@ -168,6 +171,25 @@ int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* 
                              const int32_t* seq_ids_host, int32_t n_seq, const void* q,
                              const void* packed_k, const void* packed_v, const int32_t* sel_cnt,
                              float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The slow step and the Selector in one call, with the selected rows packed
+ * as they are chosen: the whole refresh that opens a span ("Slow-Fast
+ * Inference ...", gist.science technical summary, 2.A and 2.B; packing: 3
+ * "Systemdesign und Kernel-Optimierung").  Writes exactly what
+ *   sfi_slow_step(q, out, mass); sfi_select(mass, sel_idx, sel_cnt);
+ *   sfi_pack_support(sel_idx, sel_cnt, packed_k, packed_v)
+ * would, bit for bit, in fewer kernels: the merge that produces the mass also
+ * builds the Selector's first radix histogram, and the pass that emits the
+ * kept positions also copies their K/V rows.
+ *   q, out, mass     : as for sfi_slow_step; mass must not be NULL
+ *   sel_idx, sel_cnt : as for sfi_select
+ *   packed_k/_v      : as for sfi_pack_support, or both NULL to skip packing
+ *   ws               : at least sfi_workspace_bytes(desc, sp, SFI_OP_SLOW_SELECT)
+ *                      bytes, prepared once by sfi_workspace_init. */
+int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                             const int32_t* seq_ids_host, int32_t n_seq, const void* q, float* out,
+                             float* mass, int32_t* sel_idx, int32_t* sel_cnt, void* packed_k,
+                             void* packed_v, void* ws, size_t ws_bytes, void* stream);
 
 /* Appends one token per listed sequence: writes k_new[b][g][:] and
  * v_new[b][g][:] (device [B][Hkv][D], kv_dtype) into row ctx_len[b] of

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libsfi.so")
 
 SFI_OK, SFI_ERR_INVALID_ARG, SFI_ERR_UNSUPPORTED, SFI_ERR_WORKSPACE, SFI_ERR_HIP, SFI_ERR_INJECTED = 0, -1, -2, -3, -4, -5
 SFI_F32, SFI_BF16 = 0, 1
-SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST = 0, 1, 2
+SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_OP_SLOW_SELECT = 0, 1, 2, 3
 SFI_SPAN_FIXED, SFI_SPAN_GEOMETRIC = 0, 1
 SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK, SFI_K_FAST_MERGE = range(7)
 KERNEL_NAMES = {SFI_K_SLOW_PARTIAL: "slow_partial", SFI_K_SLOW_COMBINE: "slow_combine",
@@ -69,6 +69,7 @@ def lib():
             "sfi_kv_append": (I32, [D, P(I32), I32, VP, VP, VP]),
             "sfi_pack_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP]),
             "sfi_fast_step_packed": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
+            "sfi_slow_step_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "sfi_debug_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, I32, VP]),
             "sfi_sched_create": (I32, [I32, C.c_uint64, I32, C.c_double, I32, P(VP)]),
             "sfi_sched_step": (I32, [VP, P(I32), P(I32), P(I32), P(I32)]),
@@ -181,7 +182,7 @@ def sfi_workspace_init(ws, stream=None):
            "sfi_workspace_init")
 
 
-def alloc_workspace(kv: KVDesc, sp=None, ops=(SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST)):
+def alloc_workspace(kv: KVDesc, sp=None, ops=(SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_OP_SLOW_SELECT)):
     """One workspace large enough for every op in ``ops`` (torch allocation),
     prepared with sfi_workspace_init."""
     import torch
@@ -214,6 +215,25 @@ def sfi_select(kv: KVDesc, sp, seq_ids, mass, sel_idx, sel_cnt, ws=None, stream=
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sfi_select(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(mass), _ptr(sel_idx), _ptr(sel_cnt),
                             _ptr(ws), nbytes, _stream(stream)), "sfi_select")
+
+
+def sfi_slow_step_select(kv: KVDesc, sp, seq_ids, q, out, mass, sel_idx, sel_cnt, packed_k=None, packed_v=None,
+                         ws=None, stream=None):
+    import torch
+    B, Hq, Hkv, D = kv.batch, kv.n_q_heads, kv.n_kv_heads, kv.head_dim
+    _need(q, kv.dtype, (B, Hq, D), "q")
+    _need(out, torch.float32, (B, Hq, D), "out")
+    _need(mass, torch.float32, (B, Hkv, kv.capacity), "mass")
+    _need(sel_idx, torch.int32, (B, Hkv, sp.top_k), "sel_idx")
+    _need(sel_cnt, torch.int32, (B, Hkv), "sel_cnt")
+    if packed_k is not None or packed_v is not None:
+        _need(packed_k, kv.dtype, (B, Hkv, sp.top_k, D), "packed_k")
+        _need(packed_v, kv.dtype, (B, Hkv, sp.top_k, D), "packed_v")
+    _, ids, n = _ids(seq_ids)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sfi_slow_step_select(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(out), _ptr(mass),
+                                      _ptr(sel_idx), _ptr(sel_cnt), _ptr(packed_k), _ptr(packed_v), _ptr(ws),
+                                      nbytes, _stream(stream)), "sfi_slow_step_select")
 
 
 def sfi_fast_step(kv: KVDesc, sp, seq_ids, q, sel_idx, sel_cnt, out, ws, stream=None):

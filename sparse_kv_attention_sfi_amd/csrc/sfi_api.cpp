@@ -266,6 +266,123 @@ int32_t for_each_group(const int32_t* ids, int32_t n, F&& f) {
   return SFI_OK;
 }
 
+// ---- launch planning ------------------------------------------------------
+// Slow step: split-K partial over the whole history, then the combine
+// (output merge + mass).  Fills the launch arguments of one id group.
+void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const void* q, float* out, float* mass,
+               char* w, SlowArgs& a, CombineArgs& c) {
+  const SlowLayout L = slow_layout(desc);
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int unit = slow_unit_rows(desc);
+  const int target = std::max(64, env_int("SFI_SLOW_TARGET_WGS", kSlowTargetWgs));
+  a.k = desc->k;
+  a.v = desc->v;
+  a.q = q;
+  a.logits = mass ? reinterpret_cast<float*>(w + L.logits) : nullptr;
+  a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+  a.part_o = reinterpret_cast<float*>(w + L.part_o);
+  a.out = out;
+  a.mass = mass;
+  a.t_cap = desc->kv_capacity;
+  a.n_q_heads = desc->n_q_heads;
+  a.n_kv_heads = desc->n_kv_heads;
+  a.part_stride = slow_part_stride(desc);
+  a.scale_log2 = logit_scale(desc);
+  a.logit_pitch = logit_pitch(desc);
+  int64_t rows = 0, t_max = 1;
+  for (int i = 0; i < cnt; ++i) {
+    rows += static_cast<int64_t>(desc->ctx_len_host[ids[i]]) * desc->n_kv_heads;
+    t_max = std::max<int64_t>(t_max, desc->ctx_len_host[ids[i]]);
+  }
+  // at most kMaxMergeSlots splits per head (the merge stages them in LDS)
+  const int64_t per = std::max(ceil_div(rows, target), ceil_div(t_max, kMaxMergeSlots));
+  a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
+  a.tab.n = cnt;
+  a.tab.wg_begin[0] = 0;
+  c.tab.n = cnt;
+  c.tab.wg_begin[0] = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const int b = ids[i];
+    const int T = desc->ctx_len_host[b];
+    a.tab.seq[i] = b;
+    a.tab.ctx[i] = T;
+    a.tab.nsplit[i] = static_cast<int32_t>(ceil_div(T, a.split_rows));
+    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+    c.mass_blocks[i] = mass ? static_cast<int32_t>(ceil_div(T, kMassChunk)) : 0;
+    c.tab.seq[i] = b;
+    c.tab.ctx[i] = T;
+    c.tab.nsplit[i] = a.tab.nsplit[i];
+    c.tab.wg_begin[i + 1] = c.tab.wg_begin[i] + desc->n_kv_heads * (c.mass_blocks[i] + G);
+  }
+  c.logits = a.logits;
+  c.part_ml = a.part_ml;
+  c.part_o = a.part_o;
+  c.out = out;
+  c.mass = mass;
+  c.t_cap = a.t_cap;
+  c.n_q_heads = a.n_q_heads;
+  c.n_kv_heads = a.n_kv_heads;
+  c.part_stride = a.part_stride;
+  c.logit_pitch = a.logit_pitch;
+}
+
+int32_t run_slow(const sfi_kv_desc* desc, const SlowArgs& a, const CombineArgs& c, int32_t cnt, hipStream_t s) {
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  hipError_t e = timed(SFI_K_SLOW_PARTIAL, s, [&] {
+    return launch_slow_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "slow partial launch");
+  e = timed(SFI_K_SLOW_COMBINE, s, [&] { return launch_slow_combine(c, desc->head_dim, G, c.tab.wg_begin[cnt], s); });
+  if (e != hipSuccess) return hip_fail(e, "slow combine launch");
+  return SFI_OK;
+}
+
+// Selector: candidates of each (sequence, KV head) cut into chunks of at
+// least kSelMinChunk, at most kSelMaxChunks chunks per head.
+void plan_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* ids, int32_t cnt,
+                 const float* mass, int32_t* sel_idx, int32_t* sel_cnt, char* w, SelectArgs& a) {
+  const SelectLayout L = select_layout(desc);
+  const Header H = header_layout(desc);
+  a.mass = mass;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
+  a.list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
+  a.list = reinterpret_cast<uint64_t*>(w + L.list);
+  a.chunk_above = reinterpret_cast<int32_t*>(w + L.chunk_above);
+  a.chunk_off = reinterpret_cast<int32_t*>(w + L.chunk_off);
+  a.kstar = reinterpret_cast<uint64_t*>(w + L.kstar);
+  a.t_cap = desc->kv_capacity;
+  a.n_kv_heads = desc->n_kv_heads;
+  a.n_sink = sp->n_sink;
+  a.n_recent = sp->n_recent;
+  a.top_k = sp->top_k;
+  a.lambda = sp->lambda;
+  int64_t n_max = 0;
+  for (int i = 0; i < cnt; ++i)
+    n_max = std::max<int64_t>(n_max, desc->ctx_len_host[ids[i]] - static_cast<int64_t>(sp->n_sink) - sp->n_recent);
+  const int64_t chunk = std::max<int64_t>(kSelMinChunk, ceil_div(ceil_div(n_max, kSelMaxChunks), 512) * 512);
+  a.chunk = static_cast<int32_t>(chunk);
+  a.tab.n = cnt;
+  a.tab.wg_begin[0] = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const int64_t T = desc->ctx_len_host[ids[i]];
+    const int64_t n = std::max<int64_t>(0, T - sp->n_sink - sp->n_recent);
+    const bool keep_all = n <= sp->top_k || sp->top_k == 0;
+    const int64_t M = keep_all ? std::max<int64_t>(1, ceil_div(sp->top_k, chunk)) : ceil_div(n, chunk);
+    a.tab.seq[i] = ids[i];
+    a.tab.ctx[i] = static_cast<int32_t>(T);
+    a.tab.nsplit[i] = static_cast<int32_t>(M);
+    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+  }
+}
+
+int32_t run_select(const SelectArgs& a, int32_t cnt, hipStream_t s) {
+  const int grid = a.tab.wg_begin[cnt];
+  const hipError_t e = timed(SFI_K_SELECT, s, [&] { return launch_select(a, grid, s); });
+  return e == hipSuccess ? SFI_OK : hip_fail(e, "select launch");
+}
+
 }  // namespace
 
 LaunchTiming* launch_timing() { return g_timing; }
@@ -302,6 +419,9 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp
     case SFI_OP_FAST:
       if (check_params(sp) != SFI_OK) return 0;
       return fast_layout(desc, sp).end;
+    case SFI_OP_SLOW_SELECT:
+      if (check_params(sp) != SFI_OK) return 0;
+      return std::max(slow_layout(desc).end, select_layout(desc).end);
     default: fail(SFI_ERR_INVALID_ARG, "unknown op %d", op); return 0;
   }
 }
@@ -320,72 +440,14 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
   if (n_seq == 0) return SFI_OK;
   if (q == nullptr || out == nullptr) return fail(SFI_ERR_INVALID_ARG, "q / out is NULL");
-  const SlowLayout L = slow_layout(desc);
-  if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, slow_layout(desc).end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = desc->n_q_heads / desc->n_kv_heads;
-  const int unit = slow_unit_rows(desc);
-  const int target = std::max(64, env_int("SFI_SLOW_TARGET_WGS", 1024));
   char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SlowArgs a{};
-    a.k = desc->k;
-    a.v = desc->v;
-    a.q = q;
-    a.logits = mass ? reinterpret_cast<float*>(w + L.logits) : nullptr;
-    a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
-    a.part_o = reinterpret_cast<float*>(w + L.part_o);
-    a.out = out;
-    a.mass = mass;
-    a.t_cap = desc->kv_capacity;
-    a.n_q_heads = desc->n_q_heads;
-    a.n_kv_heads = desc->n_kv_heads;
-    a.part_stride = slow_part_stride(desc);
-    a.scale_log2 = logit_scale(desc);
-    a.logit_pitch = logit_pitch(desc);
-    int64_t rows = 0;
-    for (int i = 0; i < cnt; ++i) rows += static_cast<int64_t>(desc->ctx_len_host[ids[i]]) * desc->n_kv_heads;
-    int64_t t_max = 1;
-    for (int i = 0; i < cnt; ++i) t_max = std::max<int64_t>(t_max, desc->ctx_len_host[ids[i]]);
-    // at most kMaxMergeSlots splits per head (the merge stages them in LDS)
-    const int64_t per = std::max(ceil_div(rows, target), ceil_div(t_max, kMaxMergeSlots));
-    a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
     CombineArgs c{};
-    a.tab.n = cnt;
-    a.tab.wg_begin[0] = 0;
-    c.tab.wg_begin[0] = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const int b = ids[i];
-      const int T = desc->ctx_len_host[b];
-      a.tab.seq[i] = b;
-      a.tab.ctx[i] = T;
-      a.tab.nsplit[i] = static_cast<int32_t>(ceil_div(T, a.split_rows));
-      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
-      c.mass_blocks[i] = mass ? static_cast<int32_t>(ceil_div(T, kMassChunk)) : 0;
-      c.tab.seq[i] = b;
-      c.tab.ctx[i] = T;
-      c.tab.nsplit[i] = a.tab.nsplit[i];
-      c.tab.wg_begin[i + 1] = c.tab.wg_begin[i] + desc->n_kv_heads * (c.mass_blocks[i] + G);
-    }
-    c.tab.n = cnt;
-    c.logits = a.logits;
-    c.part_ml = a.part_ml;
-    c.part_o = a.part_o;
-    c.out = out;
-    c.mass = mass;
-    c.t_cap = a.t_cap;
-    c.n_q_heads = a.n_q_heads;
-    c.n_kv_heads = a.n_kv_heads;
-    c.part_stride = a.part_stride;
-    c.logit_pitch = a.logit_pitch;
-    hipError_t e = timed(SFI_K_SLOW_PARTIAL, s, [&] {
-      return launch_slow_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "slow partial launch");
-    e = timed(SFI_K_SLOW_COMBINE, s,
-              [&] { return launch_slow_combine(c, desc->head_dim, G, c.tab.wg_begin[cnt], s); });
-    if (e != hipSuccess) return hip_fail(e, "slow combine launch");
-    return SFI_OK;
+    plan_slow(desc, ids, cnt, q, out, mass, w, a, c);
+    return run_slow(desc, a, c, cnt, s);
   });
 }
 
@@ -399,50 +461,62 @@ int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const 
   if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
   if (fault_injected("select")) return fail(SFI_ERR_INJECTED, "select failure forced by SFI_FAULT_INJECT");
   if (n_seq == 0) return SFI_OK;
-  if (mass == nullptr || sel_idx == nullptr || sel_cnt == nullptr)
+  if (mass == nullptr || sel_cnt == nullptr || (sel_idx == nullptr && sp->top_k > 0))
     return fail(SFI_ERR_INVALID_ARG, "mass / sel_idx / sel_cnt is NULL");
-  const SelectLayout L = select_layout(desc);
-  const Header H = header_layout(desc);
-  if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, select_layout(desc).end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SelectArgs a{};
-    a.mass = mass;
-    a.sel_idx = sel_idx;
-    a.sel_cnt = sel_cnt;
-    a.hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
-    a.list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
-    a.list = reinterpret_cast<uint64_t*>(w + L.list);
-    a.chunk_above = reinterpret_cast<int32_t*>(w + L.chunk_above);
-    a.chunk_off = reinterpret_cast<int32_t*>(w + L.chunk_off);
-    a.kstar = reinterpret_cast<uint64_t*>(w + L.kstar);
-    a.t_cap = desc->kv_capacity;
-    a.n_kv_heads = desc->n_kv_heads;
-    a.n_sink = sp->n_sink;
-    a.n_recent = sp->n_recent;
-    a.top_k = sp->top_k;
-    a.lambda = sp->lambda;
-    int64_t n_max = 0;
-    for (int i = 0; i < cnt; ++i)
-      n_max = std::max<int64_t>(n_max, desc->ctx_len_host[ids[i]] - static_cast<int64_t>(sp->n_sink) - sp->n_recent);
-    const int64_t chunk = std::max<int64_t>(kSelMinChunk, ceil_div(ceil_div(n_max, kSelMaxChunks), 512) * 512);
-    a.chunk = static_cast<int32_t>(chunk);
-    a.tab.n = cnt;
-    a.tab.wg_begin[0] = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const int64_t T = desc->ctx_len_host[ids[i]];
-      const int64_t n = std::max<int64_t>(0, T - sp->n_sink - sp->n_recent);
-      const bool keep_all = n <= sp->top_k || sp->top_k == 0;
-      const int64_t M = keep_all ? std::max<int64_t>(1, ceil_div(sp->top_k, chunk)) : ceil_div(n, chunk);
-      a.tab.seq[i] = ids[i];
-      a.tab.ctx[i] = static_cast<int32_t>(T);
-      a.tab.nsplit[i] = static_cast<int32_t>(M);
-      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+    plan_select(desc, sp, ids, cnt, mass, sel_idx, sel_cnt, w, a);
+    return run_select(a, cnt, s);
+  });
+}
+
+int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                             int32_t n_seq, const void* q, float* out, float* mass, int32_t* sel_idx,
+                             int32_t* sel_cnt, void* packed_k, void* packed_v, void* ws, size_t ws_bytes,
+                             void* stream) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_kv(desc)) != SFI_OK) return st;
+  if ((st = check_params(sp)) != SFI_OK) return st;
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (fault_injected("select")) return fail(SFI_ERR_INJECTED, "select failure forced by SFI_FAULT_INJECT");
+  if (n_seq == 0) return SFI_OK;
+  if (q == nullptr || out == nullptr || mass == nullptr || sel_cnt == nullptr ||
+      (sel_idx == nullptr && sp->top_k > 0))
+    return fail(SFI_ERR_INVALID_ARG, "q / out / mass / sel_idx / sel_cnt is NULL");
+  if ((packed_k == nullptr) != (packed_v == nullptr))
+    return fail(SFI_ERR_INVALID_ARG, "packed_k and packed_v must both be given or both be NULL");
+  if ((st = check_ws(ws, ws_bytes, std::max(slow_layout(desc).end, select_layout(desc).end))) != SFI_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const Header H = header_layout(desc);
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    // the slow scratch and the Selector scratch overlap: the Selector's
+    // kernels run after the combine has consumed the logits and partials
+    SlowArgs a{};
+    CombineArgs c{};
+    plan_slow(desc, ids, cnt, q, out, mass, w, a, c);
+    c.sel_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
+    c.n_sink = sp->n_sink;
+    c.n_recent = sp->n_recent;
+    c.top_k = sp->top_k;
+    c.lambda = sp->lambda;
+    int32_t r = run_slow(desc, a, c, cnt, s);
+    if (r != SFI_OK) return r;
+    SelectArgs sa{};
+    plan_select(desc, sp, ids, cnt, mass, sel_idx, sel_cnt, w, sa);
+    sa.hist_ready = true;
+    if (packed_k != nullptr) {
+      sa.k = desc->k;
+      sa.v = desc->v;
+      sa.packed_k = packed_k;
+      sa.packed_v = packed_v;
+      sa.row_bytes = desc->head_dim * elem_bytes(desc->kv_dtype);
     }
-    const int grid = a.tab.wg_begin[cnt];
-    const hipError_t e = timed(SFI_K_SELECT, s, [&] { return launch_select(a, grid, s); });
-    return e == hipSuccess ? SFI_OK : hip_fail(e, "select launch");
+    return run_select(sa, cnt, s);
   });
 }
 
@@ -458,7 +532,7 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
   if (n_seq == 0) return SFI_OK;
   if (q == nullptr || out == nullptr || sel_cnt == nullptr)
     return fail(SFI_ERR_INVALID_ARG, "q / out / sel_cnt is NULL");
-  if (sel_idx == nullptr && (packed_k == nullptr || packed_v == nullptr))
+  if (sel_idx == nullptr && (packed_k == nullptr || packed_v == nullptr) && sp->top_k > 0)
     return fail(SFI_ERR_INVALID_ARG, "sel_idx (or packed_k / packed_v) is NULL");
   if (sp->n_sink == 0 && sp->n_recent == 0 && sp->top_k == 0)
     return fail(SFI_ERR_INVALID_ARG, "the support is empty (n_sink = n_recent = top_k = 0)");
@@ -519,14 +593,15 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
 int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids, int32_t n_seq,
                       const void* q, const int32_t* sel_idx, const int32_t* sel_cnt, float* out, void* ws,
                       size_t ws_bytes, void* stream) {
-  if (sel_idx == nullptr) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
+  if (sel_idx == nullptr && sp != nullptr && sp->top_k > 0) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
   return fast_step_impl(desc, sp, seq_ids, n_seq, q, sel_idx, nullptr, nullptr, sel_cnt, out, ws, ws_bytes, stream);
 }
 
 int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
                              int32_t n_seq, const void* q, const void* packed_k, const void* packed_v,
                              const int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes, void* stream) {
-  if (packed_k == nullptr || packed_v == nullptr) return fail(SFI_ERR_INVALID_ARG, "packed_k / packed_v is NULL");
+  if ((packed_k == nullptr || packed_v == nullptr) && sp != nullptr && sp->top_k > 0)
+    return fail(SFI_ERR_INVALID_ARG, "packed_k / packed_v is NULL");
   return fast_step_impl(desc, sp, seq_ids, n_seq, q, nullptr, packed_k, packed_v, sel_cnt, out, ws, ws_bytes,
                         stream);
 }

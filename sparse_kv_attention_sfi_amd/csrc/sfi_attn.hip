@@ -37,6 +37,7 @@
 
 #include "sfi_device.hpp"
 #include "sfi_internal.hpp"
+#include "sfi_score.hpp"
 
 namespace sfi {
 
@@ -87,13 +88,15 @@ struct Attn {
   //   vb[i]     : V pieces in row layout (row lane / PPR + RPL * i)
   //   kvalid[t] : row 16 t + lane % 16 exists
   //   Pw        : this wave's LDS staging area, TILES * 16 * G floats
-  //   logit_row : if non-null, logits of row 16 t + lane % 16 of head h go to
-  //               logit_row[h * head_stride + 16 t]
+  //   logit_base: if non-null, the block's logits go to
+  //               logit_base[h * head_stride + r] for rows r < valid_rows,
+  //               staged through Pw so that each lane writes four consecutive
+  //               rows of one head with a single 16-byte store
   template <int TILES>
   __device__ __forceinline__ void consume(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
                                           const uint4 (&vb)[TILES * 16 / kRPL],
                                           const bool (&kvalid)[TILES], float* Pw, float scale_log2,
-                                          float* logit_row, int64_t head_stride, int lane) {
+                                          float* logit_base, int64_t head_stride, int valid_rows, int lane) {
     constexpr int NV = TILES * 16 / kRPL;
     // logits
     float x[TILES][4];
@@ -106,14 +109,33 @@ struct Attn {
       for (int e = 0; e < 4; ++e) x[t][e] = kvalid[t] ? c[e] * scale_log2 : -INFINITY;
     }
     const int grp = lane >> 4;
-    if (logit_row != nullptr && grp < kGroups) {
+    if (logit_base != nullptr) {
+      constexpr int ROWS = TILES * 16;
+      wave_sync();
+      if (grp < kGroups) {
 #pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        if (!kvalid[t]) continue;
+        for (int t = 0; t < TILES; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int h = 4 * grp + e;
-          if (h < G) logit_row[h * head_stride + 16 * t] = x[t][e];
+          for (int e = 0; e < 4; ++e) {
+            const int h = 4 * grp + e;
+            if (h < G) Pw[h * ROWS + 16 * t + (lane & 15)] = x[t][e];
+          }
+      }
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < (G * ROWS + 255) / 256; ++j) {
+        const int flat = 4 * (64 * j + lane);
+        if (flat < G * ROWS) {
+          const int h = flat / ROWS, r = flat - h * ROWS;
+          const float4 v = *reinterpret_cast<const float4*>(Pw + flat);
+          float* dst = logit_base + h * head_stride + r;
+          if (r + 4 <= valid_rows) {
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+            if (r < valid_rows) dst[0] = v.x;
+            if (r + 1 < valid_rows) dst[1] = v.y;
+            if (r + 2 < valid_rows) dst[2] = v.z;
+          }
         }
       }
     }
@@ -409,8 +431,8 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
       const int row = min(r0 + vr + A::kRPL * i, r_end - 1);
       vb[i] = ld16(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
     }
-    float* lrow = a.logits ? a.logits + qh0 * a.logit_pitch + r0 + kr : nullptr;
-    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lrow, a.logit_pitch, lane);
+    float* lbase = a.logits ? a.logits + qh0 * a.logit_pitch + r0 : nullptr;
+    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lbase, a.logit_pitch, r_end - r0, lane);
   }
   st.finish_wave(s_m, s_l, s_o, wave, lane);
   __syncthreads();
@@ -576,12 +598,18 @@ __device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_hstri
 // ---------------------------------------------------------------------------
 // slow step, kernel 2: merge partials; per-position softmax mass
 // ---------------------------------------------------------------------------
-template <int D, int G>
+//
+// With HIST, the mass workgroups also add every candidate's top key digit to
+// the Selector's histogram (the first pass of its radix top-k), using the same
+// score function as the Selector on the very value they store as the mass.
+template <int D, int G, bool HIST>
 __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineArgs a) {
   constexpr int NW = kCombineThreads / 64;
   constexpr int PER = kMassChunk / (4 * kCombineThreads);  // float4 groups per thread
   __shared__ float s_M[G], s_invL[G];
   __shared__ MergeSmem<1, kCombineThreads> s_merge;
+  __shared__ uint32_t s_hist[HIST ? kSelBins : 1];
+  __shared__ float s_inv2h;
 
   const int tid = threadIdx.x;
   const int wg = blockIdx.x;
@@ -614,8 +642,23 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
         x[it][h] = j < j1 ? *reinterpret_cast<const float4*>(lg + h * a.logit_pitch + j)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    head_max_sum<G, NW>(ml, ml_hstride, nsplit, s_M, s_invL);
+    // candidates [n_sink, T - n_recent) take part in a top-k only when there
+    // are more of them than k (otherwise the Selector keeps all of them)
+    const int n_cand = max(0, T - a.n_sink - a.n_recent);
+    const bool hist = HIST && n_cand > a.top_k && a.top_k > 0;
+    if (hist) {
+      for (int i = tid; i < kSelBins; i += kCombineThreads) s_hist[i] = 0u;
+      if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(n_cand)));
+    }
+    head_max_sum<G, NW>(ml, ml_hstride, nsplit, s_M, s_invL);  // ends with a barrier
     const float invG = 1.f / static_cast<float>(G);
+    ScoreParams sp;
+    sp.f = nullptr;
+    sp.n = n_cand;
+    sp.lo = a.n_sink;
+    sp.lambda = a.lambda;
+    sp.one_minus_lambda = 1.0f - a.lambda;
+    sp.inv_2h = hist ? s_inv2h : 0.f;
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
       const int j = j0 + 4 * (it * kCombineThreads + tid);
@@ -630,8 +673,21 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
         f[3] += fast_exp2(x[it][h].w - M) * il;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (j + u < j1) mrow[j + u] = f[u] * invG;
+      for (int u = 0; u < 4; ++u) {
+        if (j + u >= j1) continue;
+        const float m = f[u] * invG;
+        mrow[j + u] = m;
+        if (hist) {
+          const int i = j + u - a.n_sink;
+          if (i >= 0 && i < n_cand) atomicAdd(&s_hist[top_digit(key_of(sp, i, m))], 1u);
+        }
+      }
+    }
+    if (hist) {
+      __syncthreads();
+      uint32_t* gh = a.sel_hist + (static_cast<int64_t>(b) * a.n_kv_heads + g) * kSelBins;
+      for (int i = tid; i < kSelBins; i += kCombineThreads)
+        if (s_hist[i] != 0u) atomicAdd(gh + i, s_hist[i]);
     }
   } else {
     const int h = r - mblocks;
@@ -742,7 +798,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
     // a wave whose rows are all outside the support keeps the empty state
     if (__ballot(any) != 0) {
       st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr,
-                                 0, lane);
+                                 0, 0, lane);
     }
   }
   st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
@@ -834,7 +890,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
 #pragma unroll
   for (int tt = 0; tt < TILES; ++tt) kvalid[tt] = (w0 + 16 * tt + kr) < size;
   if (w0 < size) {
-    st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, lane);
+    st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, 0, lane);
   }
   st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
   __syncthreads();
@@ -980,13 +1036,13 @@ hipError_t launch_slow_partial(const SlowArgs& a, int dtype, int head_dim, int g
                          : slow_partial_g<F32, 64>(a, group, grid, s);
 }
 
-template <int D>
+template <int D, bool HIST>
 static hipError_t slow_combine_g(const CombineArgs& a, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: launch(slow_combine_kernel<D, 1>, grid, kCombineThreads, s, a); break;
-    case 2: launch(slow_combine_kernel<D, 2>, grid, kCombineThreads, s, a); break;
-    case 4: launch(slow_combine_kernel<D, 4>, grid, kCombineThreads, s, a); break;
-    case 8: launch(slow_combine_kernel<D, 8>, grid, kCombineThreads, s, a); break;
+    case 1: launch(slow_combine_kernel<D, 1, HIST>, grid, kCombineThreads, s, a); break;
+    case 2: launch(slow_combine_kernel<D, 2, HIST>, grid, kCombineThreads, s, a); break;
+    case 4: launch(slow_combine_kernel<D, 4, HIST>, grid, kCombineThreads, s, a); break;
+    case 8: launch(slow_combine_kernel<D, 8, HIST>, grid, kCombineThreads, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -994,8 +1050,11 @@ static hipError_t slow_combine_g(const CombineArgs& a, int group, int grid, hipS
 
 hipError_t launch_slow_combine(const CombineArgs& a, int head_dim, int group, int grid,
                                hipStream_t s) {
-  return head_dim == 128 ? slow_combine_g<128>(a, group, grid, s)
-                         : slow_combine_g<64>(a, group, grid, s);
+  if (a.sel_hist != nullptr && a.mass != nullptr)
+    return head_dim == 128 ? slow_combine_g<128, true>(a, group, grid, s)
+                           : slow_combine_g<64, true>(a, group, grid, s);
+  return head_dim == 128 ? slow_combine_g<128, false>(a, group, grid, s)
+                         : slow_combine_g<64, false>(a, group, grid, s);
 }
 
 // Fast-step rows per wave (16 per tile).  Small chunks keep many workgroups

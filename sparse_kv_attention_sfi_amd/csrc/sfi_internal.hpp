@@ -25,6 +25,7 @@ constexpr int kSelMinChunk = 4096;   // candidates per chunk (at least)
 constexpr int kFastThreads = 256;    // 4 waves, gather kernel
 constexpr int kMergeThreads = 1024;  // fast-step chunk merge
 constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a merge accepts
+constexpr int kSlowTargetWgs = 1024;  // slow partial workgroups aimed at per launch
 
 struct SeqTable {
   int32_t n;                              // entries used
@@ -65,6 +66,12 @@ struct CombineArgs {
   int32_t n_kv_heads;
   int32_t part_stride;
   int64_t logit_pitch;
+  // optional: the Selector's top-digit histogram built next to the mass
+  uint32_t* sel_hist;  // [B * Hkv][4096] or nullptr
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t top_k;
+  float lambda;
   SeqTable tab;  // nsplit = split-K splits; wg_begin counts combine workgroups
   int32_t mass_blocks[kMaxSeqPerLaunch];  // per entry: mass workgroups per KV head
 };
@@ -89,6 +96,13 @@ struct SelectArgs {
   int32_t top_k;
   int32_t chunk;         // candidates per workgroup
   float lambda;
+  bool hist_ready;       // the top-digit histogram was built with the mass
+  // optional: copy the kept rows into packed buffers while emitting them
+  const void* k;
+  const void* v;
+  void* packed_k;        // [B][Hkv][top_k][D] or nullptr
+  void* packed_v;
+  int32_t row_bytes;
   SeqTable tab;          // nsplit = chunks per KV head
 };
 

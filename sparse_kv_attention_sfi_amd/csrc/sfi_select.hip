@@ -33,38 +33,11 @@
 
 #include "sfi_device.hpp"
 #include "sfi_internal.hpp"
+#include "sfi_score.hpp"
 
 namespace sfi {
 
-constexpr int kSelDigitBits = 12;
-constexpr int kSelBins = 1 << kSelDigitBits;
 constexpr int kSelWaves = kSelThreads / 64;
-
-struct ScoreParams {
-  const float* f;   // mass row, shifted so that f[i] is candidate i
-  int n;
-  int lo;           // first candidate position
-  float one_minus_lambda;
-  float lambda;
-  float inv_2h;     // 1 / (2 H_n)
-};
-
-// Fused score and key of candidate i.  Evaluated identically in every pass.
-__device__ __forceinline__ uint64_t cand_key(const ScoreParams& p, int i) {
-#pragma clang fp contract(off)
-  const float a = static_cast<float>(i + 1);
-  const float b = static_cast<float>(p.n - i);
-  const float r = (__builtin_amdgcn_rcpf(a) + __builtin_amdgcn_rcpf(b)) * p.inv_2h;
-  const float s = __builtin_fmaf(p.lambda, r, p.one_minus_lambda * p.f[i]);
-  uint32_t u = __float_as_uint(s);
-  u ^= (u & 0x80000000u) ? 0xffffffffu : 0x80000000u;  // order-preserving
-  const uint32_t pos = static_cast<uint32_t>(p.lo + i);
-  return (static_cast<uint64_t>(u) << 32) | static_cast<uint64_t>(~pos);
-}
-
-__device__ __forceinline__ int key_position(uint64_t key) {
-  return static_cast<int>(~static_cast<uint32_t>(key & 0xffffffffull));
-}
 
 // Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
@@ -87,19 +60,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   __syncthreads();
   *total = all;
   return before + incl - v;
-}
-
-// Harmonic number in double: direct sum for small n, else the asymptotic
-// series ln n + gamma + 1/(2n) - 1/(12 n^2) + 1/(120 n^4) (error < 1/(252 n^6)).
-__device__ double harmonic_number(int n) {
-  if (n <= 256) {
-    double h = 0.0;
-    for (int i = n; i >= 1; --i) h += 1.0 / i;
-    return h;
-  }
-  const double x = static_cast<double>(n);
-  const double x2 = x * x;
-  return log(x) + 0.57721566490153286061 + 1.0 / (2.0 * x) - 1.0 / (12.0 * x2) + 1.0 / (120.0 * x2 * x2);
 }
 
 struct HeadCtx {
@@ -382,9 +342,50 @@ __global__ __launch_bounds__(kSelThreads) void select_finish_kernel(SelectArgs a
 // ---------------------------------------------------------------------------
 // 4. ordered emission
 // ---------------------------------------------------------------------------
+// Copies rows pos[r] of the cache into slots base + r of the packed buffers
+// for r < count; kernel-wide cooperative 16-byte copies.
+__device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const int* s_pos, int base, int count) {
+  const int np = a.row_bytes >> 4;  // 16-byte pieces per row
+  const int items = count * np;
+  const char* K = static_cast<const char*>(a.k) + bg * a.t_cap * a.row_bytes;
+  const char* V = static_cast<const char*>(a.v) + bg * a.t_cap * a.row_bytes;
+  char* PK = static_cast<char*>(a.packed_k) + (bg * a.top_k + base) * a.row_bytes;
+  char* PV = static_cast<char*>(a.packed_v) + (bg * a.top_k + base) * a.row_bytes;
+  constexpr int kU = 4;
+  for (int i0 = threadIdx.x; i0 < items; i0 += kU * kSelThreads) {
+    uint4 kv[kU], vv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int it = i0 + u * kSelThreads;
+      if (it < items) {
+        const int r = it / np, pc = it - r * np;
+        const int64_t off = static_cast<int64_t>(s_pos[r]) * a.row_bytes + 16 * pc;
+        kv[u] = ld16(K + off);
+        vv[u] = ld16(V + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int it = i0 + u * kSelThreads;
+      if (it < items) {
+        const int r = it / np, pc = it - r * np;
+        const int64_t off = static_cast<int64_t>(r) * a.row_bytes + 16 * pc;
+        *reinterpret_cast<uint4*>(PK + off) = kv[u];
+        *reinterpret_cast<uint4*>(PV + off) = vv[u];
+      }
+    }
+  }
+}
+
+// Writes the kept positions of the workgroup's chunk in ascending order at the
+// chunk's output offset.  With PACK it also copies their K and V rows into the
+// packed buffers at the same slots, so the fast step reads them contiguously.
+template <bool PACK>
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
+  constexpr int kStep = 4 * kSelThreads;  // candidates per pass
   __shared__ int s_wave[kSelWaves];
   __shared__ float s_inv2h;
+  __shared__ int s_pos[PACK ? kStep : 1];
   const HeadCtx h = head_ctx(a);
   const int tid = threadIdx.x;
   const int K = a.top_k;
@@ -393,6 +394,16 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     const int i0 = h.c * a.chunk, i1 = min(K, i0 + a.chunk);
     for (int i = i0 + tid; i < i1; i += kSelThreads) out[i] = i < h.n ? a.n_sink + i : -1;
     if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = min(h.n, K);
+    if (PACK) {
+      const int i_end = min(i1, h.n);
+      for (int r0 = i0; r0 < i_end; r0 += kStep) {
+        const int cnt = min(kStep, i_end - r0);
+        __syncthreads();
+        for (int r = tid; r < cnt; r += kSelThreads) s_pos[r] = a.n_sink + r0 + r;
+        __syncthreads();
+        copy_rows(a, h.bg, s_pos, r0, cnt);
+      }
+    }
     return;
   }
   if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   const uint64_t kstar = a.kstar[h.bg];
   int base = a.chunk_off[h.bg * kSelMaxChunks + h.c];
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
-  for (int t0 = i0; t0 < i1; t0 += 4 * kSelThreads) {
+  for (int t0 = i0; t0 < i1; t0 += kStep) {
     const int j0 = t0 + 4 * tid;
     int flags = 0, c = 0;
 #pragma unroll
@@ -413,25 +424,42 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
       }
     }
     int total;
-    int pos = base + block_excl_scan(c, s_wave, &total);
+    const int mine = block_excl_scan(c, s_wave, &total);  // ends with a barrier
+    int pos = base + mine;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if ((flags & (1 << u)) && pos < K) out[pos++] = a.n_sink + j0 + u;
+    for (int u = 0; u < 4; ++u) {
+      if ((flags & (1 << u)) && pos < K) {
+        out[pos] = a.n_sink + j0 + u;
+        if (PACK) s_pos[pos - base] = a.n_sink + j0 + u;
+        ++pos;
+      }
+    }
+    if (PACK) {
+      __syncthreads();
+      copy_rows(a, h.bg, s_pos, base, max(0, min(total, K - base)));
+      __syncthreads();
+    }
     base += total;
   }
 }
 
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s) {
-  launch(select_hist_kernel, grid, kSelThreads, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!a.hist_ready) {
+    launch(select_hist_kernel, grid, kSelThreads, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   launch(select_gather_kernel, grid, kSelThreads, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch(select_finish_kernel, a.tab.n * a.n_kv_heads, kSelThreads, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch(select_emit_kernel, grid, kSelThreads, s, a);
+  if (a.packed_k != nullptr)
+    launch(select_emit_kernel<true>, grid, kSelThreads, s, a);
+  else
+    launch(select_emit_kernel<false>, grid, kSelThreads, s, a);
   return hipGetLastError();
 }
 

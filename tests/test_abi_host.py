@@ -119,6 +119,16 @@ def test_validation_rejects_before_launch():
     st = lib.sfi_fast_step(C.byref(desc), C.byref(sp0), pid, 1, fake, fake, fake, fake, fake, 1 << 40, None)
     assert st == B.SFI_ERR_INVALID_ARG                         # empty support
     assert lib.sfi_slow_step(C.byref(desc), pid, 0, fake, fake, None, fake, 0, None) == 0   # nothing to do
+    sp = B.sfi_support_params(4, 16, 8, 0.1)
+    fused = lib.sfi_slow_step_select
+    assert fused(C.byref(desc), C.byref(sp), pid, 1, fake, fake, None, fake, fake, None, None, fake, 1 << 40,
+                 None) == B.SFI_ERR_INVALID_ARG                # mass is required
+    assert b"mass" in lib.sfi_last_error()
+    assert fused(C.byref(desc), C.byref(sp), pid, 1, fake, fake, fake, fake, fake, fake, None, fake, 1 << 40,
+                 None) == B.SFI_ERR_INVALID_ARG                # packed_k without packed_v
+    need = lib.sfi_workspace_bytes(C.byref(desc), C.byref(sp), B.SFI_OP_SLOW_SELECT)
+    assert fused(C.byref(desc), C.byref(sp), pid, 1, fake, fake, fake, fake, fake, None, None, fake, need - 1,
+                 None) == B.SFI_ERR_WORKSPACE
 
 
 def test_fault_injection_fails_select_before_launch(monkeypatch):
@@ -137,9 +147,12 @@ def test_workspace_bytes_grow_with_shape():
     d2, k2 = _desc(cap=100000)
     sp = B.sfi_support_params(16, 256, 2048, 0.1)
     lib = S.lib()
-    for op in (B.SFI_OP_SLOW, B.SFI_OP_SELECT, B.SFI_OP_FAST):
+    for op in (B.SFI_OP_SLOW, B.SFI_OP_SELECT, B.SFI_OP_FAST, B.SFI_OP_SLOW_SELECT):
         a = lib.sfi_workspace_bytes(C.byref(d1), C.byref(sp), op)
         b = lib.sfi_workspace_bytes(C.byref(d2), C.byref(sp), op)
         assert 0 < a <= b
+    fused = lib.sfi_workspace_bytes(C.byref(d2), C.byref(sp), B.SFI_OP_SLOW_SELECT)
+    assert fused == max(lib.sfi_workspace_bytes(C.byref(d2), C.byref(sp), op)
+                        for op in (B.SFI_OP_SLOW, B.SFI_OP_SELECT))
     bad, kb = _desc(d=96)
     assert lib.sfi_workspace_bytes(C.byref(bad), C.byref(sp), B.SFI_OP_SLOW) == 0

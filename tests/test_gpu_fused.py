@@ -1,0 +1,136 @@
+"""GPU parity of the fused slow-step + Selector + pack entry point: bit for bit
+equal to the three separate calls it replaces, and within tolerance of the
+oracle, on ragged multi-sequence batches and the Selector's edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_kv_attention_sfi_amd as S
+from tests.gpu_helpers import OUT_TOL, check_support, np64, oracle_slow, random_cache
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _outputs(kv, sp, packed):
+    dev = kv.k.device
+    B, Hq, Hkv, D, k = kv.batch, kv.n_q_heads, kv.n_kv_heads, kv.head_dim, sp.top_k
+    o = dict(out=torch.full((B, Hq, D), 7.0, device=dev),
+             mass=torch.full((B, Hkv, kv.capacity), -1.0, device=dev),
+             sel=torch.full((B, Hkv, k), -7, dtype=torch.int32, device=dev),
+             cnt=torch.full((B, Hkv), -7, dtype=torch.int32, device=dev))
+    if packed:
+        o["pk"] = torch.zeros(B, Hkv, k, D, dtype=kv.dtype, device=dev)
+        o["pv"] = torch.zeros(B, Hkv, k, D, dtype=kv.dtype, device=dev)
+    return o
+
+
+def _separate(kv, sp, ids, q, ws, packed=True):
+    o = _outputs(kv, sp, packed)
+    S.sfi_slow_step(kv, ids, q, o["out"], o["mass"], ws)
+    S.sfi_select(kv, sp, ids, o["mass"], o["sel"], o["cnt"], ws)
+    if packed:
+        S.sfi_pack_support(kv, sp, ids, o["sel"], o["cnt"], o["pk"], o["pv"])
+    return o
+
+
+def _fused(kv, sp, ids, q, ws, packed=True):
+    o = _outputs(kv, sp, packed)
+    S.sfi_slow_step_select(kv, sp, ids, q, o["out"], o["mass"], o["sel"], o["cnt"], o.get("pk"), o.get("pv"), ws)
+    return o
+
+
+def _assert_same(a, b):
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def _check_oracle(kv, sp, q, o, ids):
+    for b in ids:
+        T = int(kv.ctx[b])
+        o_ref, f_ref = oracle_slow(kv, q, b)
+        assert np.max(np.abs(np64(o["out"][b]) - o_ref)) < OUT_TOL
+        for g in range(kv.n_kv_heads):
+            c = int(o["cnt"][b, g])
+            sel = o["sel"][b, g, :c].cpu().numpy()
+            check_support(sel, f_ref[g], T, sp.n_sink, sp.n_recent, sp.top_k, sp.lambda_, f"b{b} g{g}")
+            if "pk" in o and c > 0:
+                rows = torch.from_numpy(sel.astype(np.int64)).to(kv.k.device)
+                assert torch.equal(o["pk"][b, g, :c], kv.k[b, g].index_select(0, rows))
+                assert torch.equal(o["pv"][b, g, :c], kv.v[b, g].index_select(0, rows))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_fused_equals_separate_calls(dtype, D, G):
+    """Ragged batch: a long context (top-k over several Selector chunks), a
+    medium one, one with fewer candidates than k (keep-all) and one shorter
+    than sinks + window (no candidates)."""
+    Hkv = 2
+    ctx = [9000, 2500, 300, 40]
+    kv, q = random_cache(len(ctx), G * Hkv, Hkv, 9000, D, DT[dtype], ctx, seed=40 + G + D, q_scale=2.0)
+    sp = S.support_params(4, 64, 256, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    ids = [0, 1, 2, 3]
+    a = _separate(kv, sp, ids, q, ws)
+    b = _fused(kv, sp, ids, q, ws)
+    _assert_same(a, b)
+    _check_oracle(kv, sp, q, b, ids)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.1, 1.0])
+def test_fused_uniform_attention_ties(lam):
+    """q = 0 gives every position the same mass, so with lambda = 0 all scores
+    tie and the lowest positions must win; with lambda > 0 the prior decides
+    (both ends of the candidate range)."""
+    T, ns, W, k = 20000, 16, 256, 2048
+    kv, q = random_cache(1, 32, 8, T, 128, torch.bfloat16, [T], seed=5)
+    q.zero_()
+    sp = S.support_params(ns, W, k, lam)
+    ws = S.alloc_workspace(kv, sp)
+    a = _separate(kv, sp, [0], q, ws)
+    b = _fused(kv, sp, [0], q, ws)
+    _assert_same(a, b)
+    n = T - ns - W
+    sel = b["sel"][0].cpu().numpy()
+    if lam == 0.0:
+        assert all(sel[g].tolist() == list(range(ns, ns + k)) for g in range(8))
+    else:
+        pos = (sel - ns + 1)
+        want = list(range(1, k // 2 + 1)) + list(range(n - k // 2 + 1, n + 1))
+        assert all(pos[g].tolist() == want for g in range(8))
+
+
+def test_fused_consecutive_calls_and_subsets():
+    """The Selector's bookkeeping in the workspace is left clean: calls on
+    different row subsets and lengths, one after another on one workspace,
+    each match the separate calls; unlisted rows stay untouched."""
+    ctx = [7000, 12000, 5000]
+    kv, q = random_cache(3, 32, 8, 12000, 128, torch.bfloat16, ctx, seed=9, q_scale=2.0)
+    sp = S.support_params(16, 256, 1024, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    for ids in ([0, 1], [2], [1, 2, 0], [1]):
+        a = _separate(kv, sp, ids, q, ws)
+        b = _fused(kv, sp, ids, q, ws)
+        _assert_same(a, b)
+        for r in set(range(3)) - set(ids):
+            assert torch.all(b["cnt"][r] == -7) and torch.all(b["mass"][r] == -1.0)
+            assert torch.all(b["out"][r] == 7.0)
+    _check_oracle(kv, sp, q, b, [1])
+
+
+@pytest.mark.parametrize("k,packed", [(0, True), (5000, True), (512, False)])
+def test_fused_degenerate_k_and_no_packing(k, packed):
+    """top_k = 0 (nothing selected), top_k above the candidate count (keep
+    all), and the call without packed buffers."""
+    kv, q = random_cache(2, 16, 4, 4000, 64, torch.float32, [4000, 1000], seed=k, q_scale=2.0)
+    sp = S.support_params(8, 32, k, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    a = _separate(kv, sp, [0, 1], q, ws, packed)
+    b = _fused(kv, sp, [0, 1], q, ws, packed)
+    _assert_same(a, b)
+    _check_oracle(kv, sp, q, b, [0, 1])

@@ -88,6 +88,8 @@ def parse():
     p.add_argument("--mode", choices=["graph", "eager"], default="graph")
     p.add_argument("--fast", choices=["packed", "gather"], default="packed",
                    help="fast step over the packed support (default) or gathering rows by index")
+    p.add_argument("--slow", choices=["fused", "separate"], default="fused",
+                   help="slow step + Selector (+ pack) in one call (default) or as separate calls")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -154,8 +156,14 @@ def main():
         pk = torch.empty(L, 1, w.n_kv_heads, w.top_k, w.head_dim, dtype=q_steps.dtype, device=dev)
         pv = torch.empty_like(pk)
 
+    fused = args.slow == "fused"
+
     def slow_layers():
         for l in range(L):
+            if fused:
+                S.sfi_slow_step_select(kvs[l], sp, [0], q_buf[l], out_buf[l], mass, sel[l], cnt[l],
+                                       pk[l] if packed else None, pv[l] if packed else None, ws)
+                continue
             S.sfi_slow_step(kvs[l], [0], q_buf[l], out_buf[l], mass, ws)
             S.sfi_select(kvs[l], sp, [0], mass, sel[l], cnt[l], ws)
             if packed:
@@ -241,7 +249,8 @@ def main():
     alg = {
         "slow_partial": 2 * w.n_kv_heads * T * kv_row + q_bytes,
         "slow_combine": 4 * w.n_kv_heads * T + 4 * w.n_q_heads * w.head_dim,
-        "select": 4 * w.n_kv_heads * n_cand + 4 * w.n_kv_heads * w.top_k,
+        "select": 4 * w.n_kv_heads * n_cand + 4 * w.n_kv_heads * w.top_k
+                  + (2 * 2 * w.n_kv_heads * kk * kv_row if fused and packed else 0),
         "pack": 2 * 2 * w.n_kv_heads * kk * kv_row + 4 * w.n_kv_heads * w.top_k,
         "fast_partial": 2 * w.n_kv_heads * supp * kv_row + q_bytes + (0 if packed else 4 * w.n_kv_heads * w.top_k),
         "fast_merge": 4 * w.n_q_heads * w.head_dim,
@@ -284,6 +293,7 @@ def main():
                                f"top-k {w.top_k}, lambda {w.lam}, geometric spans mean {w.span_param}; "
                                f"{L} independent layer caches per decode step",
                    "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode, "fast_path": args.fast,
+                   "slow_path": args.slow,
                    "slow_steps_timed": n_slow_timed},
         "slow_steps_per_s_layer": 1e6 / slow_us if slow_us else None,
         "fast_steps_per_s_layer": 1e6 / fast_us if fast_us else None,

@@ -98,12 +98,10 @@ typedef struct {
  * for SFI_OP_SLOW.  Returns 0 and sets sfi_last_error() on invalid input. */
 size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp, int32_t op);
 
-/* Prepares a freshly allocated workspace (device, ws_bytes) for use: clears
- * the bookkeeping the Selector keeps at its start (a per-head histogram and a
- * list counter).  Call once after allocation, before the first sfi_select
- * or sfi_slow_step_select;
- * the Selector's kernels leave that bookkeeping cleared when they finish.
- * Workspaces must not be shared by calls that may run concurrently. */
+/* Zero-fills a workspace (device, ws_bytes).  Optional: every call prepares
+ * the parts of the workspace it uses (the Selector's per-head histogram and
+ * list counter are cleared by the first kernel of each call that builds
+ * them).  Workspaces must not be shared by calls that may run concurrently. */
 int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Slow step (dense decode attention over the whole history).
@@ -130,8 +128,7 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int3
  *   sel_idx : device int32 [B][Hkv][top_k]; the kept positions in ascending
  *             order, then -1 up to top_k
  *   sel_cnt : device int32 [B][Hkv]; min(top_k, n) (0 when T <= n_sink + n_recent)
- *   ws      : at least sfi_workspace_bytes(desc, sp, SFI_OP_SELECT) bytes,
- *             prepared once by sfi_workspace_init. */
+ *   ws      : at least sfi_workspace_bytes(desc, sp, SFI_OP_SELECT) bytes. */
 int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp,
                    const int32_t* seq_ids_host, int32_t n_seq, const float* mass,
                    int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes, void* stream);
@@ -185,7 +182,7 @@ int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* 
  *   sel_idx, sel_cnt : as for sfi_select
  *   packed_k/_v      : as for sfi_pack_support, or both NULL to skip packing
  *   ws               : at least sfi_workspace_bytes(desc, sp, SFI_OP_SLOW_SELECT)
- *                      bytes, prepared once by sfi_workspace_init. */
+ *                      bytes. */
 int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* sp,
                              const int32_t* seq_ids_host, int32_t n_seq, const void* q, float* out,
                              float* mass, int32_t* sel_idx, int32_t* sel_cnt, void* packed_k,

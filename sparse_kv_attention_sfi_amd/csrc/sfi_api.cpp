@@ -118,10 +118,10 @@ float logit_scale(const sfi_kv_desc* d) {
 }
 
 // ---- workspace layout -----------------------------------------------------
-// [ persistent header | op scratch ].  The header holds the Selector's
-// bookkeeping (top-digit histogram, list counter), which its kernels leave
-// cleared when they finish; it sits at a fixed offset so slow, select and fast
-// calls may share one workspace.
+// [ header | op scratch ].  The header holds the Selector's per-head
+// bookkeeping (top-digit histogram, list counter), cleared by the first kernel
+// of every call that builds a histogram; it sits at a fixed offset so slow,
+// select and fast calls may share one workspace.
 struct Header {
   size_t sel_hist, sel_list_n, end;
 };
@@ -136,16 +136,15 @@ Header header_layout(const sfi_kv_desc* d) {
 size_t header_bytes(const sfi_kv_desc* d) { return header_layout(d).end; }
 
 struct SelectLayout {
-  size_t list, chunk_above, chunk_off, kstar, end;
+  size_t list, chunk_above, head_info, end;
 };
 SelectLayout select_layout(const sfi_kv_desc* d) {
   const size_t bh = static_cast<size_t>(d->batch) * d->n_kv_heads;
   SelectLayout L;
   L.list = header_bytes(d);
   L.chunk_above = L.list + align_up(bh * kSelListCap * sizeof(uint64_t));
-  L.chunk_off = L.chunk_above + align_up(bh * kSelMaxChunks * sizeof(int32_t));
-  L.kstar = L.chunk_off + align_up(bh * kSelMaxChunks * sizeof(int32_t));
-  L.end = L.kstar + align_up(bh * sizeof(uint64_t));
+  L.head_info = L.chunk_above + align_up(bh * kSelMaxChunks * sizeof(int32_t));
+  L.end = L.head_info + align_up(bh * 2 * sizeof(int32_t));
   return L;
 }
 
@@ -350,8 +349,7 @@ void plan_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const in
   a.list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
   a.list = reinterpret_cast<uint64_t*>(w + L.list);
   a.chunk_above = reinterpret_cast<int32_t*>(w + L.chunk_above);
-  a.chunk_off = reinterpret_cast<int32_t*>(w + L.chunk_off);
-  a.kstar = reinterpret_cast<uint64_t*>(w + L.kstar);
+  a.head_info = reinterpret_cast<int32_t*>(w + L.head_info);
   a.t_cap = desc->kv_capacity;
   a.n_kv_heads = desc->n_kv_heads;
   a.n_sink = sp->n_sink;
@@ -499,6 +497,8 @@ int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* 
     SlowArgs a{};
     CombineArgs c{};
     plan_slow(desc, ids, cnt, q, out, mass, w, a, c);
+    a.clear_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
+    a.clear_list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
     c.sel_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
     c.n_sink = sp->n_sink;
     c.n_recent = sp->n_recent;

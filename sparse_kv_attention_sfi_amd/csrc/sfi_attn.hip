@@ -399,6 +399,13 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   const int T = a.tab.ctx[e];
   const int r_begin = split * a.split_rows;
   const int r_end = min(T, r_begin + a.split_rows);
+  if (a.clear_hist != nullptr && split == 0) {
+    // fresh Selector bookkeeping for the histogram the combine builds next
+    const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+    uint4* h4 = reinterpret_cast<uint4*>(a.clear_hist + bg * kSelBins);
+    for (int i = threadIdx.x; i < kSelBins / 4; i += kSlowThreads) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x == 0) a.clear_list_n[bg] = 0;
+  }
 
   const int64_t kv_row0 = (static_cast<int64_t>(b) * a.n_kv_heads + g) * a.t_cap;
   const char* Kb = static_cast<const char*>(a.k) + kv_row0 * RB;

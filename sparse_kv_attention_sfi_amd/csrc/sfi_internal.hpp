@@ -52,6 +52,9 @@ struct SlowArgs {
   int32_t part_stride;  // max splits per head (workspace pitch)
   float scale_log2;     // logit scale times log2(e)
   int64_t logit_pitch;  // floats per logit row (multiple of 64)
+  // optional: Selector bookkeeping the first split of each head clears
+  uint32_t* clear_hist;    // [B * Hkv][4096] or nullptr
+  int32_t* clear_list_n;   // [B * Hkv]
   SeqTable tab;
 };
 
@@ -81,14 +84,13 @@ struct SelectArgs {
   const float* mass;
   int32_t* sel_idx;
   int32_t* sel_cnt;
-  // persistent bookkeeping (zero between calls)
+  // per-head bookkeeping, zero at the start of every call
   uint32_t* hist;        // [B * Hkv][4096] top-digit histogram
   int32_t* list_n;       // [B * Hkv] keys appended to the threshold-bin list
   // per-call scratch
-  uint64_t* list;        // [B * Hkv][kSelListCap]
-  int32_t* chunk_above;  // [B * Hkv][kSelMaxChunks]
-  int32_t* chunk_off;    // [B * Hkv][kSelMaxChunks]
-  uint64_t* kstar;       // [B * Hkv]
+  uint64_t* list;        // [B * Hkv][kSelListCap] keys of the threshold bin
+  int32_t* chunk_above;  // [B * Hkv][kSelMaxChunks] keys above the bin per chunk
+  int32_t* head_info;    // [B * Hkv][2] threshold bin, keys above it
   int64_t t_cap;
   int32_t n_kv_heads;
   int32_t n_sink;

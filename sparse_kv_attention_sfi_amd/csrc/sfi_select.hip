@@ -13,22 +13,22 @@
 //
 // The candidates of a head are cut into chunks handled by separate
 // workgroups, so the selection of one head spreads over many CUs:
-//   1. select_hist:   histogram of the top 12 key bits, added into a
-//                     per-head global histogram.
+//   0. the head's histogram and list counter start at zero (cleared by
+//      select_clear, or by the slow step's partial kernel in the fused call)
+//   1. histogram of the top 12 key bits, added into a per-head global
+//      histogram (select_hist, or the slow step's combine in the fused call).
 //   2. select_gather: every workgroup finds the bin d1 holding K*, counts its
-//                     keys above d1 and appends its keys in d1 to a per-head
-//                     list (one atomic per workgroup reserves its range).
-//   3. select_finish: one workgroup per head resolves K* inside the list in
-//                     LDS (by direct ranking when the list is short, else 12
-//                     bits per level), derives how many keys each
-//                     chunk keeps, turns that into output offsets, and clears
-//                     the head's histogram and list counter.  If d1 holds more
-//                     keys than fit in LDS, it resolves K* by radix passes
-//                     over all candidates instead.
-//   4. select_emit:   every workgroup writes the kept positions of its chunk
-//                     in ascending order at its offset.
-// Workgroups never hand data to each other inside a kernel: on gfx950 a
-// device-scope fence writes back and invalidates the XCD's L2.
+//      keys above d1 and appends its keys in d1 to a per-head list (one
+//      atomic per workgroup reserves its range).
+//   3. select_emit: every workgroup resolves K* inside the list in LDS (by
+//      direct ranking when the list is short, else 12 bits per level), derives
+//      how many kept keys precede its chunk, and writes the kept positions of
+//      its chunk in ascending order from there.  If d1 holds more keys than
+//      fit in LDS, K* comes from radix passes over all candidates instead.
+// Resolving K* redundantly in every emitting workgroup costs less than a
+// kernel boundary.  Workgroups never hand data to each other inside a
+// kernel: on gfx950 a device-scope fence writes back and invalidates the
+// XCD's L2.
 #include <math.h>
 
 #include "sfi_device.hpp"
@@ -154,6 +154,18 @@ __device__ uint64_t radix_resolve(Src src, int count, uint64_t prefix, uint64_t 
 }
 
 // ---------------------------------------------------------------------------
+// 0. clear the per-head bookkeeping (one workgroup per listed head)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void select_clear_kernel(SelectArgs a) {
+  const int e = blockIdx.x / a.n_kv_heads;
+  const int g = blockIdx.x - e * a.n_kv_heads;
+  const int64_t bg = static_cast<int64_t>(a.tab.seq[e]) * a.n_kv_heads + g;
+  uint4* h4 = reinterpret_cast<uint4*>(a.hist + bg * kSelBins);
+  for (int i = threadIdx.x; i < kSelBins / 4; i += 256) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) a.list_n[bg] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // 1. histogram of the top digit
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a) {
@@ -167,8 +179,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a) 
   __syncthreads();
   const ScoreParams sp = score_params(a, h, s_inv2h);
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
-  for (int i = i0 + tid; i < i1; i += kSelThreads)
-    atomicAdd(&s_hist[cand_key(sp, i) >> (64 - kSelDigitBits)], 1u);
+  for (int i = i0 + tid; i < i1; i += kSelThreads) atomicAdd(&s_hist[top_digit(cand_key(sp, i))], 1u);
   __syncthreads();
   uint32_t* gh = a.hist + h.bg * kSelBins;
   for (int i = tid; i < kSelBins; i += kSelThreads)
@@ -178,8 +189,11 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a) 
 // ---------------------------------------------------------------------------
 // 2. collect the keys of the threshold bin
 // ---------------------------------------------------------------------------
+constexpr int kRun = 8;                         // candidates per thread and pass
+constexpr int kGatherStep = kRun * kSelThreads;  // candidates per pass
+
 __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a) {
-  __shared__ uint32_t s_hist[kSelBins];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSelBins];
   __shared__ int s_wave[kSelWaves];
   __shared__ int s_res[2];
   __shared__ int s_base;
@@ -187,163 +201,80 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
   const HeadCtx h = head_ctx(a);
   if (h.keep_all) return;
   const int tid = threadIdx.x;
+  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  // each thread owns a contiguous run of kRun candidates per pass, so its
+  // keys in d1 are written without per-key atomics; the first pass's evidence
+  // is loaded before the histogram so both share a round trip
+  const float* frow = a.mass + h.bg * a.t_cap + a.n_sink;
+  float fv[kRun];
+#pragma unroll
+  for (int u = 0; u < kRun; ++u) {
+    const int i = i0 + tid * kRun + u;
+    fv[u] = i < i1 ? frow[i] : 0.f;
+  }
   if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
   const uint32_t* gh = a.hist + h.bg * kSelBins;
-  for (int i = tid; i < kSelBins; i += kSelThreads) s_hist[i] = gh[i];
+  for (int i = tid; i < kSelBins / 4; i += kSelThreads)
+    reinterpret_cast<uint4*>(s_hist)[i] = reinterpret_cast<const uint4*>(gh)[i];
   __syncthreads();
   find_digit(s_hist, kSelBins, a.top_k, s_wave, s_res);
   const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
+  if (h.c == 0 && tid == 0) {
+    a.head_info[2 * h.bg] = s_res[0];
+    a.head_info[2 * h.bg + 1] = s_res[1];
+  }
   const ScoreParams sp = score_params(a, h, s_inv2h);
-
-  // each thread handles a contiguous run of the chunk so that its keys in d1
-  // can be written without per-key atomics
-  constexpr int kRun = 8;
-  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
-  int gt = 0, eq = 0;
-  for (int t0 = i0; t0 < i1; t0 += kRun * kSelThreads) {
-    const int j0 = t0 + tid;
+  uint64_t* glist = a.list + h.bg * kSelListCap;
+  int gt_all = 0;
+  for (int t0 = i0; t0 < i1; t0 += kGatherStep) {
+    if (t0 != i0) {
 #pragma unroll
-    for (int u = 0; u < kRun; ++u) {
-      const int i = j0 + u * kSelThreads;
-      if (i < i1) {
-        const uint32_t dig = static_cast<uint32_t>(cand_key(sp, i) >> (64 - kSelDigitBits));
-        gt += dig > d1;
-        eq += dig == d1;
+      for (int u = 0; u < kRun; ++u) {
+        const int i = t0 + tid * kRun + u;
+        fv[u] = i < i1 ? frow[i] : 0.f;
       }
     }
-  }
-  int gt_total, eq_total;
-  (void)block_excl_scan(gt, s_wave, &gt_total);
-  const int my = block_excl_scan(eq, s_wave, &eq_total);
-  if (tid == 0) {
-    a.chunk_above[h.bg * kSelMaxChunks + h.c] = gt_total;
-    s_base = eq_total > 0 ? atomicAdd(a.list_n + h.bg, eq_total) : 0;
-  }
-  __syncthreads();
-  if (eq == 0) return;
-  uint64_t* glist = a.list + h.bg * kSelListCap;
-  int slot = s_base + my;
-  for (int t0 = i0; t0 < i1; t0 += kRun * kSelThreads) {
-    const int j0 = t0 + tid;
+    uint64_t key[kRun];
+    int gt = 0, eq = 0;
 #pragma unroll
     for (int u = 0; u < kRun; ++u) {
-      const int i = j0 + u * kSelThreads;
-      if (i < i1) {
-        const uint64_t key = cand_key(sp, i);
-        if (static_cast<uint32_t>(key >> (64 - kSelDigitBits)) == d1) {
-          if (slot < kSelListCap) glist[slot] = key;
-          ++slot;
+      const int i = t0 + tid * kRun + u;
+      key[u] = key_of(sp, i, fv[u]);
+      const uint32_t dig = top_digit(key[u]);
+      const bool in = i < i1;
+      gt += in && dig > d1;
+      eq += in && dig == d1;
+    }
+    // one scan of both counts: (gt << 16) | eq, totals below 2^16 per pass
+    int tot;
+    const int pre = block_excl_scan((gt << 16) | eq, s_wave, &tot);
+    gt_all += tot >> 16;
+    const int eq_tot = tot & 0xffff;
+    if (eq_tot > 0) {
+      if (tid == 0) s_base = atomicAdd(a.list_n + h.bg, eq_tot);
+      __syncthreads();
+      if (eq > 0) {
+        int slot = s_base + (pre & 0xffff);
+#pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+          const int i = t0 + tid * kRun + u;
+          if (i < i1 && top_digit(key[u]) == d1) {
+            if (slot < kSelListCap) glist[slot] = key[u];
+            ++slot;
+          }
         }
       }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 3. resolve K*, per-chunk output offsets; clear the head's bookkeeping
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelThreads) void select_finish_kernel(SelectArgs a) {
-  __shared__ uint64_t s_kstar;
-  __shared__ uint32_t s_hist[kSelBins];
-  __shared__ uint64_t s_list[kSelListCap];
-  __shared__ int s_cnt[kSelMaxChunks];
-  __shared__ int s_wave[kSelWaves];
-  __shared__ int s_res[2];
-  __shared__ float s_inv2h;
-  HeadCtx h;
-  {
-    const int e = blockIdx.x / a.n_kv_heads;
-    h.e = e;
-    h.g = blockIdx.x - e * a.n_kv_heads;
-    h.c = 0;
-    h.M = a.tab.nsplit[e];
-    h.b = a.tab.seq[e];
-    h.T = a.tab.ctx[e];
-    h.bg = static_cast<int64_t>(h.b) * a.n_kv_heads + h.g;
-    h.n = max(0, h.T - a.n_recent - a.n_sink);
-    h.keep_all = h.n <= a.top_k || a.top_k == 0;
-  }
-  if (h.keep_all) return;
-  const int tid = threadIdx.x;
-  const int K = a.top_k;
-  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
-  uint32_t* gh = a.hist + h.bg * kSelBins;
-  for (int i = tid; i < kSelBins; i += kSelThreads) s_hist[i] = gh[i];
-  __syncthreads();
-  find_digit(s_hist, kSelBins, K, s_wave, s_res);
-  const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
-  const int above = s_res[1];
-  const int cnt_d1 = static_cast<int>(s_hist[d1]);
-  const int need = K - above;
-  const ScoreParams sp = score_params(a, h, s_inv2h);
-  const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
-  const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
-  for (int c = tid; c < kSelMaxChunks; c += kSelThreads) s_cnt[c] = 0;
-  uint64_t kstar;
-  if (cnt_d1 <= kSelListCap) {
-    const uint64_t* glist = a.list + h.bg * kSelListCap;
-    for (int i = tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
-    __syncthreads();
-    if (cnt_d1 <= kSelThreads) {
-      // few keys: K* is the key with exactly need - 1 larger keys (all distinct)
-      if (tid < cnt_d1) {
-        const uint64_t mine = s_list[tid];
-        int rank = 0;
-        for (int j = 0; j < cnt_d1; ++j) rank += s_list[j] > mine;
-        if (rank == need - 1) s_kstar = mine;
-      }
       __syncthreads();
-      kstar = s_kstar;
-    } else {
-      kstar = radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
-                            s_hist, s_wave, s_res);
-    }
-    for (int i = tid; i < cnt_d1; i += kSelThreads) {
-      const uint64_t key = s_list[i];
-      if (key >= kstar) atomicAdd(&s_cnt[(key_position(key) - a.n_sink) / a.chunk], 1);
-    }
-    __syncthreads();
-    for (int c = tid; c < h.M; c += kSelThreads) s_cnt[c] += a.chunk_above[h.bg * kSelMaxChunks + c];
-  } else {
-    // the threshold bin does not fit in LDS: radix passes over all candidates
-    kstar = radix_resolve([&](int i) { return cand_key(sp, i); }, h.n, pfx, pmask, 64 - kSelDigitBits, need,
-                          s_hist, s_wave, s_res);
-    for (int i = tid; i < h.n; i += kSelThreads)
-      if (cand_key(sp, i) >= kstar) atomicAdd(&s_cnt[i / a.chunk], 1);
-  }
-  __syncthreads();
-  // exclusive scan of the per-chunk counts -> output offsets
-  {
-    constexpr int PER = kSelMaxChunks / kSelThreads;
-    int v[PER], loc = 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid * PER + u;
-      v[u] = c < h.M ? s_cnt[c] : 0;
-      loc += v[u];
-    }
-    int tot;
-    int run = block_excl_scan(loc, s_wave, &tot);
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid * PER + u;
-      if (c < h.M) a.chunk_off[h.bg * kSelMaxChunks + c] = run;
-      run += v[u];
     }
   }
-  if (tid == 0) {
-    a.kstar[h.bg] = kstar;
-    a.sel_cnt[h.bg] = K;
-    a.list_n[h.bg] = 0;
-  }
-  for (int i = tid; i < kSelBins; i += kSelThreads) gh[i] = 0u;
+  if (tid == 0) a.chunk_above[h.bg * kSelMaxChunks + h.c] = gt_all;
 }
 
 // ---------------------------------------------------------------------------
-// 4. ordered emission
+// 3. resolve K* and emit in order
 // ---------------------------------------------------------------------------
 // Copies rows pos[r] of the cache into slots base + r of the packed buffers
-// for r < count; kernel-wide cooperative 16-byte copies.
+// for r < count; workgroup-wide cooperative 16-byte copies.
 __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const int* s_pos, int base, int count) {
   const int np = a.row_bytes >> 4;  // 16-byte pieces per row
   const int items = count * np;
@@ -382,10 +313,14 @@ __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const
 // packed buffers at the same slots, so the fast step reads them contiguously.
 template <bool PACK>
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
-  constexpr int kStep = 4 * kSelThreads;  // candidates per pass
-  __shared__ int s_wave[kSelWaves];
-  __shared__ float s_inv2h;
+  constexpr int kStep = 4 * kSelThreads;  // candidates per emission pass
+  __shared__ uint64_t s_list[kSelListCap];
+  __shared__ uint32_t s_hist[kSelBins];
   __shared__ int s_pos[PACK ? kStep : 1];
+  __shared__ int s_wave[kSelWaves];
+  __shared__ int s_res[2];
+  __shared__ uint64_t s_kstar;
+  __shared__ float s_inv2h;
   const HeadCtx h = head_ctx(a);
   const int tid = threadIdx.x;
   const int K = a.top_k;
@@ -406,12 +341,53 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     }
     return;
   }
+  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  const int d1 = a.head_info[2 * h.bg];
+  const int above = a.head_info[2 * h.bg + 1];
+  const int cnt_d1 = a.list_n[h.bg];
+  const int need = K - above;  // rank of K* inside bin d1 (1-based)
   if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
+  const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
+  const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
+  uint64_t kstar;
+  int before = 0;  // kept keys of the chunks before this one (this thread's share)
+  if (cnt_d1 <= kSelListCap) {
+    const uint64_t* glist = a.list + h.bg * kSelListCap;
+    for (int i = tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
+    for (int c = tid; c < h.c; c += kSelThreads) before += a.chunk_above[h.bg * kSelMaxChunks + c];
+    __syncthreads();
+    if (cnt_d1 <= kSelThreads) {
+      // few keys: K* is the key with exactly need - 1 larger keys (all distinct)
+      if (tid < cnt_d1) {
+        const uint64_t mine = s_list[tid];
+        int rank = 0;
+        for (int j = 0; j < cnt_d1; ++j) rank += s_list[j] > mine;
+        if (rank == need - 1) s_kstar = mine;
+      }
+      __syncthreads();
+      kstar = s_kstar;
+    } else {
+      kstar = radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
+                            s_hist, s_wave, s_res);
+    }
+    const int lo = a.n_sink + i0;  // first position of this chunk
+    for (int i = tid; i < cnt_d1; i += kSelThreads) {
+      const uint64_t key = s_list[i];
+      before += key >= kstar && key_position(key) < lo;
+    }
+  } else {
+    // the threshold bin does not fit in LDS: radix passes over all candidates
+    __syncthreads();
+    const ScoreParams sp = score_params(a, h, s_inv2h);
+    kstar = radix_resolve([&](int i) { return cand_key(sp, i); }, h.n, pfx, pmask, 64 - kSelDigitBits, need,
+                          s_hist, s_wave, s_res);
+    for (int i = tid; i < i0; i += kSelThreads) before += cand_key(sp, i) >= kstar;
+  }
+  int base;
+  (void)block_excl_scan(before, s_wave, &base);
+  if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = K;
   __syncthreads();
   const ScoreParams sp = score_params(a, h, s_inv2h);
-  const uint64_t kstar = a.kstar[h.bg];
-  int base = a.chunk_off[h.bg * kSelMaxChunks + h.c];
-  const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
   for (int t0 = i0; t0 < i1; t0 += kStep) {
     const int j0 = t0 + 4 * tid;
     int flags = 0, c = 0;
@@ -446,14 +422,14 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s) {
   hipError_t e;
   if (!a.hist_ready) {
+    launch(select_clear_kernel, a.tab.n * a.n_kv_heads, 256, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     launch(select_hist_kernel, grid, kSelThreads, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   launch(select_gather_kernel, grid, kSelThreads, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  launch(select_finish_kernel, a.tab.n * a.n_kv_heads, kSelThreads, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.packed_k != nullptr)

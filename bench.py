@@ -51,7 +51,7 @@ def csrc_digest():
 
 
 def kernel_group(name):
-    """Bench kernel name of a device kernel (the Selector's four kernels form one group)."""
+    """Bench kernel name of a device kernel (the Selector's kernels form one group)."""
     for key, group in (("slow_partial", "slow_partial"), ("slow_combine", "slow_combine"), ("select_", "select"),
                        ("pack_kernel", "pack"), ("fast_packed", "fast_partial"), ("fast_partial", "fast_partial"),
                        ("fast_merge", "fast_merge")):

@@ -469,21 +469,31 @@ constexpr int kMaxSlots = kMaxMergeSlots;
 
 // Global max M_h and 1 / L_h of NH heads over n slots; ml of head h is at
 // ml + h * ml_hstride as (m, l) pairs.  Ends with a barrier.
+// Global max M_h and 1 / L_h of NH heads from n <= kMaxSlots (max, sum)
+// partial pairs (one wave per head); every pair is read once, in a single
+// round trip.
 template <int NH, int NW>
 __device__ __forceinline__ void head_max_sum(const float* ml, int64_t ml_hstride, int n, float* sM,
                                              float* sInvL) {
+  constexpr int kPer = kMaxSlots / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int h = wave; h < NH; h += NW) {
     const float* p = ml + h * ml_hstride;
+    float2 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int s = lane + 64 * u;
+      v[u] = s < n ? *reinterpret_cast<const float2*>(p + 2 * s) : make_float2(-INFINITY, 0.f);
+    }
     float m = -INFINITY;
-    for (int s = lane; s < n; s += 64) m = fmaxf(m, p[2 * s]);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) m = fmaxf(m, v[u].x);
     m = wave_max(m);
     float l = 0.f;
     if (m != -INFINITY) {
-      for (int s = lane; s < n; s += 64) {
-        const float ms = p[2 * s];
-        if (ms != -INFINITY) l += p[2 * s + 1] * fast_exp2(ms - m);
-      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (v[u].x != -INFINITY) l += v[u].y * fast_exp2(v[u].x - m);
     }
     l = wave_sum(l);
     if (lane == 0) {

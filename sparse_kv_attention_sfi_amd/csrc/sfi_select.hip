@@ -125,13 +125,51 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int 
   __syncthreads();
 }
 
-// Resolves the remaining digits of K* (below `shift`) among keys that match
-// `prefix` on `pmask`.  Keys come from `src(i)` for i < count.
+// Among `m` distinct keys in LDS (16-byte aligned), the one with exactly
+// need - 1 larger keys.  Every thread ranks one key; the comparisons read the
+// list eight keys at a time (broadcast 16-byte LDS reads).
+__device__ __forceinline__ uint64_t rank_select(const uint64_t* keys, int m, int need, uint64_t* s_out) {
+  const int tid = threadIdx.x;
+  if (tid < m) {
+    const uint64_t mine = keys[tid];
+    int rank = 0;
+    const int m8 = m & ~7;
+    for (int j = 0; j < m8; j += 8) {
+      const ulonglong2* p = reinterpret_cast<const ulonglong2*>(keys + j);
+      const ulonglong2 a = p[0], b = p[1], c = p[2], d = p[3];
+      rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine) + (c.x > mine) + (c.y > mine) +
+              (d.x > mine) + (d.y > mine);
+    }
+    for (int j = m8; j < m; ++j) rank += keys[j] > mine;
+    if (rank == need - 1) *s_out = mine;
+  }
+  __syncthreads();
+  return *s_out;
+}
+
+// Resolves the remaining digits of K* (below `shift`) among the `match` keys
+// that equal `prefix` on `pmask`; keys come from `src(i)` for i < count.  Each
+// level histograms the next (up to) 12 bits; as soon as at most kSelThreads
+// keys share the resolved prefix they are gathered into LDS and ranked.
+// s_hist must be 16-byte aligned (its first 4 KiB also hold the gathered keys).
 template <typename Src>
-__device__ uint64_t radix_resolve(Src src, int count, uint64_t prefix, uint64_t pmask, int shift, int need,
-                                  uint32_t* s_hist, int* s_wave, int* s_res) {
+__device__ uint64_t radix_resolve(Src src, int count, int match, uint64_t prefix, uint64_t pmask, int shift,
+                                  int need, uint32_t* s_hist, int* s_wave, int* s_res, uint64_t* s_key) {
   const int tid = threadIdx.x;
   while (shift > 0) {
+    if (match <= kSelThreads) {
+      uint64_t* small = reinterpret_cast<uint64_t*>(s_hist);
+      if (tid == 0) s_res[0] = 0;
+      __syncthreads();
+      for (int i = tid; i < count; i += kSelThreads) {
+        const uint64_t key = src(i);
+        if ((key & pmask) == prefix) small[atomicAdd(&s_res[0], 1)] = key;
+      }
+      __syncthreads();
+      const uint64_t k = rank_select(small, match, need, s_key);
+      __syncthreads();
+      return k;
+    }
     const int width = shift >= kSelDigitBits ? kSelDigitBits : shift;
     shift -= width;
     const uint32_t dmask = (1u << width) - 1u;
@@ -146,6 +184,7 @@ __device__ uint64_t radix_resolve(Src src, int count, uint64_t prefix, uint64_t 
     find_digit(s_hist, nbins, need, s_wave, s_res);
     const int digit = s_res[0];
     need -= s_res[1];
+    match = static_cast<int>(s_hist[digit]);
     prefix |= static_cast<uint64_t>(digit) << shift;
     pmask |= static_cast<uint64_t>(dmask) << shift;
     __syncthreads();
@@ -311,16 +350,17 @@ __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const
 // Writes the kept positions of the workgroup's chunk in ascending order at the
 // chunk's output offset.  With PACK it also copies their K and V rows into the
 // packed buffers at the same slots, so the fast step reads them contiguously.
+// The chunk's evidence, the head's bookkeeping and the head of the threshold
+// bin's list are all requested in the first round trip.
 template <bool PACK>
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
-  constexpr int kStep = 4 * kSelThreads;  // candidates per emission pass
-  __shared__ uint64_t s_list[kSelListCap];
-  __shared__ uint32_t s_hist[kSelBins];
+  constexpr int kStep = kGatherStep;  // candidates per emission pass (kRun per thread)
+  __shared__ __attribute__((aligned(16))) uint64_t s_list[kSelListCap];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSelBins];
   __shared__ int s_pos[PACK ? kStep : 1];
   __shared__ int s_wave[kSelWaves];
   __shared__ int s_res[2];
   __shared__ uint64_t s_kstar;
-  __shared__ float s_inv2h;
   const HeadCtx h = head_ctx(a);
   const int tid = threadIdx.x;
   const int K = a.top_k;
@@ -342,34 +382,38 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     return;
   }
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  const float* frow = a.mass + h.bg * a.t_cap + a.n_sink;
+  float fv[kRun];
+#pragma unroll
+  for (int u = 0; u < kRun; ++u) {
+    const int i = i0 + tid * kRun + u;
+    fv[u] = i < i1 ? frow[i] : 0.f;
+  }
   const int d1 = a.head_info[2 * h.bg];
   const int above = a.head_info[2 * h.bg + 1];
   const int cnt_d1 = a.list_n[h.bg];
+  const uint64_t* glist = a.list + h.bg * kSelListCap;
+  const uint64_t first = glist[tid];  // always inside the list; used if tid < cnt_d1
+  int before = 0;  // kept keys of the chunks before this one (this thread's share)
+  for (int c = tid; c < h.c; c += kSelThreads) before += a.chunk_above[h.bg * kSelMaxChunks + c];
+  const float inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
+  const ScoreParams sp = score_params(a, h, inv2h);
+  // keys of the first pass, computed while the list is still on its way
+  uint64_t key[kRun];
+#pragma unroll
+  for (int u = 0; u < kRun; ++u) key[u] = key_of(sp, i0 + tid * kRun + u, fv[u]);
+  s_list[tid] = first;
   const int need = K - above;  // rank of K* inside bin d1 (1-based)
-  if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
   const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
   const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
   uint64_t kstar;
-  int before = 0;  // kept keys of the chunks before this one (this thread's share)
   if (cnt_d1 <= kSelListCap) {
-    const uint64_t* glist = a.list + h.bg * kSelListCap;
-    for (int i = tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
-    for (int c = tid; c < h.c; c += kSelThreads) before += a.chunk_above[h.bg * kSelMaxChunks + c];
+    for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
     __syncthreads();
-    if (cnt_d1 <= kSelThreads) {
-      // few keys: K* is the key with exactly need - 1 larger keys (all distinct)
-      if (tid < cnt_d1) {
-        const uint64_t mine = s_list[tid];
-        int rank = 0;
-        for (int j = 0; j < cnt_d1; ++j) rank += s_list[j] > mine;
-        if (rank == need - 1) s_kstar = mine;
-      }
-      __syncthreads();
-      kstar = s_kstar;
-    } else {
-      kstar = radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
-                            s_hist, s_wave, s_res);
-    }
+    kstar = cnt_d1 <= kSelThreads
+                ? rank_select(s_list, cnt_d1, need, &s_kstar)
+                : radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, cnt_d1, pfx, pmask, 64 - kSelDigitBits,
+                                need, s_hist, s_wave, s_res, &s_kstar);
     const int lo = a.n_sink + i0;  // first position of this chunk
     for (int i = tid; i < cnt_d1; i += kSelThreads) {
       const uint64_t key = s_list[i];
@@ -378,23 +422,26 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   } else {
     // the threshold bin does not fit in LDS: radix passes over all candidates
     __syncthreads();
-    const ScoreParams sp = score_params(a, h, s_inv2h);
-    kstar = radix_resolve([&](int i) { return cand_key(sp, i); }, h.n, pfx, pmask, 64 - kSelDigitBits, need,
-                          s_hist, s_wave, s_res);
+    kstar = radix_resolve([&](int i) { return cand_key(sp, i); }, h.n, cnt_d1, pfx, pmask, 64 - kSelDigitBits,
+                          need, s_hist, s_wave, s_res, &s_kstar);
     for (int i = tid; i < i0; i += kSelThreads) before += cand_key(sp, i) >= kstar;
   }
   int base;
   (void)block_excl_scan(before, s_wave, &base);
   if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = K;
-  __syncthreads();
-  const ScoreParams sp = score_params(a, h, s_inv2h);
   for (int t0 = i0; t0 < i1; t0 += kStep) {
-    const int j0 = t0 + 4 * tid;
+    if (t0 != i0) {
+#pragma unroll
+      for (int u = 0; u < kRun; ++u) {
+        const int i = t0 + tid * kRun + u;
+        key[u] = key_of(sp, i, i < i1 ? frow[i] : 0.f);
+      }
+    }
     int flags = 0, c = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = j0 + u;
-      if (i < i1 && cand_key(sp, i) >= kstar) {
+    for (int u = 0; u < kRun; ++u) {
+      const int i = t0 + tid * kRun + u;
+      if (i < i1 && key[u] >= kstar) {
         flags |= 1 << u;
         ++c;
       }
@@ -403,10 +450,11 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     const int mine = block_excl_scan(c, s_wave, &total);  // ends with a barrier
     int pos = base + mine;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRun; ++u) {
       if ((flags & (1 << u)) && pos < K) {
-        out[pos] = a.n_sink + j0 + u;
-        if (PACK) s_pos[pos - base] = a.n_sink + j0 + u;
+        const int j = a.n_sink + t0 + tid * kRun + u;
+        out[pos] = j;
+        if (PACK) s_pos[pos - base] = j;
         ++pos;
       }
     }

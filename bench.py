@@ -244,16 +244,22 @@ def main():
     kk = min(w.top_k, n_cand)
     supp = min(w.n_sink, T) + min(w.n_recent, T) + kk
     kv_row = w.head_dim * esz
+    nsplit = S.sfi_slow_plan(kvs[0], [0])[0]
+    nchunk = S.sfi_fast_plan(kvs[0], sp, [0])[0]
     q_bytes = w.n_q_heads * w.head_dim * esz
     # algorithmic bytes per launch (what the method has to move)
     alg = {
         "slow_partial": 2 * w.n_kv_heads * T * kv_row + q_bytes,
-        "slow_combine": 4 * w.n_kv_heads * T + 4 * w.n_q_heads * w.head_dim,
+        # the combine reads the partial kernel's logits and split partials and
+        # writes the mass and the output
+        "slow_combine": 4 * w.n_q_heads * T + 4 * w.n_q_heads * nsplit * (w.head_dim + 2)
+                        + 4 * w.n_kv_heads * T + 4 * w.n_q_heads * w.head_dim,
         "select": 4 * w.n_kv_heads * n_cand + 4 * w.n_kv_heads * w.top_k
                   + (2 * 2 * w.n_kv_heads * kk * kv_row if fused and packed else 0),
         "pack": 2 * 2 * w.n_kv_heads * kk * kv_row + 4 * w.n_kv_heads * w.top_k,
         "fast_partial": 2 * w.n_kv_heads * supp * kv_row + q_bytes + (0 if packed else 4 * w.n_kv_heads * w.top_k),
-        "fast_merge": 4 * w.n_q_heads * w.head_dim,
+        # the merge reads every chunk's (max, sum) and output partial
+        "fast_merge": 4 * w.n_q_heads * nchunk * (w.head_dim + 2) + 4 * w.n_q_heads * w.head_dim,
     }
     for name, k in kern.items():
         if name in alg:
@@ -305,10 +311,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d.get("frac"), "traffic": measured_traffic(dominant, w.name),
                      "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},
-        "roofline_slow_partial": {"bound": "hbm", "achieved": kern["slow_partial"]["GBps"], "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": kern["slow_partial"]["frac"],
-                                  "traffic": measured_traffic("slow_partial", w.name),
-                                  "avg_launch_us": kern["slow_partial"]["avg_us"]},
+        **{f"roofline_{n}": {"bound": "hbm", "achieved": kern[n]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": kern[n]["frac"], "traffic": measured_traffic(n, w.name),
+                             "alg_bytes_per_launch": kern[n]["alg_bytes"], "avg_launch_us": kern[n]["avg_us"]}
+           for n in ("slow_partial", "fast_partial") if n in kern and n != dominant},
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, sp, args.cpu_budget)

@@ -117,6 +117,20 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int3
                       const void* q, float* out, float* mass, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* Launch plan of sfi_slow_step / sfi_slow_step_select for these rows: writes
+ * to splits_host[i] (host int32 [n_seq]) how many split-K partials the slow
+ * step forms for each of the KV heads of sequence seq_ids_host[i], which sets
+ * how much partial state its merge reads.  Launches nothing. */
+int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int32_t n_seq,
+                      int32_t* splits_host);
+
+/* Launch plan of sfi_fast_step / sfi_fast_step_packed for these rows: writes
+ * to chunks_host[i] (host int32 [n_seq]) how many partials (one per chunk of
+ * support rows) the fast step forms for each KV head of sequence
+ * seq_ids_host[i] and its merge then reads.  Launches nothing. */
+int32_t sfi_fast_plan(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                      const int32_t* seq_ids_host, int32_t n_seq, int32_t* chunks_host);
+
 /* Selector.  For each listed sequence b (context T = ctx_len[b]) and KV head
  * g: candidates are positions [n_sink, T - n_recent) (n of them); candidate
  * at 1-based offset a from the sinks gets the prior

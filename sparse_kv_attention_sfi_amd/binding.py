@@ -69,6 +69,8 @@ def lib():
             "sfi_kv_append": (I32, [D, P(I32), I32, VP, VP, VP]),
             "sfi_pack_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP]),
             "sfi_fast_step_packed": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
+            "sfi_slow_plan": (I32, [D, P(I32), I32, P(I32)]),
+            "sfi_fast_plan": (I32, [D, S, P(I32), I32, P(I32)]),
             "sfi_slow_step_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "sfi_debug_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, I32, VP]),
             "sfi_sched_create": (I32, [I32, C.c_uint64, I32, C.c_double, I32, P(VP)]),
@@ -203,6 +205,24 @@ def sfi_slow_step(kv: KVDesc, seq_ids, q, out, mass=None, ws=None, stream=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sfi_slow_step(C.byref(kv.desc), ids, n, _ptr(q), _ptr(out), _ptr(mass), _ptr(ws), nbytes,
                                _stream(stream)), "sfi_slow_step")
+
+
+def sfi_slow_plan(kv: KVDesc, seq_ids):
+    """Split-K partials per KV head the slow step forms for each listed row."""
+    _, ids, n = _ids(seq_ids)
+    out = np.zeros(max(n, 1), dtype=np.int32)
+    _check(lib().sfi_slow_plan(C.byref(kv.desc), ids, n, out.ctypes.data_as(C.POINTER(C.c_int32))),
+           "sfi_slow_plan")
+    return out[:n].tolist()
+
+
+def sfi_fast_plan(kv: KVDesc, sp, seq_ids):
+    """Partials per KV head the fast step forms for each listed row."""
+    _, ids, n = _ids(seq_ids)
+    out = np.zeros(max(n, 1), dtype=np.int32)
+    _check(lib().sfi_fast_plan(C.byref(kv.desc), C.byref(sp), ids, n, out.ctypes.data_as(C.POINTER(C.c_int32))),
+           "sfi_fast_plan")
+    return out[:n].tolist()
 
 
 def sfi_select(kv: KVDesc, sp, seq_ids, mass, sel_idx, sel_cnt, ws=None, stream=None):

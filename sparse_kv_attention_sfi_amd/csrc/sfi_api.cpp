@@ -177,6 +177,17 @@ int fast_part_stride(const sfi_support_params* sp) {
   return static_cast<int>(std::max<int64_t>(1, ceil_div(rows, fast_chunk_rows())));
 }
 
+// Fast-step workgroups per KV head at context t: the support's largest
+// possible size in chunks of crow rows.
+int32_t fast_chunks(const sfi_support_params* sp, int64_t t, int crow) {
+  const int64_t ns_eff = std::min<int64_t>(sp->n_sink, t);
+  const int64_t w_lo = std::max<int64_t>(sp->n_sink, t - sp->n_recent);
+  const int64_t w_eff = std::max<int64_t>(0, t - w_lo);
+  const int64_t n = std::max<int64_t>(0, t - sp->n_sink - sp->n_recent);
+  const int64_t smax = ns_eff + w_eff + std::min<int64_t>(sp->top_k, n);
+  return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(smax, crow)));
+}
+
 struct FastLayout {
   size_t part_ml, part_o, end;
 };
@@ -449,6 +460,38 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   });
 }
 
+int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n_seq, int32_t* splits) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if (desc->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (n_seq == 0) return SFI_OK;
+  if (splits == nullptr) return fail(SFI_ERR_INVALID_ARG, "splits is NULL");
+  int32_t done = 0;
+  return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    SlowArgs a{};
+    CombineArgs c{};
+    plan_slow(desc, ids, cnt, nullptr, nullptr, nullptr, nullptr, a, c);
+    for (int i = 0; i < cnt; ++i) splits[done + i] = a.tab.nsplit[i];
+    done += cnt;
+    return SFI_OK;
+  });
+}
+
+int32_t sfi_fast_plan(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                      int32_t n_seq, int32_t* chunks) {
+  int32_t st;
+  if ((st = check_desc(desc)) != SFI_OK) return st;
+  if ((st = check_params(sp)) != SFI_OK) return st;
+  if (desc->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (n_seq == 0) return SFI_OK;
+  if (chunks == nullptr) return fail(SFI_ERR_INVALID_ARG, "chunks is NULL");
+  const int crow = fast_chunk_rows();
+  for (int32_t i = 0; i < n_seq; ++i) chunks[i] = fast_chunks(sp, desc->ctx_len_host[seq_ids[i]], crow);
+  return SFI_OK;
+}
+
 int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids, int32_t n_seq,
                    const float* mass, int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes,
                    void* stream) {
@@ -570,15 +613,9 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
     a.tab.wg_begin[0] = 0;
     for (int i = 0; i < cnt; ++i) {
       const int b = ids[i];
-      const int64_t t = desc->ctx_len_host[b];
-      const int64_t ns_eff = std::min<int64_t>(sp->n_sink, t);
-      const int64_t w_lo = std::max<int64_t>(sp->n_sink, t - sp->n_recent);
-      const int64_t w_eff = std::max<int64_t>(0, t - w_lo);
-      const int64_t n = std::max<int64_t>(0, t - sp->n_sink - sp->n_recent);
-      const int64_t smax = ns_eff + w_eff + std::min<int64_t>(sp->top_k, n);
       a.tab.seq[i] = b;
-      a.tab.ctx[i] = static_cast<int32_t>(t);
-      a.tab.nsplit[i] = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(smax, crow)));
+      a.tab.ctx[i] = desc->ctx_len_host[b];
+      a.tab.nsplit[i] = fast_chunks(sp, desc->ctx_len_host[b], crow);
       a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
     }
     hipError_t e = timed(SFI_K_FAST, s, [&] {

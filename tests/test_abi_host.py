@@ -156,3 +156,50 @@ def test_workspace_bytes_grow_with_shape():
                         for op in (B.SFI_OP_SLOW, B.SFI_OP_SELECT))
     bad, kb = _desc(d=96)
     assert lib.sfi_workspace_bytes(C.byref(bad), C.byref(sp), B.SFI_OP_SLOW) == 0
+
+
+def test_slow_plan_covers_every_row():
+    """The slow step's launch plan: every sequence gets at least one split, no
+    split is smaller than one block of rows per wave, and no KV head needs
+    more partial slots than the merge accepts.  At the 128K layer the 8 KV
+    heads' 1M rows spread over about 1024 workgroups: 128 splits per head."""
+    lib = S.lib()
+    cases = (((131072,), 131072, 8, 128, B.SFI_BF16), ((1, 300, 65536, 8192), 65536, 8, 128, B.SFI_BF16),
+             ((5000, 17), 5000, 2, 64, B.SFI_F32))
+    for ctx, cap, hkv, d, dt in cases:
+        desc, keep = _desc(batch=len(ctx), hq=4 * hkv, hkv=hkv, d=d, dtype=dt, cap=cap, ctx=ctx)
+        ids = np.arange(len(ctx), dtype=np.int32)
+        out = np.full(len(ctx), -1, dtype=np.int32)
+        st = lib.sfi_slow_plan(C.byref(desc), ids.ctypes.data_as(C.POINTER(C.c_int32)), len(ctx),
+                               out.ctypes.data_as(C.POINTER(C.c_int32)))
+        assert st == 0
+        unit = 4 * 16384 // (d * (2 if dt == B.SFI_BF16 else 4))   # 4 waves x one 16 KiB block each
+        for t, n in zip(ctx, out):
+            assert 1 <= n <= 512 and n <= -(-t // unit), (t, n)
+    assert S.sfi_slow_plan is not None
+    desc, keep = _desc(batch=1, hq=32, hkv=8, d=128, dtype=B.SFI_BF16, cap=131072, ctx=(131072,))
+    one = np.zeros(1, dtype=np.int32)
+    out = np.zeros(1, dtype=np.int32)
+    assert lib.sfi_slow_plan(C.byref(desc), one.ctypes.data_as(C.POINTER(C.c_int32)), 1,
+                             out.ctypes.data_as(C.POINTER(C.c_int32))) == 0 and out[0] == 128
+    desc, keep = _desc(ctx=(100,))
+    bad = np.array([3], dtype=np.int32)
+    assert lib.sfi_slow_plan(C.byref(desc), bad.ctypes.data_as(C.POINTER(C.c_int32)), 1,
+                             out.ctypes.data_as(C.POINTER(C.c_int32))) == B.SFI_ERR_INVALID_ARG
+
+
+def test_fast_plan_chunks_cover_the_support():
+    """The fast step's launch plan: chunks of the per-workgroup row count cover
+    the largest support (sinks + window + min(top_k, candidates))."""
+    lib = S.lib()
+    sp = B.sfi_support_params(16, 256, 2048, 0.1)
+    ctx = (131072, 3000, 300, 5)
+    desc, keep = _desc(batch=4, hq=32, hkv=8, d=128, dtype=B.SFI_BF16, cap=131072, ctx=ctx)
+    ids = np.arange(4, dtype=np.int32)
+    out = np.zeros(4, dtype=np.int32)
+    assert lib.sfi_fast_plan(C.byref(desc), C.byref(sp), ids.ctypes.data_as(C.POINTER(C.c_int32)), 4,
+                             out.ctypes.data_as(C.POINTER(C.c_int32))) == 0
+    sizes = [min(16, t) + max(0, t - max(16, t - 256)) + min(2048, max(0, t - 272)) for t in ctx]
+    assert sizes == [2320, 2320, 300, 5]
+    # 4 waves x 2 tiles x 16 rows = 128 support rows per workgroup by default
+    assert out.tolist() == [max(1, -(-s // 128)) for s in sizes]

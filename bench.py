@@ -9,11 +9,15 @@ caches (32 by default, as a decoder stack would), so a layer's KV rows and
 support are not reused from L2/MALL between two of its own steps.
 
 A "step" is one decode step over all layers: for every layer either the slow
-path (dense split-K attention + mass + Selector) or the fast path (gathered
-sparse attention), as the scheduler says.  ``value`` = K * layers / wall
-time of K steps (decode steps per second per layer), with inputs resident in
-HBM.  Each step's queries are staged into fixed buffers and the step is
-replayed as a HIP graph (one for slow steps, one for fast steps).
+path (dense split-K attention + mass + Selector + packing of the selected
+rows) or the fast path (sparse attention over the packed support), as the
+scheduler says (``--slow async`` runs each layer's Selector on a second
+stream under the next layer's slow attention, the pages' asynchronous layer
+pipeline; on this attention-only loop it is slower than one stream).
+``value`` = K * layers / wall time of K steps (decode steps per
+second per layer), with inputs resident in HBM.  Each step's queries are
+staged into fixed buffers and the step is replayed as a HIP graph (one for
+slow steps, one for fast steps).
 
 Also reported: per-kernel average durations from HIP events recorded by the
 library around its launches (eager pass over the same steps), the roofline
@@ -88,8 +92,11 @@ def parse():
     p.add_argument("--mode", choices=["graph", "eager"], default="graph")
     p.add_argument("--fast", choices=["packed", "gather"], default="packed",
                    help="fast step over the packed support (default) or gathering rows by index")
-    p.add_argument("--slow", choices=["fused", "separate"], default="fused",
-                   help="slow step + Selector (+ pack) in one call (default) or as separate calls")
+    p.add_argument("--slow", choices=["fused", "async", "separate"], default="fused",
+                   help="slow step + Selector (+ pack): fused on one stream (default), fused with the Selector on a "
+                        "second stream under the next layer's slow step, or as separate calls")
+    p.add_argument("--async-depth", type=int, default=4,
+                   help="layers whose Selector may still run when a later layer's slow step starts (--slow async)")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -156,9 +163,28 @@ def main():
         pk = torch.empty(L, 1, w.n_kv_heads, w.top_k, w.head_dim, dtype=q_steps.dtype, device=dev)
         pv = torch.empty_like(pk)
 
-    fused = args.slow == "fused"
+    fused = args.slow in ("fused", "async")
+    if args.slow == "async":
+        # up to `depth` layers in flight: layer l + depth reuses layer l's
+        # workspace and mass buffer, so it waits for layer l's Selector
+        depth = args.async_depth
+        side = torch.cuda.Stream()
+        wsd = [ws] + [S.alloc_workspace(kvs[0], sp) for _ in range(depth - 1)]
+        massd = [mass] + [torch.empty_like(mass) for _ in range(depth - 1)]
+        sel_done = [torch.cuda.Event() for _ in range(L)]
 
     def slow_layers():
+        if args.slow == "async":
+            main = torch.cuda.current_stream()
+            for l in range(L):
+                if l >= depth:
+                    main.wait_event(sel_done[l - depth])
+                S.sfi_slow_step_select_async(kvs[l], sp, [0], q_buf[l], out_buf[l], massd[l % depth], sel[l], cnt[l],
+                                             pk[l] if packed else None, pv[l] if packed else None, wsd[l % depth],
+                                             main, side)
+                sel_done[l].record(side)
+            main.wait_stream(side)
+            return
         for l in range(L):
             if fused:
                 S.sfi_slow_step_select(kvs[l], sp, [0], q_buf[l], out_buf[l], mass, sel[l], cnt[l],

@@ -202,6 +202,28 @@ int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* 
                              float* mass, int32_t* sel_idx, int32_t* sel_cnt, void* packed_k,
                              void* packed_v, void* ws, size_t ws_bytes, void* stream);
 
+/* sfi_slow_step_select with the Selector's kernels (and the packing) on a
+ * second stream, so that they overlap with whatever the caller enqueues on
+ * `stream` next, typically the next layer's attention: the pages' pipeline
+ * runs a layer's Selector and cache reorganisation asynchronously with the
+ * following layer ("Slow-Fast Inference ...", gist.science technical
+ * summary, 3 "Systemdesign und Kernel-Optimierung").  Results are those of
+ * sfi_slow_step_select, bit for bit.
+ *   stream        : runs the slow step; `out` is ready in its order
+ *   select_stream : waits for the slow step, then runs the Selector; mass,
+ *                   sel_idx, sel_cnt and packed_k/v are ready in its order.
+ * mass, the output arrays and ws stay in use until select_stream reaches
+ * that point: the caller orders any later use of them (a fast step, another
+ * call on the same ws or mass) after it, e.g. with an event.  Two layers in
+ * flight need two workspaces and two mass buffers.  With more than 64 rows
+ * the calls' launch groups run one after another through the same two
+ * streams.  Given the same stream twice it behaves as sfi_slow_step_select. */
+int32_t sfi_slow_step_select_async(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                                   const int32_t* seq_ids_host, int32_t n_seq, const void* q,
+                                   float* out, float* mass, int32_t* sel_idx, int32_t* sel_cnt,
+                                   void* packed_k, void* packed_v, void* ws, size_t ws_bytes,
+                                   void* stream, void* select_stream);
+
 /* Appends one token per listed sequence: writes k_new[b][g][:] and
  * v_new[b][g][:] (device [B][Hkv][D], kv_dtype) into row ctx_len[b] of
  * desc->k and desc->v.  Requires ctx_len[b] < kv_capacity.  The caller then

@@ -72,6 +72,7 @@ def lib():
             "sfi_slow_plan": (I32, [D, P(I32), I32, P(I32)]),
             "sfi_fast_plan": (I32, [D, S, P(I32), I32, P(I32)]),
             "sfi_slow_step_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+            "sfi_slow_step_select_async": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP, VP]),
             "sfi_debug_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, I32, VP]),
             "sfi_sched_create": (I32, [I32, C.c_uint64, I32, C.c_double, I32, P(VP)]),
             "sfi_sched_step": (I32, [VP, P(I32), P(I32), P(I32), P(I32)]),
@@ -100,8 +101,9 @@ def _ptr(t):
 
 
 def _stream(stream):
+    """A raw hipStream_t handle from an int, a torch stream, or None (torch's current stream)."""
     if stream is not None:
-        return C.c_void_p(int(stream))
+        return C.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -254,6 +256,30 @@ def sfi_slow_step_select(kv: KVDesc, sp, seq_ids, q, out, mass, sel_idx, sel_cnt
     _check(lib().sfi_slow_step_select(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(out), _ptr(mass),
                                       _ptr(sel_idx), _ptr(sel_cnt), _ptr(packed_k), _ptr(packed_v), _ptr(ws),
                                       nbytes, _stream(stream)), "sfi_slow_step_select")
+
+
+def sfi_slow_step_select_async(kv: KVDesc, sp, seq_ids, q, out, mass, sel_idx, sel_cnt, packed_k, packed_v, ws,
+                               stream, select_stream):
+    """Like sfi_slow_step_select, with the Selector on ``select_stream`` (see
+    include/sfi.h for the ordering the caller owes)."""
+    import torch
+    B, Hq, Hkv, D = kv.batch, kv.n_q_heads, kv.n_kv_heads, kv.head_dim
+    _need(q, kv.dtype, (B, Hq, D), "q")
+    _need(out, torch.float32, (B, Hq, D), "out")
+    _need(mass, torch.float32, (B, Hkv, kv.capacity), "mass")
+    _need(sel_idx, torch.int32, (B, Hkv, sp.top_k), "sel_idx")
+    _need(sel_cnt, torch.int32, (B, Hkv), "sel_cnt")
+    if packed_k is not None or packed_v is not None:
+        _need(packed_k, kv.dtype, (B, Hkv, sp.top_k, D), "packed_k")
+        _need(packed_v, kv.dtype, (B, Hkv, sp.top_k, D), "packed_v")
+    if stream is None or select_stream is None or _stream(stream).value == _stream(select_stream).value:
+        raise ValueError("stream and select_stream must be two distinct streams")
+    _, ids, n = _ids(seq_ids)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sfi_slow_step_select_async(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(out), _ptr(mass),
+                                            _ptr(sel_idx), _ptr(sel_cnt), _ptr(packed_k), _ptr(packed_v),
+                                            _ptr(ws), nbytes, _stream(stream), _stream(select_stream)),
+           "sfi_slow_step_select_async")
 
 
 def sfi_fast_step(kv: KVDesc, sp, seq_ids, q, sel_idx, sel_cnt, out, ws, stream=None):

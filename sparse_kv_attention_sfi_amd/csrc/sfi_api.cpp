@@ -235,6 +235,19 @@ hipEvent_t take_event(Prof& p) {
 
 thread_local LaunchTiming* g_timing = nullptr;
 
+// Per-thread events that order work across two streams (timing disabled).  A
+// wait binds to the record that precedes it, so one event per role can be
+// re-recorded by every call.
+bool stream_event(int role, hipEvent_t* out) {
+  thread_local hipEvent_t ev[2] = {nullptr, nullptr};
+  if (ev[role] == nullptr && hipEventCreateWithFlags(&ev[role], hipEventDisableTiming) != hipSuccess) {
+    ev[role] = nullptr;
+    return false;
+  }
+  *out = ev[role];
+  return true;
+}
+
 // Runs `launch` (returning hipError_t); when timing is on, its kernels stamp a
 // fresh event pair from their own dispatch packets.
 template <typename F>
@@ -514,10 +527,14 @@ int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const 
   });
 }
 
-int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
-                             int32_t n_seq, const void* q, float* out, float* mass, int32_t* sel_idx,
-                             int32_t* sel_cnt, void* packed_k, void* packed_v, void* ws, size_t ws_bytes,
-                             void* stream) {
+// Slow step + Selector (+ packing).  The Selector's kernels run on sel_s; when
+// that is another stream it waits for the slow step's kernels on s, and with
+// several launch groups the next group's slow step (which reuses the
+// workspace) waits for the previous group's Selector.
+static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                                     int32_t n_seq, const void* q, float* out, float* mass, int32_t* sel_idx,
+                                     int32_t* sel_cnt, void* packed_k, void* packed_v, void* ws, size_t ws_bytes,
+                                     hipStream_t s, hipStream_t sel_s) {
   int32_t st;
   if ((st = check_desc(desc)) != SFI_OK) return st;
   if ((st = check_kv(desc)) != SFI_OK) return st;
@@ -531,10 +548,18 @@ int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* 
   if ((packed_k == nullptr) != (packed_v == nullptr))
     return fail(SFI_ERR_INVALID_ARG, "packed_k and packed_v must both be given or both be NULL");
   if ((st = check_ws(ws, ws_bytes, std::max(slow_layout(desc).end, select_layout(desc).end))) != SFI_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool split = sel_s != s;
+  hipEvent_t ev_slow = nullptr, ev_sel = nullptr;
+  if (split && (!stream_event(0, &ev_slow) || !stream_event(1, &ev_sel)))
+    return fail(SFI_ERR_HIP, "could not create the events that order the two streams");
   char* w = static_cast<char*>(ws);
   const Header H = header_layout(desc);
+  bool first = true;
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    hipError_t e;
+    if (split && !first && (e = hipStreamWaitEvent(s, ev_sel, 0)) != hipSuccess)
+      return hip_fail(e, "stream wait");
+    first = false;
     // the slow scratch and the Selector scratch overlap: the Selector's
     // kernels run after the combine has consumed the logits and partials
     SlowArgs a{};
@@ -549,6 +574,10 @@ int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* 
     c.lambda = sp->lambda;
     int32_t r = run_slow(desc, a, c, cnt, s);
     if (r != SFI_OK) return r;
+    if (split) {
+      if ((e = hipEventRecord(ev_slow, s)) != hipSuccess) return hip_fail(e, "event record");
+      if ((e = hipStreamWaitEvent(sel_s, ev_slow, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    }
     SelectArgs sa{};
     plan_select(desc, sp, ids, cnt, mass, sel_idx, sel_cnt, w, sa);
     sa.hist_ready = true;
@@ -559,8 +588,28 @@ int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* 
       sa.packed_v = packed_v;
       sa.row_bytes = desc->head_dim * elem_bytes(desc->kv_dtype);
     }
-    return run_select(sa, cnt, s);
+    r = run_select(sa, cnt, sel_s);
+    if (r != SFI_OK) return r;
+    if (split && (e = hipEventRecord(ev_sel, sel_s)) != hipSuccess) return hip_fail(e, "event record");
+    return SFI_OK;
   });
+}
+
+int32_t sfi_slow_step_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                             int32_t n_seq, const void* q, float* out, float* mass, int32_t* sel_idx,
+                             int32_t* sel_cnt, void* packed_k, void* packed_v, void* ws, size_t ws_bytes,
+                             void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return slow_step_select_impl(desc, sp, seq_ids, n_seq, q, out, mass, sel_idx, sel_cnt, packed_k, packed_v, ws,
+                               ws_bytes, s, s);
+}
+
+int32_t sfi_slow_step_select_async(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                                   int32_t n_seq, const void* q, float* out, float* mass, int32_t* sel_idx,
+                                   int32_t* sel_cnt, void* packed_k, void* packed_v, void* ws, size_t ws_bytes,
+                                   void* stream, void* select_stream) {
+  return slow_step_select_impl(desc, sp, seq_ids, n_seq, q, out, mass, sel_idx, sel_cnt, packed_k, packed_v, ws,
+                               ws_bytes, static_cast<hipStream_t>(stream), static_cast<hipStream_t>(select_stream));
 }
 
 static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,

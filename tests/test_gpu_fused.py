@@ -134,3 +134,98 @@ def test_fused_degenerate_k_and_no_packing(k, packed):
     b = _fused(kv, sp, [0, 1], q, ws, packed)
     _assert_same(a, b)
     _check_oracle(kv, sp, q, b, [0, 1])
+
+
+# ------------------------------------------------------------------ two streams
+def _async(kv, sp, ids, q, ws, main, side, o=None):
+    o = o if o is not None else _outputs(kv, sp, True)
+    S.sfi_slow_step_select_async(kv, sp, ids, q, o["out"], o["mass"], o["sel"], o["cnt"], o["pk"], o["pv"], ws,
+                                 main, side)
+    return o
+
+
+def test_async_equals_fused():
+    """The Selector on a second stream gives the single-stream results bit for
+    bit (ragged batch: top-k over chunks, keep-all and no candidates)."""
+    ctx = [9000, 2500, 300, 40]
+    kv, q = random_cache(len(ctx), 32, 8, 9000, 128, torch.bfloat16, ctx, seed=77, q_scale=2.0)
+    sp = S.support_params(16, 256, 512, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    ref = _fused(kv, sp, [0, 1, 2, 3], q, ws)
+    torch.cuda.synchronize()
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    ws2 = S.alloc_workspace(kv, sp)
+    torch.cuda.synchronize()
+    o = _async(kv, sp, [0, 1, 2, 3], q, ws2, main, side)
+    _assert_same(ref, o)
+
+
+def _layers(n, ctx, seed):
+    layers = []
+    for l in range(n):
+        kv, q = random_cache(1, 32, 8, ctx, 128, torch.bfloat16, [ctx - 3 * l], seed=seed + l, q_scale=2.0)
+        layers.append((kv, q))
+    return layers
+
+
+def _pipelined(layers, sp, ws, outs, main, side, done):
+    """Layer l's slow step on `main`, its Selector on `side`; layer l + 2 reuses
+    layer l's workspace and mass buffer, so it waits for layer l's Selector."""
+    for l, (kv, q) in enumerate(layers):
+        if l >= 2:
+            main.wait_event(done[l - 2])
+        o = outs[l]
+        o["mass"] = outs[l % 2]["mass_buf"]
+        S.sfi_slow_step_select_async(kv, sp, [0], q, o["out"], o["mass"], o["sel"], o["cnt"], o["pk"], o["pv"],
+                                     ws[l % 2], main, side)
+        done[l].record(side)
+    main.wait_stream(side)
+
+
+def test_async_pipelined_layers_and_graph_replay():
+    """Six layers pipelined over two streams with double-buffered workspaces and
+    mass buffers give each layer's single-stream results bit for bit, eagerly
+    and as a captured graph replayed several times with eager work between."""
+    layers = _layers(6, 12000, seed=300)
+    sp = S.support_params(16, 256, 1024, 0.1)
+    kv0 = layers[0][0]
+    ws_ref = S.alloc_workspace(kv0, sp)
+    refs = []
+    for kv, q in layers:
+        refs.append(_fused(kv, sp, [0], q, ws_ref))
+    torch.cuda.synchronize()
+    ws = [S.alloc_workspace(kv0, sp), S.alloc_workspace(kv0, sp)]
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [_outputs(kv, sp, True) for kv, _ in layers]
+    for l in range(2):
+        outs[l]["mass_buf"] = torch.full_like(outs[l]["mass"], -1.0)
+    done = [torch.cuda.Event() for _ in layers]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(main):
+        _pipelined(layers, sp, ws, outs, main, side, done)
+    torch.cuda.synchronize()
+    for l in range(6):
+        for key in ("out", "sel", "cnt", "pk", "pv"):
+            assert torch.equal(outs[l][key], refs[l][key]), (l, key)
+    for l in (4, 5):   # the mass buffers hold the last two layers'
+        T = int(layers[l][0].ctx[0])
+        assert torch.equal(outs[l % 2]["mass_buf"][..., :T], refs[l]["mass"][..., :T])
+
+    # the same pipeline captured once and replayed
+    g = torch.cuda.CUDAGraph()
+    for o in outs:
+        for key in ("out", "sel", "cnt", "pk", "pv"):
+            o[key].fill_(0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=main):
+        _pipelined(layers, sp, ws, outs, main, side, done)
+    for rep in range(3):
+        for o in outs:
+            o["out"].fill_(float(rep))
+            o["sel"].fill_(-9)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(6):
+            for key in ("out", "sel", "cnt", "pk", "pv"):
+                assert torch.equal(outs[l][key], refs[l][key]), (rep, l, key)

@@ -5,8 +5,10 @@ Workload (default): the 8B-shaped layer at 128K context, batch 1, bf16 KV,
 32 query / 8 KV heads, head_dim 128, 16 sinks + 256 recent + top-2048,
 lambda 0.1, spans geometric with mean 18 drawn by the boundary scheduler.
 Every decode step runs that layer shape over ``--layers`` independent
-caches (32 by default, as a decoder stack would), so a layer's KV rows and
-support are not reused from L2/MALL between two of its own steps.
+caches (128 by default: four 32-layer stacks' worth), so none of a layer's KV
+rows or support (9.5 MB per fast step) is still in L2 or the 256 MB
+last-level cache at its next step; a timed cold-cache check (each call after
+a 1 GiB read) confirms the kernel times.
 
 A "step" is one decode step over all layers: for every layer either the slow
 path (dense split-K attention + mass + Selector + packing of the selected
@@ -86,7 +88,9 @@ def parse():
     p.add_argument("--steps", type=int, default=1024)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", default="C3")
-    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--layers", type=int, default=128,
+                   help="independent layer caches cycled per decode step (128: a layer's fast-step data, "
+                        "9.5 MB, is never still in the 256 MB last-level cache at its next step)")
     p.add_argument("--dense-steps", type=int, default=64)
     p.add_argument("--eager-steps", type=int, default=128)
     p.add_argument("--mode", choices=["graph", "eager"], default="graph")
@@ -97,6 +101,8 @@ def parse():
                         "second stream under the next layer's slow step, or as separate calls")
     p.add_argument("--async-depth", type=int, default=4,
                    help="layers whose Selector may still run when a later layer's slow step starts (--slow async)")
+    p.add_argument("--cold-checks", type=int, default=16,
+                   help="calls of the slow and the fast path timed after a 1 GiB cache flush (0: skip)")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -173,6 +179,16 @@ def main():
         massd = [mass] + [torch.empty_like(mass) for _ in range(depth - 1)]
         sel_done = [torch.cuda.Event() for _ in range(L)]
 
+    def slow_layer(l):
+        S.sfi_slow_step_select(kvs[l], sp, [0], q_buf[l], out_buf[l], mass, sel[l], cnt[l],
+                               pk[l] if packed else None, pv[l] if packed else None, ws)
+
+    def fast_layer(l):
+        if packed:
+            S.sfi_fast_step_packed(kvs[l], sp, [0], q_buf[l], pk[l], pv[l], cnt[l], out_buf[l], ws)
+        else:
+            S.sfi_fast_step(kvs[l], sp, [0], q_buf[l], sel[l], cnt[l], out_buf[l], ws)
+
     def slow_layers():
         if args.slow == "async":
             main = torch.cuda.current_stream()
@@ -187,8 +203,7 @@ def main():
             return
         for l in range(L):
             if fused:
-                S.sfi_slow_step_select(kvs[l], sp, [0], q_buf[l], out_buf[l], mass, sel[l], cnt[l],
-                                       pk[l] if packed else None, pv[l] if packed else None, ws)
+                slow_layer(l)
                 continue
             S.sfi_slow_step(kvs[l], [0], q_buf[l], out_buf[l], mass, ws)
             S.sfi_select(kvs[l], sp, [0], mass, sel[l], cnt[l], ws)
@@ -197,10 +212,7 @@ def main():
 
     def fast_layers():
         for l in range(L):
-            if packed:
-                S.sfi_fast_step_packed(kvs[l], sp, [0], q_buf[l], pk[l], pv[l], cnt[l], out_buf[l], ws)
-            else:
-                S.sfi_fast_step(kvs[l], sp, [0], q_buf[l], sel[l], cnt[l], out_buf[l], ws)
+            fast_layer(l)
 
     def dense_layers():
         for l in range(L):
@@ -264,6 +276,34 @@ def main():
         ms, n = S.sfi_profile_read(kid)
         if n:
             kern[name] = {"launches": n, "avg_us": 1e3 * ms / n}
+
+    # Cold-cache check: the same kernels, each call preceded by a 1 GiB read
+    # that evicts L2 and the 256 MB last-level cache.  (A read, not a write: a
+    # written flush would leave the caches full of dirty lines whose write-back
+    # the next kernel pays for, which the decode loop never does.)  Close
+    # agreement with the averages above shows the 32-layer loop runs cold.
+    cold = None
+    if args.cold_checks:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        S.sfi_profile_reset()
+        for i in range(args.cold_checks):
+            l = i % L
+            for fn in (lambda: slow_layer(l), lambda: fast_layer(l)):
+                # the timed call follows the flush in stream order, with the GPU busy
+                # in between (after an idle wait a short kernel also pays to wake up)
+                torch.sum(flush, dim=0, out=sink)
+                S.sfi_profile_enable(True)
+                fn()
+                S.sfi_profile_enable(False)
+                torch.cuda.synchronize()
+        cold = {}
+        for kid, name in S.KERNEL_NAMES.items():
+            ms, n = S.sfi_profile_read(kid)
+            if n:
+                cold[name + "_us"] = 1e3 * ms / n
+        cold["calls"] = args.cold_checks
+        del flush
     T = w.ctx
     esz = 2 if w.dtype == "bf16" else 4
     n_cand = T - w.n_sink - w.n_recent
@@ -334,6 +374,7 @@ def main():
         "speedup_vs_dense": value / dense_rate if dense_rate else None,
         "kernels": kern,
         "kernel_time_share": {n: t / sum(total_time.values()) for n, t in total_time.items()},
+        "cold_cache_check": cold,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d.get("frac"), "traffic": measured_traffic(dominant, w.name),
                      "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},

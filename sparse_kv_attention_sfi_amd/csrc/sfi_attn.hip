@@ -431,12 +431,12 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
       kvalid[t] = row < r_end;
       const char* src = Kb + static_cast<int64_t>(kvalid[t] ? row : r_end - 1) * RB + 16 * kg;
 #pragma unroll
-      for (int kk = 0; kk < A::kNL; ++kk) kb[t][kk] = ld16(src + 64 * kk);
+      for (int kk = 0; kk < A::kNL; ++kk) kb[t][kk] = ld16_stream(src + 64 * kk);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int row = min(r0 + vr + A::kRPL * i, r_end - 1);
-      vb[i] = ld16(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
+      vb[i] = ld16_stream(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
     }
     float* lbase = a.logits ? a.logits + qh0 * a.logit_pitch + r0 : nullptr;
     st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lbase, a.logit_pitch, r_end - r0, lane);
@@ -656,8 +656,7 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
       const int j = j0 + 4 * (it * kCombineThreads + tid);
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        x[it][h] = j < j1 ? *reinterpret_cast<const float4*>(lg + h * a.logit_pitch + j)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[it][h] = j < j1 ? ld16_stream_f(lg + h * a.logit_pitch + j) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     // candidates [n_sink, T - n_recent) take part in a top-k only when there
     // are more of them than k (otherwise the Selector keeps all of them)
@@ -805,12 +804,12 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
       any |= kvalid[tt];
       const char* src = Kb + static_cast<int64_t>(pos >= 0 ? pos : 0) * RB + 16 * kg;
 #pragma unroll
-      for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16(src + 64 * kk);
+      for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16_stream(src + 64 * kk);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int pos = s_pos[w0 + vr + A::kRPL * i];
-      vb[i] = ld16(Vb + static_cast<int64_t>(pos >= 0 ? pos : 0) * RB + 16 * vp);
+      vb[i] = ld16_stream(Vb + static_cast<int64_t>(pos >= 0 ? pos : 0) * RB + 16 * vp);
     }
     // a wave whose rows are all outside the support keeps the empty state
     if (__ballot(any) != 0) {
@@ -893,13 +892,13 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
     const int64_t off = row_off(w0 + 16 * tt + kr, pk);
     const char* src = (pk ? Kp : Kc) + off + 16 * kg;
 #pragma unroll
-    for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16(src + 64 * kk);
+    for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16_stream(src + 64 * kk);
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     bool pk;
     const int64_t off = row_off(w0 + vr + A::kRPL * i, pk);
-    vb[i] = ld16((pk ? Vp : Vc) + off + 16 * vp);
+    vb[i] = ld16_stream((pk ? Vp : Vc) + off + 16 * vp);
   }
   const int cnt = min(max(a.sel_cnt[bg], 0), kmax);
   const int size = fixed + cnt;

@@ -28,6 +28,20 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte streaming load: the non-temporal hint (`nt`) marks data read once,
+// so streaming it does not push reusable lines (such as the logits the next
+// kernel reads back) out of the caches.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float4 ld16_stream_f(const float* p) {
+  const uint4 u = ld16_stream(p);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
 // Widen a 16-byte piece to floats.  bf16 -> f32 is exact (shift into the
 // high half of the word).
 __device__ __forceinline__ void widen(BF16, const uint4& u, float* f) {

@@ -330,8 +330,8 @@ __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const
       if (it < items) {
         const int r = it / np, pc = it - r * np;
         const int64_t off = static_cast<int64_t>(s_pos[r]) * a.row_bytes + 16 * pc;
-        kv[u] = ld16(K + off);
-        vv[u] = ld16(V + off);
+        kv[u] = ld16_stream(K + off);
+        vv[u] = ld16_stream(V + off);
       }
     }
 #pragma unroll

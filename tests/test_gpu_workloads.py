@@ -1,5 +1,6 @@
 """GPU parity on the five synthetic workloads, in the launch configuration the
-bench uses: the full 64-step loop of the tiny fp32 case, sampled steps of the
+bench uses (the fused refresh with packing, the fast step over the packed
+support): the full 64-step loop of the tiny fp32 case, sampled steps of the
 larger ones (every output the oracle can afford is compared element by
 element; the rest is checked through properties that hold at any size), and
 HIP-graph replay against eager results."""
@@ -30,7 +31,10 @@ def _schedules(w, n_steps):
 
 
 class Runner:
-    """Buffers and calls of one layer of a workload through the C ABI."""
+    """Buffers and calls of one layer of a workload through the C ABI, in the
+    bench's configuration: the fused refresh (slow step + Selector + packing)
+    and the fast step over the packed support.  The separate calls and the
+    gather fast step serve as cross-checks."""
 
     def __init__(self, w, kv):
         dev = kv.k.device
@@ -42,26 +46,31 @@ class Runner:
         self.mass = torch.full((B, w.n_kv_heads, kv.capacity), -1.0, device=dev)
         self.sel = torch.full((B, w.n_kv_heads, w.top_k), -1, dtype=torch.int32, device=dev)
         self.cnt = torch.zeros(B, w.n_kv_heads, dtype=torch.int32, device=dev)
-        self.pk = self.pv = None
+        shape = (B, w.n_kv_heads, w.top_k, w.head_dim)
+        self.pk = torch.zeros(shape, dtype=kv.dtype, device=dev)
+        self.pv = torch.zeros(shape, dtype=kv.dtype, device=dev)
 
     def slow(self, ids, q):
         if ids:
+            S.sfi_slow_step_select(self.kv, self.sp, ids, q, self.out, self.mass, self.sel, self.cnt, self.pk,
+                                   self.pv, self.ws)
+
+    def slow_separate(self, ids, q):
+        if ids:
             S.sfi_slow_step(self.kv, ids, q, self.out, self.mass, self.ws)
             S.sfi_select(self.kv, self.sp, ids, self.mass, self.sel, self.cnt, self.ws)
+            S.sfi_pack_support(self.kv, self.sp, ids, self.sel, self.cnt, self.pk, self.pv)
 
     def fast(self, ids, q):
         if ids:
+            S.sfi_fast_step_packed(self.kv, self.sp, ids, q, self.pk, self.pv, self.cnt, self.out, self.ws)
+
+    def fast_gather(self, ids, q):
+        if ids:
             S.sfi_fast_step(self.kv, self.sp, ids, q, self.sel, self.cnt, self.out, self.ws)
 
-    def fast_packed(self, ids, q):
-        """Pack the current selection, then the packed fast step."""
-        if ids:
-            if self.pk is None:
-                shape = (self.w.batch, self.w.n_kv_heads, self.w.top_k, self.w.head_dim)
-                self.pk = torch.empty(shape, dtype=self.kv.dtype, device=self.kv.k.device)
-                self.pv = torch.empty_like(self.pk)
-            S.sfi_pack_support(self.kv, self.sp, ids, self.sel, self.cnt, self.pk, self.pv)
-            S.sfi_fast_step_packed(self.kv, self.sp, ids, q, self.pk, self.pv, self.cnt, self.out, self.ws)
+    def state(self):
+        return [x.clone() for x in (self.out, self.mass, self.sel, self.cnt, self.pk, self.pv)]
 
     def gpu_sel(self, b):
         cnt = self.cnt[b].cpu().numpy()
@@ -111,8 +120,12 @@ def test_tiny_fp32_full_loop():
     recalls, exact = [], 0
     for t in range(w.n_steps):
         if flags[0][t]:
+            r.slow_separate([0], q[t])
+            torch.cuda.synchronize()
+            separate = r.state()
             r.slow([0], q[t])
             torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip(r.state(), separate))   # fused == separate calls
             _, kinds = _check_slow(r, 0, np64(q[t, 0]), K64, V64, T)
             exact += kinds.count("exact")
             s_idx = span_ids[0][t]
@@ -124,10 +137,10 @@ def test_tiny_fp32_full_loop():
             torch.cuda.synchronize()
             ref = O.fast_step(np64(q[t, 0]), K64, V64, T, w.n_sink, w.n_recent, r.gpu_sel(0))
             assert np.max(np.abs(np64(r.out[0]) - ref)) < OUT_TOL
-            gather_out = r.out.clone()
-            r.fast_packed([0], q[t])
+            packed_out = r.out.clone()
+            r.fast_gather([0], q[t])
             torch.cuda.synchronize()
-            assert torch.equal(r.out, gather_out)
+            assert torch.equal(r.out, packed_out)
     assert exact >= 1                       # supports with clear gaps match bit for bit
     assert np.mean(recalls) > 0.9
 
@@ -159,6 +172,10 @@ def test_8b_layer_sampled_steps(wname, n_fast):
             r.fast([0], q[t])
             torch.cuda.synchronize()
             gpu = np64(r.out[0])
+            packed_out = r.out.clone()
+            r.fast_gather([0], q[t])
+            torch.cuda.synchronize()
+            assert torch.equal(r.out, packed_out)
             ref = O.fast_step(np64(q[t, 0]), K64, V64, T, w.n_sink, w.n_recent, r.gpu_sel(0))
             assert np.max(np.abs(gpu - ref)) < OUT_TOL
             # with the oracle's own support (differs only at near-ties)
@@ -255,12 +272,11 @@ def test_graph_replay_matches_eager():
     sel = torch.empty(B, Hkv, 512, dtype=torch.int32, device=dev)
     cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
 
-    def slow():
-        S.sfi_slow_step(kv, [0, 1], q_buf, out, mass, ws)
-        S.sfi_select(kv, sp, [0, 1], mass, sel, cnt, ws)
-
     pk = torch.empty(B, Hkv, 512, D, dtype=torch.bfloat16, device=dev)
     pv = torch.empty_like(pk)
+
+    def slow():
+        S.sfi_slow_step_select(kv, sp, [0, 1], q_buf, out, mass, sel, cnt, pk, pv, ws)
 
     def fast():
         S.sfi_fast_step(kv, sp, [0, 1], q_buf, sel, cnt, out, ws)

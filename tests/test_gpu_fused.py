@@ -229,3 +229,39 @@ def test_async_pipelined_layers_and_graph_replay():
         for l in range(6):
             for key in ("out", "sel", "cnt", "pk", "pv"):
                 assert torch.equal(outs[l][key], refs[l][key]), (rep, l, key)
+
+
+def test_more_rows_than_one_launch_group():
+    """70 sequences (more than one launch group of 64): the fused, separate,
+    two-stream and fast paths agree bit for bit, rows of both groups match the
+    oracle, and unlisted rows stay untouched."""
+    B = 70
+    rng = np.random.default_rng(70)
+    ctx = [int(x) for x in rng.integers(300, 2600, size=B)]
+    kv, q = random_cache(B, 8, 2, 2600, 64, torch.bfloat16, ctx, seed=70, q_scale=2.0)
+    sp = S.support_params(4, 32, 64, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    ids = [b for b in range(B) if b != 5]          # row 5 unlisted
+    a = _separate(kv, sp, ids, q, ws)
+    b = _fused(kv, sp, ids, q, ws)
+    _assert_same(a, b)
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    ws2 = S.alloc_workspace(kv, sp)
+    torch.cuda.synchronize()
+    c = _async(kv, sp, ids, q, ws2, main, side)
+    _assert_same(a, c)
+    assert torch.all(b["cnt"][5] == -7) and torch.all(b["out"][5] == 7.0)
+    _check_oracle(kv, sp, q, b, [0, 63, 64, 69])
+    # fast steps over both launch groups: packed == gather, and the oracle
+    out_p = torch.full_like(b["out"], 7.0)
+    out_g = torch.full_like(b["out"], 7.0)
+    S.sfi_fast_step_packed(kv, sp, ids, q, b["pk"], b["pv"], b["cnt"], out_p, ws)
+    S.sfi_fast_step(kv, sp, ids, q, b["sel"], b["cnt"], out_g, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_g) and torch.all(out_p[5] == 7.0)
+    for r in (1, 64, 68):
+        T = ctx[r]
+        c_ = b["cnt"][r].cpu().numpy()
+        sels = [b["sel"][r, g, :c_[g]].cpu().numpy().astype(np.int64) for g in range(2)]
+        ref = O.fast_step(np64(q[r]), np64(kv.k[r, :, :T]), np64(kv.v[r, :, :T]), T, 4, 32, sels)
+        assert np.max(np.abs(np64(out_p[r]) - ref)) < OUT_TOL

@@ -103,6 +103,8 @@ def parse():
                    help="layers whose Selector may still run when a later layer's slow step starts (--slow async)")
     p.add_argument("--cold-checks", type=int, default=16,
                    help="calls of the slow and the fast path timed after a 1 GiB cache flush (0: skip)")
+    p.add_argument("--batch-check", type=int, default=16, metavar="B",
+                   help="also time the fast step for B sequences in one launch (0: skip)")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -383,6 +385,8 @@ def main():
                              "alg_bytes_per_launch": kern[n]["alg_bytes"], "avg_launch_us": kern[n]["avg_us"]}
            for n in ("slow_partial", "fast_partial") if n in kern and n != dominant},
     }
+    if args.batch_check:
+        result["fast_step_batch"] = fast_batch_check(w, sp, args.batch_check, dev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, sp, args.cpu_budget)
     if args.copy_probe:
@@ -393,6 +397,57 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
     print(json.dumps(result))
+
+
+def fast_batch_check(w, sp, batch, dev, ctx=32768, calls=20):
+    """The fast step of the same layer shape for `batch` sequences in one
+    launch (contexts of 32K; the support, 2320 rows per KV head, does not
+    depend on the context), each timed launch right after a 1 GiB read so
+    that it runs cold: the kernel's bandwidth once a launch moves enough data
+    to fill the chip.  Reported beside the batch-1 workload, not part of it."""
+    import torch
+
+    import sparse_kv_attention_sfi_amd as S
+    from synth import gen
+
+    K, V = gen.random_cache(batch, w.n_kv_heads, ctx, w.head_dim, w.dtype, dev, seed=w.seed + 77)
+    kv = S.KVDesc(K, V, [ctx] * batch, w.n_q_heads)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 78)
+    q = (2 * torch.randn(batch, w.n_q_heads, w.head_dim, generator=g, device=dev)).to(K.dtype)
+    ws = S.alloc_workspace(kv, sp)
+    out = torch.empty(batch, w.n_q_heads, w.head_dim, device=dev)
+    mass = torch.empty(batch, w.n_kv_heads, ctx, device=dev)
+    sel = torch.empty(batch, w.n_kv_heads, w.top_k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(batch, w.n_kv_heads, dtype=torch.int32, device=dev)
+    pk = torch.empty(batch, w.n_kv_heads, w.top_k, w.head_dim, dtype=K.dtype, device=dev)
+    pv = torch.empty_like(pk)
+    ids = list(range(batch))
+    S.sfi_slow_step_select(kv, sp, ids, q, out, mass, sel, cnt, pk, pv, ws)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    S.sfi_profile_reset()
+    for _ in range(calls):
+        torch.sum(flush, dim=0, out=sink)
+        S.sfi_profile_enable(True)
+        S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out, ws)
+        S.sfi_profile_enable(False)
+        torch.cuda.synchronize()
+    res = {"batch": batch, "ctx": ctx, "calls": calls}
+    for kid, name in S.KERNEL_NAMES.items():
+        ms, n = S.sfi_profile_read(kid)
+        if n:
+            res[name + "_us"] = 1e3 * ms / n
+    supp = w.n_sink + w.n_recent + w.top_k
+    esz = 2 if w.dtype == "bf16" else 4
+    alg = batch * (2 * w.n_kv_heads * supp * w.head_dim * esz + w.n_q_heads * w.head_dim * esz)
+    res["fast_partial_alg_bytes"] = alg
+    res["fast_partial_GBps"] = alg / (res["fast_partial_us"] * 1e-6) / 1e9
+    res["fast_partial_frac"] = res["fast_partial_GBps"] / HBM_PEAK_GBS
+    del K, V, kv, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, kv, q_steps, flags, sp, budget):

@@ -125,23 +125,36 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int 
   __syncthreads();
 }
 
-// Among `m` distinct keys in LDS (16-byte aligned), the one with exactly
-// need - 1 larger keys.  Every thread ranks one key; the comparisons read the
-// list eight keys at a time (broadcast 16-byte LDS reads).
-__device__ __forceinline__ uint64_t rank_select(const uint64_t* keys, int m, int need, uint64_t* s_out) {
+// Among m <= kSelThreads distinct keys in LDS (16-byte aligned), the one with
+// exactly need - 1 larger keys.  The list is cut into P = kSelThreads / m
+// parts; thread t counts the keys of part t / m that exceed key t % m (eight
+// keys per step, broadcast 16-byte LDS reads), and the P partial ranks are
+// summed through LDS.  s_part holds kSelThreads ints.
+__device__ __forceinline__ uint64_t rank_select(const uint64_t* keys, int m, int need, int* s_part,
+                                                uint64_t* s_out) {
   const int tid = threadIdx.x;
-  if (tid < m) {
-    const uint64_t mine = keys[tid];
+  const int parts = m > 0 ? kSelThreads / m : 1;
+  const int span = ((m + parts - 1) / parts + 7) & ~7;  // keys per part, a multiple of 8
+  const int i = m > 0 ? tid % m : 0, part = m > 0 ? tid / m : parts;
+  if (part < parts) {
+    const uint64_t mine = keys[i];
+    const int j0 = min(m, part * span), j1 = min(m, j0 + span);
     int rank = 0;
-    const int m8 = m & ~7;
-    for (int j = 0; j < m8; j += 8) {
+    const int j8 = j0 + ((j1 - j0) & ~7);
+    for (int j = j0; j < j8; j += 8) {
       const ulonglong2* p = reinterpret_cast<const ulonglong2*>(keys + j);
       const ulonglong2 a = p[0], b = p[1], c = p[2], d = p[3];
       rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine) + (c.x > mine) + (c.y > mine) +
               (d.x > mine) + (d.y > mine);
     }
-    for (int j = m8; j < m; ++j) rank += keys[j] > mine;
-    if (rank == need - 1) *s_out = mine;
+    for (int j = j8; j < j1; ++j) rank += keys[j] > mine;
+    s_part[tid] = rank;
+  }
+  __syncthreads();
+  if (tid < m) {
+    int rank = 0;
+    for (int p = 0; p < parts; ++p) rank += s_part[p * m + tid];
+    if (rank == need - 1) *s_out = keys[tid];
   }
   __syncthreads();
   return *s_out;
@@ -166,7 +179,8 @@ __device__ uint64_t radix_resolve(Src src, int count, int match, uint64_t prefix
         if ((key & pmask) == prefix) small[atomicAdd(&s_res[0], 1)] = key;
       }
       __syncthreads();
-      const uint64_t k = rank_select(small, match, need, s_key);
+      // partial ranks after the gathered keys (kSelThreads 64-bit keys = 2 kSelThreads words)
+      const uint64_t k = rank_select(small, match, need, reinterpret_cast<int*>(s_hist) + 2 * kSelThreads, s_key);
       __syncthreads();
       return k;
     }
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
     __syncthreads();
     kstar = cnt_d1 <= kSelThreads
-                ? rank_select(s_list, cnt_d1, need, &s_kstar)
+                ? rank_select(s_list, cnt_d1, need, reinterpret_cast<int*>(s_hist), &s_kstar)
                 : radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, cnt_d1, pfx, pmask, 64 - kSelDigitBits,
                                 need, s_hist, s_wave, s_res, &s_kstar);
     const int lo = a.n_sink + i0;  // first position of this chunk

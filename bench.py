@@ -43,16 +43,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3_128k_layer_traffic.json")
 
 
 def csrc_digest():
-    """Digest of the kernel sources; counter readings apply only to kernels
-    built from the sources they were taken on."""
+    """Digest of the library's code (comments and whitespace left out);
+    counter readings apply only to kernels built from the code they were
+    taken on."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "sparse_kv_attention_sfi_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(d, f)) as fh:
+                text = fh.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -271,7 +271,7 @@ int32_t sfi_version(void); /* MAJOR * 100 + MINOR */
 typedef enum {
   SFI_K_SLOW_PARTIAL = 0, /* split-K dense partials (+ logit scratch) */
   SFI_K_SLOW_COMBINE = 1, /* split merge + per-position mass */
-  SFI_K_SELECT = 2,       /* Selector (its four kernels together) */
+  SFI_K_SELECT = 2,       /* Selector (all of its kernels of one call together) */
   SFI_K_FAST = 3,         /* sparse attention over support chunks (gather or packed) */
   SFI_K_APPEND = 4,
   SFI_K_PACK = 5,         /* packing of the selected rows */

@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
 }
 
 // ---------------------------------------------------------------------------
-// fast step: gathered sparse attention with a last-workgroup merge
+// fast step: sparse attention over the support in chunks, then a merge kernel
 // ---------------------------------------------------------------------------
 struct SupportGeom {
   int ns_eff, w_lo, w_eff, cnt, size;

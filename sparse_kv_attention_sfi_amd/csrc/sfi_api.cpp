@@ -301,9 +301,10 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
   a.k = desc->k;
   a.v = desc->v;
   a.q = q;
-  a.logits = mass ? reinterpret_cast<float*>(w + L.logits) : nullptr;
-  a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
-  a.part_o = reinterpret_cast<float*>(w + L.part_o);
+  // w is NULL when only the launch table is wanted (sfi_slow_plan)
+  a.logits = (mass && w) ? reinterpret_cast<float*>(w + L.logits) : nullptr;
+  a.part_ml = w ? reinterpret_cast<float*>(w + L.part_ml) : nullptr;
+  a.part_o = w ? reinterpret_cast<float*>(w + L.part_o) : nullptr;
   a.out = out;
   a.mass = mass;
   a.t_cap = desc->kv_capacity;

@@ -1,0 +1,142 @@
+// Host-side checks of the C ABI run under AddressSanitizer and
+// UndefinedBehaviorSanitizer (host code only; nothing here touches a GPU):
+// the scheduler, argument validation of every entry point, workspace sizes,
+// launch-plan queries, status strings and the timing registry.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "sfi.h"
+
+static int g_fail = 0;
+#define CHECK(cond)                                                     \
+  do {                                                                  \
+    if (!(cond)) {                                                      \
+      std::fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #cond); \
+      ++g_fail;                                                         \
+    }                                                                   \
+  } while (0)
+
+static sfi_kv_desc desc(int batch, int hq, int hkv, int d, int dtype, long long cap, const int32_t* ctx) {
+  sfi_kv_desc x;
+  x.batch = batch;
+  x.n_q_heads = hq;
+  x.n_kv_heads = hkv;
+  x.head_dim = d;
+  x.kv_dtype = dtype;
+  x.kv_capacity = cap;
+  x.k = reinterpret_cast<void*>(0x1000);
+  x.v = reinterpret_cast<void*>(0x2000);
+  x.ctx_len_host = ctx;
+  x.scale = 0.f;
+  return x;
+}
+
+static void scheduler() {
+  sfi_sched* s = nullptr;
+  CHECK(sfi_sched_create(3, 42, SFI_SPAN_FIXED, 16.0, 0, &s) == SFI_OK && s != nullptr);
+  std::vector<int32_t> slow(3), fast(3);
+  for (int t = 0; t < 64; ++t) {
+    int32_t ns = -1, nf = -1;
+    CHECK(sfi_sched_step(s, slow.data(), &ns, fast.data(), &nf) == SFI_OK);
+    CHECK(ns + nf == 3);
+    CHECK((t % 16 == 0) == (ns == 3));
+  }
+  CHECK(sfi_sched_force_slow(s, 1) == SFI_OK);
+  CHECK(sfi_sched_force_slow(s, 7) != SFI_OK);
+  sfi_sched_destroy(s);
+  CHECK(sfi_sched_create(64, 7, SFI_SPAN_GEOMETRIC, 18.0, 40, &s) == SFI_OK);
+  std::vector<int32_t> a(64), b(64);
+  long long slow_total = 0;
+  for (int t = 0; t < 20000; ++t) {
+    int32_t ns = 0, nf = 0;
+    CHECK(sfi_sched_step(s, a.data(), &ns, b.data(), &nf) == SFI_OK);
+    slow_total += ns;
+  }
+  CHECK(slow_total > 20000 * 64 / 30 && slow_total < 20000 * 64 / 12);
+  sfi_sched_destroy(s);
+  s = nullptr;
+  CHECK(sfi_sched_create(1, 0, 99, 3.0, 0, &s) != SFI_OK && s == nullptr);
+  CHECK(sfi_sched_create(1, 0, SFI_SPAN_GEOMETRIC, 0.5, 0, &s) != SFI_OK);
+  CHECK(sfi_sched_create(0, 0, SFI_SPAN_FIXED, 4.0, 0, &s) != SFI_OK);
+}
+
+static void validation() {
+  const int32_t ctx1[1] = {100};
+  const int32_t ctx2[2] = {100, 100};
+  const int32_t id0[1] = {0}, id_bad[1] = {1}, ids_dup[2] = {0, 0};
+  void* fake = reinterpret_cast<void*>(0x3000);
+  float* ffake = reinterpret_cast<float*>(0x3000);
+  int32_t* ifake = reinterpret_cast<int32_t*>(0x3000);
+  const sfi_support_params sp = {4, 16, 8, 0.1f}, sp_bad = {4, 16, 8, 1.5f}, sp_empty = {0, 0, 0, 0.1f};
+  const sfi_kv_desc bad[] = {desc(1, 6, 4, 64, SFI_F32, 100, ctx1), desc(1, 24, 2, 64, SFI_F32, 100, ctx1),
+                             desc(1, 8, 2, 96, SFI_F32, 100, ctx1), desc(1, 8, 2, 64, 7, 100, ctx1),
+                             desc(1, 8, 2, 64, SFI_F32, 0, ctx1)};
+  for (const sfi_kv_desc& d : bad) {
+    CHECK(sfi_slow_step(&d, id0, 1, fake, ffake, nullptr, fake, 1u << 30, nullptr) < 0);
+    CHECK(sfi_select(&d, &sp, id0, 1, ffake, ifake, ifake, fake, 1u << 30, nullptr) < 0);
+    CHECK(sfi_fast_step(&d, &sp, id0, 1, fake, ifake, ifake, ffake, fake, 1u << 30, nullptr) < 0);
+    CHECK(sfi_slow_step_select(&d, &sp, id0, 1, fake, ffake, ffake, ifake, ifake, nullptr, nullptr, fake, 1u << 30,
+                               nullptr) < 0);
+    CHECK(sfi_workspace_bytes(&d, &sp, SFI_OP_SLOW) == 0);
+    CHECK(sfi_last_error()[0] != '\0');
+  }
+  const sfi_kv_desc d = desc(1, 8, 2, 64, SFI_F32, 100, ctx1);
+  const sfi_kv_desc d2 = desc(2, 8, 2, 64, SFI_F32, 100, ctx2);
+  CHECK(sfi_slow_step(&d, id_bad, 1, fake, ffake, nullptr, fake, 1u << 30, nullptr) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_slow_step(&d2, ids_dup, 2, fake, ffake, nullptr, fake, 1u << 30, nullptr) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_slow_step(&d, id0, 1, fake, ffake, nullptr, fake, 16, nullptr) == SFI_ERR_WORKSPACE);
+  CHECK(sfi_select(&d, &sp_bad, id0, 1, ffake, ifake, ifake, fake, 1u << 30, nullptr) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_fast_step(&d, &sp_empty, id0, 1, fake, ifake, ifake, ffake, fake, 1u << 30, nullptr) ==
+        SFI_ERR_INVALID_ARG);
+  CHECK(sfi_slow_step_select(&d, &sp, id0, 1, fake, ffake, nullptr, ifake, ifake, nullptr, nullptr, fake,
+                             1u << 30, nullptr) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_slow_step_select(&d, &sp, id0, 1, fake, ffake, ffake, ifake, ifake, fake, nullptr, fake, 1u << 30,
+                             nullptr) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_slow_step_select_async(&d, &sp, id0, 1, fake, ffake, ffake, ifake, ifake, nullptr, nullptr, fake, 8,
+                                   nullptr, fake) == SFI_ERR_WORKSPACE);
+  CHECK(sfi_pack_support(&d, &sp, id0, 1, nullptr, ifake, fake, fake, nullptr) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_kv_append(&d, id0, 1, nullptr, fake, nullptr) == SFI_ERR_INVALID_ARG);
+  const int32_t full[1] = {100};
+  const sfi_kv_desc dfull = desc(1, 8, 2, 64, SFI_F32, 100, full);
+  CHECK(sfi_kv_append(&dfull, id0, 1, fake, fake, nullptr) == SFI_ERR_INVALID_ARG);   // no room
+  CHECK(sfi_debug_support(&d, &sp, id0, 1, ifake, ifake, nullptr, ifake, 8, nullptr) < 0);
+  CHECK(sfi_slow_step(&d, id0, 0, fake, ffake, nullptr, fake, 0, nullptr) == SFI_OK);  // nothing to do
+  for (int op : {SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_OP_SLOW_SELECT}) {
+    const sfi_support_params big = {16, 256, 2048, 0.1f};
+    const sfi_kv_desc small = desc(1, 32, 8, 128, SFI_BF16, 1000, ctx1);
+    const sfi_kv_desc large = desc(1, 32, 8, 128, SFI_BF16, 131072, ctx1);
+    const size_t a = sfi_workspace_bytes(&small, &big, op), b = sfi_workspace_bytes(&large, &big, op);
+    CHECK(a > 0 && a <= b);
+  }
+  CHECK(sfi_workspace_bytes(&d, &sp, 42) == 0);
+  int32_t splits[1] = {-1}, chunks[1] = {-1};
+  CHECK(sfi_slow_plan(&d, id0, 1, splits) == SFI_OK && splits[0] >= 1);
+  CHECK(sfi_fast_plan(&d, &sp, id0, 1, chunks) == SFI_OK && chunks[0] >= 1);
+  CHECK(sfi_slow_plan(&d, id_bad, 1, splits) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_fast_plan(&d, &sp_bad, id0, 1, chunks) == SFI_ERR_INVALID_ARG);
+  setenv("SFI_FAULT_INJECT", "select", 1);
+  CHECK(sfi_select(&d, &sp, id0, 1, ffake, ifake, ifake, fake, 1u << 30, nullptr) == SFI_ERR_INJECTED);
+  unsetenv("SFI_FAULT_INJECT");
+}
+
+static void strings_and_timing() {
+  for (int st : {0, -1, -2, -3, -4, -5, 5})
+    CHECK(sfi_status_str(st) != nullptr && sfi_status_str(st)[0] != '\0');
+  CHECK(sfi_version() == SFI_VERSION_MAJOR * 100 + SFI_VERSION_MINOR);
+  CHECK(sfi_profile_reset() == SFI_OK);
+  double ms = -1.0;
+  long long n = -1;
+  int64_t n64 = -1;
+  CHECK(sfi_profile_read(SFI_K_FAST, &ms, &n64) == SFI_OK && ms == 0.0 && n64 == 0);
+  CHECK(sfi_profile_read(SFI_K_COUNT, &ms, &n64) != SFI_OK);
+  (void)n;
+}
+
+int main() {
+  scheduler();
+  validation();
+  strings_and_timing();
+  if (g_fail == 0) std::printf("host checks passed\n");
+  return g_fail == 0 ? 0 : 1;
+}

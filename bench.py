@@ -108,6 +108,8 @@ def parse():
                    help="layers whose Selector may still run when a later layer's slow step starts (--slow async)")
     p.add_argument("--cold-checks", type=int, default=16,
                    help="calls of the slow and the fast path timed after a 1 GiB cache flush (0: skip)")
+    p.add_argument("--batched-caches", type=int, default=8,
+                   help="independent layer caches cycled per step for single-layer batched workloads (C4)")
     p.add_argument("--batch-check", type=int, default=16, metavar="B",
                    help="also time the fast step for B sequences in one launch (0: skip)")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
@@ -139,9 +141,10 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     S.lib()  # fail loudly when the library is missing
     dev = torch.device("cuda:0")
-    w = {"C1": synth.C1, "C2": synth.C2, "C3": synth.C3, "C4": synth.C4}[args.workload]
-    if w.batch != 1:
-        raise SystemExit("bench.py times batch-1 workloads")
+    w = {"C1": synth.C1, "C2": synth.C2, "C3": synth.C3, "C4": synth.C4, "C5": synth.C5}[args.workload]
+    if w.batch != 1 or w.append:
+        run_batched(args, w, dev)
+        return
     L, K, W = args.layers, args.steps, args.warmup
     n_steps = W + K
 
@@ -284,6 +287,22 @@ def main():
         if n:
             kern[name] = {"launches": n, "avg_us": 1e3 * ms / n}
 
+    # The dense slow step alone (the baseline's kernels, no mass, no Selector):
+    # its partial kernel's bandwidth is the figure the dense decode reaches.
+    dense_kern = {}
+    if kd:
+        S.sfi_profile_reset()
+        S.sfi_profile_enable(True)
+        for t in range(min(8, kd)):
+            q_buf.copy_(q_steps[t])
+            dense_layers()
+        torch.cuda.synchronize()
+        S.sfi_profile_enable(False)
+        for kid, name in S.KERNEL_NAMES.items():
+            ms, n = S.sfi_profile_read(kid)
+            if n:
+                dense_kern[name] = {"launches": n, "avg_us": 1e3 * ms / n}
+
     # Cold-cache check: the same kernels, each call preceded by a 1 GiB read
     # that evicts L2 and the 256 MB last-level cache.  (A read, not a write: a
     # written flush would leave the caches full of dirty lines whose write-back
@@ -385,6 +404,13 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d.get("frac"), "traffic": measured_traffic(dominant, w.name),
                      "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},
+        "roofline_dense_slow_partial": ({"bound": "hbm", "achieved": alg["slow_partial"] / (dense_kern["slow_partial"]["avg_us"] * 1e-6) / 1e9,
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": alg["slow_partial"] / (dense_kern["slow_partial"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                         "alg_bytes_per_launch": alg["slow_partial"],
+                                         "avg_launch_us": dense_kern["slow_partial"]["avg_us"],
+                                         "dense_combine_us": dense_kern.get("slow_combine", {}).get("avg_us")}
+                                        if "slow_partial" in dense_kern else None),
         **{f"roofline_{n}": {"bound": "hbm", "achieved": kern[n]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": kern[n]["frac"], "traffic": measured_traffic(n, w.name),
                              "alg_bytes_per_launch": kern[n]["alg_bytes"], "avg_launch_us": kern[n]["avg_us"]}
@@ -401,6 +427,144 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+    print(json.dumps(result))
+
+
+def run_batched(args, w, dev):
+    """Batched and growing-history workloads (16 sequences with mixed slow and
+    fast steps; 4 sequences over 32 layers with a KV append every step).  The
+    rows that take a slow step change from step to step and, with appends, so
+    do the context lengths baked into every launch, so the loop runs eagerly:
+    per layer one append, one fused refresh for the rows that start a span and
+    one packed fast step for the others, called through the C ABI with
+    prepared arguments.  The dense baseline runs the same loop with a dense
+    step for every row."""
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    import sparse_kv_attention_sfi_amd as S
+    from sparse_kv_attention_sfi_amd import binding as Bd
+    from synth import gen
+
+    lib = S.lib()
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    # layers: the workload's own count, or (single-layer workloads) independent
+    # caches cycled so that no layer's data is still cached at its next step
+    L = w.n_layers if w.n_layers > 1 else max(1, args.batched_caches)
+    K, W = args.steps, args.warmup
+    n_steps = W + K
+    sched = S.Scheduler(B, w.seed, w.span_mode, w.span_param)
+    plan = [sched.step() for _ in range(n_steps)]
+    sched.close()
+    flags = [[b in slow for slow, _ in plan] for b in range(B)]
+    span_ids = [gen.span_ids_from_flags(f) for f in flags]
+    t0 = time.time()
+    kvs, qs, apps = [], [], []
+    for l in range(L):
+        c = gen.build_cache(w, dev, layer=l, n_spans=None)
+        kvs.append(S.KVDesc(c["K"], c["V"], c["ctx_len"], Hq))
+        qs.append(gen.build_queries(w, dev, span_ids, c, layer=l))
+        if w.append:
+            apps.append(gen.append_rows(w, dev, layer=l, n_steps=n_steps))
+        del c
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: {L} layers, batch {B}, ctx {kvs[0].ctx.min()}..{kvs[0].ctx.max()}")
+    ctx0 = [kv.ctx.copy() for kv in kvs]
+    sp = S.support_params(w.n_sink, w.n_recent, w.top_k, w.lam)
+    ws = S.alloc_workspace(kvs[0], sp)
+    ws_ptr, ws_bytes = C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel())
+    out = torch.empty(B, Hq, D, device=dev)
+    mass = torch.empty(B, Hkv, kvs[0].capacity, device=dev)
+    sel = [torch.empty(B, Hkv, w.top_k, dtype=torch.int32, device=dev) for _ in range(L)]
+    cnt = [torch.zeros(B, Hkv, dtype=torch.int32, device=dev) for _ in range(L)]
+    pk = [torch.empty(B, Hkv, w.top_k, D, dtype=kvs[0].dtype, device=dev) for _ in range(L)]
+    pv = [torch.empty_like(pk[0]) for _ in range(L)]
+    esz = kvs[0].k.element_size()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
+    id_cache = {}
+
+    def ids_of(lst):
+        key = tuple(lst)
+        if key not in id_cache:
+            a = np.asarray(lst, dtype=np.int32)
+            id_cache[key] = (a, a.ctypes.data_as(C.POINTER(C.c_int32)), len(lst))
+        return id_cache[key][1:]
+
+    all_ids = ids_of(list(range(B)))
+    lay = [dict(desc=C.byref(kvs[l].desc), q=qs[l].data_ptr(), qstride=qs[l].stride(0) * esz, sel=P(sel[l]),
+                cnt=P(cnt[l]), pk=P(pk[l]), pv=P(pv[l]),
+                kn=apps[l][0].data_ptr() if w.append else 0, vn=apps[l][1].data_ptr() if w.append else 0,
+                astride=apps[l][0].stride(0) * esz if w.append else 0) for l in range(L)]
+    spr, outp, massp = C.byref(sp), P(out), P(mass)
+
+    def ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {lib.sfi_last_error().decode()}")
+
+    def step(t, dense=False):
+        slow, fast = plan[t]
+        if dense:
+            slow, fast = list(range(B)), []
+        for l in range(L):
+            d = lay[l]
+            qp = C.c_void_p(d["q"] + t * d["qstride"])
+            if w.append:
+                ok(lib.sfi_kv_append(d["desc"], all_ids[0], all_ids[1], C.c_void_p(d["kn"] + t * d["astride"]),
+                                     C.c_void_p(d["vn"] + t * d["astride"]), stream), "append")
+                kvs[l].ctx += 1
+            if slow:
+                ip, n = ids_of(slow)
+                if dense:
+                    ok(lib.sfi_slow_step(d["desc"], ip, n, qp, outp, None, ws_ptr, ws_bytes, stream), "dense")
+                else:
+                    ok(lib.sfi_slow_step_select(d["desc"], spr, ip, n, qp, outp, massp, d["sel"], d["cnt"], d["pk"],
+                                                d["pv"], ws_ptr, ws_bytes, stream), "slow")
+            if fast:
+                ip, n = ids_of(fast)
+                ok(lib.sfi_fast_step_packed(d["desc"], spr, ip, n, qp, d["pk"], d["pv"], d["cnt"], outp, ws_ptr,
+                                            ws_bytes, stream), "fast")
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for t in range(W, W + K):
+        step(t)
+    torch.cuda.synchronize()
+    t_sfi = time.perf_counter() - t_start
+    slow_rows = sum(len(plan[t][0]) for t in range(W, W + K))
+    log(f"SFI: {K} steps x {L} layers in {t_sfi * 1e3:.1f} ms ({slow_rows} slow row-steps of {K * B})")
+    # dense baseline: same loop, every row dense (contexts restarted)
+    for l in range(L):
+        kvs[l].ctx[:] = ctx0[l]
+    kd = min(args.dense_steps, n_steps) if args.dense_steps else min(64, n_steps)
+    step(0, dense=True)
+    torch.cuda.synchronize()
+    for l in range(L):
+        kvs[l].ctx[:] = ctx0[l]
+    t_start = time.perf_counter()
+    for t in range(kd):
+        step(t, dense=True)
+    torch.cuda.synchronize()
+    t_dense = time.perf_counter() - t_start
+    value = K * L / t_sfi
+    dense_rate = kd * L / t_dense
+    result = {
+        "metric": METRIC, "value": value, "unit": "decode steps/s/layer", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": 1e3 * t_sfi / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B}, {Hq}q/{Hkv}kv heads, D={D}, ctx {w.ctx_min}..{w.ctx}, "
+                               f"{w.dtype} KV, sinks {w.n_sink}, recent {w.n_recent}, top-k {w.top_k}, "
+                               f"{w.span_mode} spans {w.span_param}, append {w.append}; {L} layers",
+                   "layers": L, "batch": B, "mode": "eager (C ABI calls with prepared arguments)"},
+        "tokens_per_s_layer": value * B,
+        "dense_steps_per_s_layer": dense_rate,
+        "speedup_vs_dense": value / dense_rate,
+        "slow_row_fraction": slow_rows / (K * B),
+    }
     print(json.dumps(result))
 
 
@@ -432,24 +596,31 @@ def fast_batch_check(w, sp, batch, dev, ctx=32768, calls=20):
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    S.sfi_profile_reset()
-    for _ in range(calls):
-        torch.sum(flush, dim=0, out=sink)
-        S.sfi_profile_enable(True)
-        S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out, ws)
-        S.sfi_profile_enable(False)
-        torch.cuda.synchronize()
-    res = {"batch": batch, "ctx": ctx, "calls": calls}
-    for kid, name in S.KERNEL_NAMES.items():
-        ms, n = S.sfi_profile_read(kid)
-        if n:
-            res[name + "_us"] = 1e3 * ms / n
     supp = w.n_sink + w.n_recent + w.top_k
     esz = 2 if w.dtype == "bf16" else 4
     alg = batch * (2 * w.n_kv_heads * supp * w.head_dim * esz + w.n_q_heads * w.head_dim * esz)
-    res["fast_partial_alg_bytes"] = alg
-    res["fast_partial_GBps"] = alg / (res["fast_partial_us"] * 1e-6) / 1e9
-    res["fast_partial_frac"] = res["fast_partial_GBps"] / HBM_PEAK_GBS
+    res = {"batch": batch, "ctx": ctx, "calls": calls}
+    for path in ("packed", "gather"):
+        S.sfi_profile_reset()
+        for _ in range(calls):
+            torch.sum(flush, dim=0, out=sink)
+            S.sfi_profile_enable(True)
+            if path == "packed":
+                S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out, ws)
+            else:
+                S.sfi_fast_step(kv, sp, ids, q, sel, cnt, out, ws)
+            S.sfi_profile_enable(False)
+            torch.cuda.synchronize()
+        r = {}
+        for kid, name in S.KERNEL_NAMES.items():
+            ms, n = S.sfi_profile_read(kid)
+            if n:
+                r[name + "_us"] = 1e3 * ms / n
+        a = alg + (batch * 4 * w.n_kv_heads * w.top_k if path == "gather" else 0)
+        r["fast_partial_alg_bytes"] = a
+        r["fast_partial_GBps"] = a / (r["fast_partial_us"] * 1e-6) / 1e9
+        r["fast_partial_frac"] = r["fast_partial_GBps"] / HBM_PEAK_GBS
+        res[path] = r
     del K, V, kv, flush
     torch.cuda.empty_cache()
     return res

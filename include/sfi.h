@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define SFI_VERSION_MAJOR 0
-#define SFI_VERSION_MINOR 1
+#define SFI_VERSION_MINOR 2
 
 typedef enum {
   SFI_OK = 0,

@@ -237,7 +237,9 @@ thread_local LaunchTiming* g_timing = nullptr;
 
 // Per-thread events that order work across two streams (timing disabled).  A
 // wait binds to the record that precedes it, so one event per role can be
-// re-recorded by every call.
+// re-recorded by every call.  They live until the process ends: destroying
+// them from a thread-exit destructor could run after the HIP runtime has shut
+// down.
 bool stream_event(int role, hipEvent_t* out) {
   thread_local hipEvent_t ev[2] = {nullptr, nullptr};
   if (ev[role] == nullptr && hipEventCreateWithFlags(&ev[role], hipEventDisableTiming) != hipSuccess) {

@@ -265,3 +265,42 @@ def test_more_rows_than_one_launch_group():
         sels = [b["sel"][r, g, :c_[g]].cpu().numpy().astype(np.int64) for g in range(2)]
         ref = O.fast_step(np64(q[r]), np64(kv.k[r, :, :T]), np64(kv.v[r, :, :T]), T, 4, 32, sels)
         assert np.max(np.abs(np64(out_p[r]) - ref)) < OUT_TOL
+
+
+def test_refresh_and_fast_rows_on_two_streams():
+    """A layer's refresh rows and fast rows touch disjoint rows of every
+    output: the fused refresh on one stream and the packed fast step on
+    another, each with its own workspace and running side by side, give the
+    serial results bit for bit, over several decode steps that alternate which
+    rows refresh."""
+    ctx = [6000, 3000, 9000, 700, 5000, 8000]
+    B = len(ctx)
+    kv, q = random_cache(B, 32, 8, 9000, 128, torch.bfloat16, ctx, seed=88, q_scale=2.0)
+    sp = S.support_params(16, 256, 512, 0.1)
+    qs = [q] + [(2 * torch.randn_like(q.float())).to(q.dtype) for _ in range(3)]
+    plan = [(list(range(B)), []), ([1, 4], [0, 2, 3, 5]), ([0, 2, 3], [1, 4, 5]), ([5], [0, 1, 2, 3, 4])]
+
+    def run(two_streams):
+        ws, ws2 = S.alloc_workspace(kv, sp), S.alloc_workspace(kv, sp)
+        o = _outputs(kv, sp, True)
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        outs = []
+        torch.cuda.synchronize()
+        for qt, (slow, fast) in zip(qs, plan):
+            fork = two_streams and slow and fast
+            if fork:
+                side.wait_stream(main)
+            S.sfi_slow_step_select(kv, sp, slow, qt, o["out"], o["mass"], o["sel"], o["cnt"], o["pk"], o["pv"],
+                                   ws2 if fork else ws, side if fork else main)
+            if fast:
+                S.sfi_fast_step_packed(kv, sp, fast, qt, o["pk"], o["pv"], o["cnt"], o["out"], ws, main)
+            if fork:
+                main.wait_stream(side)
+            outs.append({key: v.clone() for key, v in o.items()})
+        torch.cuda.synchronize()
+        return outs
+
+    serial, forked = run(False), run(True)
+    for t, (a, b) in enumerate(zip(serial, forked)):
+        for key in a:
+            assert torch.equal(a[key], b[key]), (t, key)

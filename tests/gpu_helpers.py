@@ -52,6 +52,14 @@ def oracle_slow(kv, q, b):
     return out, O.group_mass(P, kv.n_kv_heads)
 
 
+def check_mass(f, f_ref, where=""):
+    """Mass parity per KV-head row: max-abs error within MASS_REL_TOL of that
+    row's largest oracle mass, and each row sums to 1 within MASS_SUM_TOL."""
+    err = np.abs(f - f_ref).max(axis=1)
+    assert np.all(err <= MASS_REL_TOL * f_ref.max(axis=1)), (where, err, f_ref.max(axis=1))
+    assert np.all(np.abs(f.sum(axis=1) - 1.0) < MASS_SUM_TOL), (where, f.sum(axis=1))
+
+
 def check_support(gpu_sel, f_row, T, ns, W, k, lam, where=""):
     """Support parity: exact when the oracle's k-th / (k+1)-th scores are
     separated by more than GAP_REL relative, tie-tolerant otherwise."""

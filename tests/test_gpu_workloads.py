@@ -12,7 +12,7 @@ import oracle as O
 import sparse_kv_attention_sfi_amd as S
 import synth
 from synth import gen
-from tests.gpu_helpers import MASS_REL_TOL, MASS_SUM_TOL, OUT_TOL, check_support, np64
+from tests.gpu_helpers import MASS_SUM_TOL, OUT_TOL, check_mass, check_support, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +83,7 @@ def _check_slow(r, b, q_b, K64, V64, T):
     o_ref, P = O.dense_attention(q_b, K64[:, :T], V64[:, :T])
     f_ref = O.group_mass(P, w.n_kv_heads)
     assert np.max(np.abs(np64(r.out[b]) - o_ref)) < OUT_TOL
-    f = np64(r.mass[b, :, :T])
-    assert np.max(np.abs(f - f_ref)) <= MASS_REL_TOL * f_ref.max()
-    assert np.max(np.abs(f.sum(axis=1) - 1.0)) < MASS_SUM_TOL
+    check_mass(np64(r.mass[b, :, :T]), f_ref, b)
     kinds = [check_support(s, f_ref[g], T, w.n_sink, w.n_recent, w.top_k, w.lam, f"b{b} g{g}")
              for g, s in enumerate(r.gpu_sel(b))]
     return f_ref, kinds

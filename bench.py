@@ -393,6 +393,8 @@ def main():
                    "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode, "fast_path": args.fast,
                    "slow_path": args.slow,
                    "slow_steps_timed": n_slow_timed},
+        "slow_step_us": slow_us or None,
+        "fast_step_us": fast_us or None,
         "slow_steps_per_s_layer": 1e6 / slow_us if slow_us else None,
         "fast_steps_per_s_layer": 1e6 / fast_us if fast_us else None,
         "blended_steps_per_s_layer": value,

@@ -39,6 +39,10 @@
  *    [0, B)) are read or written by a call.
  *  - Arrays with a top_k extent (sel_idx, packed_k, packed_v) may be NULL
  *    when top_k = 0.
+ *  - Alignment: K, V, q, k_new, v_new, out, mass, packed_k, packed_v and the
+ *    workspace start on a 16-byte boundary, the int32 arrays on a 4-byte
+ *    one (fresh allocations and whole-row views of them do).  A misaligned
+ *    buffer fails validation with SFI_ERR_INVALID_ARG.
  *  - Supported shapes: head_dim 64 or 128; Hq / Hkv in {1, 2, 4, 8};
  *    kv_dtype SFI_F32 or SFI_BF16; 1 <= ctx_len[b] <= kv_capacity.
  */

@@ -6,11 +6,14 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "sfi_internal.hpp"
@@ -75,10 +78,23 @@ int32_t check_desc(const sfi_kv_desc* d) {
   return SFI_OK;
 }
 
+// The kernels move K, V, q, the float outputs, the packed rows and the
+// workspace in 16-byte vectors and the int32 arrays in 4-byte words, so each
+// buffer must start on that boundary (NULL entries are not checked here).
+constexpr size_t kVecAlign = 16;
+constexpr size_t kIntAlign = 4;
+
+int32_t check_aligned(std::initializer_list<std::pair<const void*, const char*>> bufs, size_t align) {
+  for (const auto& [p, name] : bufs)
+    if (p != nullptr && reinterpret_cast<uintptr_t>(p) % align != 0)
+      return fail(SFI_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return SFI_OK;
+}
+
 int32_t check_kv(const sfi_kv_desc* d) {
   if (d->k == nullptr || d->v == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->k / desc->v is NULL");
   if (d->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
-  return SFI_OK;
+  return check_aligned({{d->k, "desc->k"}, {d->v, "desc->v"}}, kVecAlign);
 }
 
 int32_t check_seqs(const sfi_kv_desc* d, const int32_t* ids, int32_t n, bool need_ctx, int32_t min_ctx,
@@ -205,7 +221,7 @@ int32_t check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return SFI_OK;
   if (ws == nullptr) return fail(SFI_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (have < need) return fail(SFI_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
-  return SFI_OK;
+  return check_aligned({{ws, "workspace"}}, kVecAlign);
 }
 
 // ---- event timing ---------------------------------------------------------
@@ -453,6 +469,7 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp
 
 int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (ws == nullptr || ws_bytes == 0) return SFI_OK;
+  if (const int32_t st = check_aligned({{ws, "workspace"}}, kVecAlign); st != SFI_OK) return st;
   const hipError_t e = launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SFI_OK : hip_fail(e, "workspace init");
 }
@@ -465,6 +482,7 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
   if (n_seq == 0) return SFI_OK;
   if (q == nullptr || out == nullptr) return fail(SFI_ERR_INVALID_ARG, "q / out is NULL");
+  if ((st = check_aligned({{q, "q"}, {out, "out"}, {mass, "mass"}}, kVecAlign)) != SFI_OK) return st;
   if ((st = check_ws(ws, ws_bytes, slow_layout(desc).end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -520,6 +538,8 @@ int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const 
   if (n_seq == 0) return SFI_OK;
   if (mass == nullptr || sel_cnt == nullptr || (sel_idx == nullptr && sp->top_k > 0))
     return fail(SFI_ERR_INVALID_ARG, "mass / sel_idx / sel_cnt is NULL");
+  if ((st = check_aligned({{mass, "mass"}}, kVecAlign)) != SFI_OK) return st;
+  if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}}, kIntAlign)) != SFI_OK) return st;
   if ((st = check_ws(ws, ws_bytes, select_layout(desc).end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -550,6 +570,10 @@ static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_
     return fail(SFI_ERR_INVALID_ARG, "q / out / mass / sel_idx / sel_cnt is NULL");
   if ((packed_k == nullptr) != (packed_v == nullptr))
     return fail(SFI_ERR_INVALID_ARG, "packed_k and packed_v must both be given or both be NULL");
+  if ((st = check_aligned({{q, "q"}, {out, "out"}, {mass, "mass"}, {packed_k, "packed_k"}, {packed_v, "packed_v"}},
+                          kVecAlign)) != SFI_OK)
+    return st;
+  if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}}, kIntAlign)) != SFI_OK) return st;
   if ((st = check_ws(ws, ws_bytes, std::max(slow_layout(desc).end, select_layout(desc).end))) != SFI_OK) return st;
   const bool split = sel_s != s;
   hipEvent_t ev_slow = nullptr, ev_sel = nullptr;
@@ -631,6 +655,10 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
     return fail(SFI_ERR_INVALID_ARG, "sel_idx (or packed_k / packed_v) is NULL");
   if (sp->n_sink == 0 && sp->n_recent == 0 && sp->top_k == 0)
     return fail(SFI_ERR_INVALID_ARG, "the support is empty (n_sink = n_recent = top_k = 0)");
+  if ((st = check_aligned({{q, "q"}, {out, "out"}, {packed_k, "packed_k"}, {packed_v, "packed_v"}}, kVecAlign)) !=
+      SFI_OK)
+    return st;
+  if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}}, kIntAlign)) != SFI_OK) return st;
   const int crow = fast_chunk_rows();
   if (static_cast<int64_t>(sp->n_sink) + sp->n_recent + sp->top_k > static_cast<int64_t>(crow) * kMaxMergeSlots)
     return fail(SFI_ERR_UNSUPPORTED, "support of %lld rows exceeds %d",
@@ -706,6 +734,8 @@ int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp, 
   if (n_seq == 0 || sp->top_k == 0) return SFI_OK;
   if (sel_idx == nullptr || sel_cnt == nullptr || packed_k == nullptr || packed_v == nullptr)
     return fail(SFI_ERR_INVALID_ARG, "sel_idx / sel_cnt / packed_k / packed_v is NULL");
+  if ((st = check_aligned({{packed_k, "packed_k"}, {packed_v, "packed_v"}}, kVecAlign)) != SFI_OK) return st;
+  if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}}, kIntAlign)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     PackArgs a{};
@@ -745,6 +775,7 @@ int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   if ((st = check_seqs(desc, seq_ids, n_seq, true, 0, desc->kv_capacity - 1)) != SFI_OK) return st;
   if (n_seq == 0) return SFI_OK;
   if (k_new == nullptr || v_new == nullptr) return fail(SFI_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  if ((st = check_aligned({{k_new, "k_new"}, {v_new, "v_new"}}, kVecAlign)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     AppendArgs a{};
@@ -781,6 +812,9 @@ int32_t sfi_debug_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
   if (sel_idx == nullptr || sel_cnt == nullptr || support_out == nullptr || support_cnt == nullptr)
     return fail(SFI_ERR_INVALID_ARG, "NULL buffer");
   if (cap_per_head < 1) return fail(SFI_ERR_INVALID_ARG, "cap_per_head must be >= 1");
+  if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}, {support_out, "support_out"},
+                           {support_cnt, "support_cnt"}}, kIntAlign)) != SFI_OK)
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SupportArgs a{};

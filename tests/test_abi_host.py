@@ -134,6 +134,42 @@ def test_validation_rejects_before_launch():
                  None) == B.SFI_ERR_WORKSPACE
 
 
+def test_misaligned_buffers_rejected_before_launch():
+    """Every entry point rejects a buffer off its 16-byte (int32 arrays:
+    4-byte) boundary before it enqueues anything; the error names it."""
+    lib = S.lib()
+    ids = np.zeros(1, dtype=np.int32)
+    pid = ids.ctypes.data_as(C.POINTER(C.c_int32))
+    a = C.c_void_p(0x3000)                  # aligned fake device address
+    m8, m2 = C.c_void_p(0x3008), C.c_void_p(0x3002)
+    desc, keep = _desc()
+    sp = B.sfi_support_params(4, 16, 8, 0.1)
+    big = 1 << 40
+    calls = {
+        "q": lambda: lib.sfi_slow_step(C.byref(desc), pid, 1, m8, a, None, a, big, None),
+        "mass": lambda: lib.sfi_select(C.byref(desc), C.byref(sp), pid, 1, m8, a, a, a, big, None),
+        "sel_idx": lambda: lib.sfi_select(C.byref(desc), C.byref(sp), pid, 1, a, m2, a, a, big, None),
+        "packed_k": lambda: lib.sfi_slow_step_select(C.byref(desc), C.byref(sp), pid, 1, a, a, a, a, a, m8, a, a,
+                                                     big, None),
+        "out": lambda: lib.sfi_fast_step(C.byref(desc), C.byref(sp), pid, 1, a, a, a, m8, a, big, None),
+        "packed_v": lambda: lib.sfi_fast_step_packed(C.byref(desc), C.byref(sp), pid, 1, a, a, m8, a, a, a, big,
+                                                     None),
+        "sel_cnt": lambda: lib.sfi_pack_support(C.byref(desc), C.byref(sp), pid, 1, a, m2, a, a, None),
+        "k_new": lambda: lib.sfi_kv_append(C.byref(_desc(ctx=(99,))[0]), pid, 1, m8, a, None),
+        "support_out": lambda: lib.sfi_debug_support(C.byref(desc), C.byref(sp), pid, 1, a, a, m2, a, 64, None),
+        "workspace": lambda: lib.sfi_slow_step(C.byref(desc), pid, 1, a, a, None, m8, big, None),
+    }
+    for name, call in calls.items():
+        assert call() == B.SFI_ERR_INVALID_ARG, name
+        err = lib.sfi_last_error().decode()
+        assert name in err and "aligned" in err, (name, err)
+    assert lib.sfi_workspace_init(m8, 4096, None) == B.SFI_ERR_INVALID_ARG
+    kd, keep2 = _desc()
+    kd.k = 0x1004
+    assert lib.sfi_slow_step(C.byref(kd), pid, 1, a, a, None, a, big, None) == B.SFI_ERR_INVALID_ARG
+    assert b"desc->k" in lib.sfi_last_error()
+
+
 def test_fault_injection_fails_select_before_launch(monkeypatch):
     monkeypatch.setenv("SFI_FAULT_INJECT", "select")
     desc, keep = _desc()

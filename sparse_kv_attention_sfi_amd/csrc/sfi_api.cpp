@@ -251,18 +251,24 @@ hipEvent_t take_event(Prof& p) {
 
 thread_local LaunchTiming* g_timing = nullptr;
 
-// Per-thread events that order work across two streams (timing disabled).  A
-// wait binds to the record that precedes it, so one event per role can be
-// re-recorded by every call.  They live until the process ends: destroying
-// them from a thread-exit destructor could run after the HIP runtime has shut
-// down.
+// Per-thread, per-device events that order work across two streams (timing
+// disabled; an event is created on the device current at the call, the device
+// of the caller's streams).  A wait binds to the record that precedes it, so
+// one event per role can be re-recorded by every call.  They live until the
+// process ends: destroying them from a thread-exit destructor could run after
+// the HIP runtime has shut down.
+constexpr int kMaxDevices = 64;
+
 bool stream_event(int role, hipEvent_t* out) {
-  thread_local hipEvent_t ev[2] = {nullptr, nullptr};
-  if (ev[role] == nullptr && hipEventCreateWithFlags(&ev[role], hipEventDisableTiming) != hipSuccess) {
-    ev[role] = nullptr;
+  thread_local hipEvent_t ev[kMaxDevices][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  hipEvent_t& e = ev[dev][role];
+  if (e == nullptr && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+    e = nullptr;
     return false;
   }
-  *out = ev[role];
+  *out = e;
   return true;
 }
 
@@ -346,14 +352,14 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
   for (int i = 0; i < cnt; ++i) {
     const int b = ids[i];
     const int T = desc->ctx_len_host[b];
-    a.tab.seq[i] = b;
-    a.tab.ctx[i] = T;
-    a.tab.nsplit[i] = static_cast<int32_t>(ceil_div(T, a.split_rows));
-    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+    a.tab.ent[i].seq = b;
+    a.tab.ent[i].ctx = T;
+    a.tab.ent[i].nsplit = static_cast<int32_t>(ceil_div(T, a.split_rows));
+    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
     c.mass_blocks[i] = mass ? static_cast<int32_t>(ceil_div(T, kMassChunk)) : 0;
-    c.tab.seq[i] = b;
-    c.tab.ctx[i] = T;
-    c.tab.nsplit[i] = a.tab.nsplit[i];
+    c.tab.ent[i].seq = b;
+    c.tab.ent[i].ctx = T;
+    c.tab.ent[i].nsplit = a.tab.ent[i].nsplit;
     c.tab.wg_begin[i + 1] = c.tab.wg_begin[i] + desc->n_kv_heads * (c.mass_blocks[i] + G);
   }
   c.logits = a.logits;
@@ -411,10 +417,10 @@ void plan_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const in
     const int64_t n = std::max<int64_t>(0, T - sp->n_sink - sp->n_recent);
     const bool keep_all = n <= sp->top_k || sp->top_k == 0;
     const int64_t M = keep_all ? std::max<int64_t>(1, ceil_div(sp->top_k, chunk)) : ceil_div(n, chunk);
-    a.tab.seq[i] = ids[i];
-    a.tab.ctx[i] = static_cast<int32_t>(T);
-    a.tab.nsplit[i] = static_cast<int32_t>(M);
-    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+    a.tab.ent[i].seq = ids[i];
+    a.tab.ent[i].ctx = static_cast<int32_t>(T);
+    a.tab.ent[i].nsplit = static_cast<int32_t>(M);
+    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
   }
 }
 
@@ -506,7 +512,7 @@ int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
     SlowArgs a{};
     CombineArgs c{};
     plan_slow(desc, ids, cnt, nullptr, nullptr, nullptr, nullptr, a, c);
-    for (int i = 0; i < cnt; ++i) splits[done + i] = a.tab.nsplit[i];
+    for (int i = 0; i < cnt; ++i) splits[done + i] = a.tab.ent[i].nsplit;
     done += cnt;
     return SFI_OK;
   });
@@ -693,10 +699,10 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
     a.tab.wg_begin[0] = 0;
     for (int i = 0; i < cnt; ++i) {
       const int b = ids[i];
-      a.tab.seq[i] = b;
-      a.tab.ctx[i] = desc->ctx_len_host[b];
-      a.tab.nsplit[i] = fast_chunks(sp, desc->ctx_len_host[b], crow);
-      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+      a.tab.ent[i].seq = b;
+      a.tab.ent[i].ctx = desc->ctx_len_host[b];
+      a.tab.ent[i].nsplit = fast_chunks(sp, desc->ctx_len_host[b], crow);
+      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
     }
     hipError_t e = timed(SFI_K_FAST, s, [&] {
       return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
@@ -755,10 +761,10 @@ int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp, 
     for (int i = 0; i < cnt; ++i) {
       const int64_t t = desc->ctx_len_host[ids[i]];
       const int64_t kmax = std::min<int64_t>(sp->top_k, std::max<int64_t>(0, t - sp->n_sink - sp->n_recent));
-      a.tab.seq[i] = ids[i];
-      a.tab.ctx[i] = static_cast<int32_t>(t);
-      a.tab.nsplit[i] = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(kmax, kPackRows)));
-      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.nsplit[i];
+      a.tab.ent[i].seq = ids[i];
+      a.tab.ent[i].ctx = static_cast<int32_t>(t);
+      a.tab.ent[i].nsplit = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(kmax, kPackRows)));
+      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
     }
     const hipError_t e = timed(SFI_K_PACK, s, [&] {
       return launch_pack(a, desc->kv_dtype, desc->head_dim, a.tab.wg_begin[cnt], s);
@@ -787,9 +793,9 @@ int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
     a.n_kv_heads = desc->n_kv_heads;
     a.tab.n = cnt;
     for (int i = 0; i < cnt; ++i) {
-      a.tab.seq[i] = ids[i];
-      a.tab.ctx[i] = desc->ctx_len_host[ids[i]];
-      a.tab.nsplit[i] = 1;
+      a.tab.ent[i].seq = ids[i];
+      a.tab.ent[i].ctx = desc->ctx_len_host[ids[i]];
+      a.tab.ent[i].nsplit = 1;
       a.tab.wg_begin[i] = i * desc->n_kv_heads;
     }
     a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;
@@ -830,9 +836,9 @@ int32_t sfi_debug_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
     a.cap_per_head = cap_per_head;
     a.tab.n = cnt;
     for (int i = 0; i < cnt; ++i) {
-      a.tab.seq[i] = ids[i];
-      a.tab.ctx[i] = desc->ctx_len_host[ids[i]];
-      a.tab.nsplit[i] = 1;
+      a.tab.ent[i].seq = ids[i];
+      a.tab.ent[i].ctx = desc->ctx_len_host[ids[i]];
+      a.tab.ent[i].nsplit = 1;
       a.tab.wg_begin[i] = i * desc->n_kv_heads;
     }
     a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;

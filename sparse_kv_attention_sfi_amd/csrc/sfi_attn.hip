@@ -392,11 +392,11 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   const int wg = blockIdx.x;
   const int e = find_entry(a.tab, wg);
   const int local = wg - a.tab.wg_begin[e];
-  const int nsplit = a.tab.nsplit[e];
+  const int nsplit = a.tab.ent[e].nsplit;
   const int g = local / nsplit;
   const int split = local - g * nsplit;
-  const int b = a.tab.seq[e];
-  const int T = a.tab.ctx[e];
+  const int b = a.tab.ent[e].seq;
+  const int T = a.tab.ent[e].ctx;
   const int r_begin = split * a.split_rows;
   const int r_end = min(T, r_begin + a.split_rows);
   if (a.clear_hist != nullptr && split == 0) {
@@ -636,9 +636,9 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
   const int per_g = mblocks + G;
   const int g = local / per_g;
   const int r = local - g * per_g;
-  const int b = a.tab.seq[e];
-  const int T = a.tab.ctx[e];
-  const int nsplit = a.tab.nsplit[e];
+  const int b = a.tab.ent[e].seq;
+  const int T = a.tab.ent[e].ctx;
+  const int nsplit = a.tab.ent[e].nsplit;
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
   const int64_t ml_hstride = static_cast<int64_t>(a.part_stride) * 2;
   const float* ml = a.part_ml + qh0 * ml_hstride;
@@ -749,7 +749,7 @@ __device__ __forceinline__ int support_pos(const SupportGeom& s, int p, int t,
   return -1;
 }
 
-template <typename E, int D, int G, int TILES>
+template <typename E, int D, int G, int TILES, bool ONE>
 __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
@@ -765,13 +765,15 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
-  const int e = find_entry(a.tab, wg);
-  const int local = wg - a.tab.wg_begin[e];
-  const int nchunk = a.tab.nsplit[e];
+  // ONE: a one-row launch, whose entry sits at fixed kernel-argument offsets
+  // that load with the other arguments (no table search)
+  const int e = ONE ? 0 : find_entry(a.tab, wg);
+  const int local = ONE ? wg : wg - a.tab.wg_begin[e];
+  const int nchunk = a.tab.ent[e].nsplit;
   const int g = local / nchunk;
   const int chunk = local - g * nchunk;
-  const int b = a.tab.seq[e];
-  const int t = a.tab.ctx[e];
+  const int b = a.tab.ent[e].seq;
+  const int t = a.tab.ent[e].ctx;
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const SupportGeom sg = support_geom(t, a.n_sink, a.n_recent, a.top_k, a.sel_cnt, bg);
   const int32_t* sel_row = a.sel_idx + bg * a.top_k;
@@ -832,7 +834,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
 // read from the cache.  Every row address follows from host-known lengths,
 // so all K/V loads are issued at once with no index lookups; only the end of
 // the selected rows (sel_cnt) masks the tail.
-template <typename E, int D, int G, int TILES>
+template <typename E, int D, int G, int TILES, bool ONE>
 __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
@@ -846,13 +848,13 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
-  const int e = find_entry(a.tab, wg);
-  const int local = wg - a.tab.wg_begin[e];
-  const int nchunk = a.tab.nsplit[e];
+  const int e = ONE ? 0 : find_entry(a.tab, wg);
+  const int local = ONE ? wg : wg - a.tab.wg_begin[e];
+  const int nchunk = a.tab.ent[e].nsplit;
   const int g = local / nchunk;
   const int chunk = local - g * nchunk;
-  const int b = a.tab.seq[e];
-  const int t = a.tab.ctx[e];
+  const int b = a.tab.ent[e].seq;
+  const int t = a.tab.ent[e].ctx;
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const int ns_eff = min(a.n_sink, t);
   const int w_lo = max(a.n_sink, t - a.n_recent);
@@ -925,11 +927,11 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   const int wg = blockIdx.x;
   const int e = find_entry(a.tab, wg);
   const int local = wg - a.tab.wg_begin[e];
-  const int nchunk = a.tab.nsplit[e];
+  const int nchunk = a.tab.ent[e].nsplit;
   const int g = local / nchunk;
   const int chunk = local - g * nchunk;
-  const int b = a.tab.seq[e];
-  const int t = a.tab.ctx[e];
+  const int b = a.tab.ent[e].seq;
+  const int t = a.tab.ent[e].ctx;
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const int kmax = min(a.top_k, max(0, t - a.n_sink - a.n_recent));
   const int cnt = min(max(a.sel_cnt[bg], 0), kmax);
@@ -973,13 +975,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 
 // Merge of the chunk partials of one (sequence, KV head): the output of its G
 // query heads, renormalised over the whole support.
-template <int D, int G>
+template <int D, int G, bool ONE>
 __global__ __launch_bounds__(kMergeThreads) void fast_merge_kernel(FastArgs a) {
   __shared__ MergeSmem<G, kMergeThreads> s_merge;
-  const int e = blockIdx.x / a.n_kv_heads;
-  const int g = blockIdx.x - e * a.n_kv_heads;
-  const int b = a.tab.seq[e];
-  const int nchunk = a.tab.nsplit[e];
+  const int e = ONE ? 0 : blockIdx.x / a.n_kv_heads;
+  const int g = ONE ? blockIdx.x : blockIdx.x - e * a.n_kv_heads;
+  const int b = a.tab.ent[e].seq;
+  const int nchunk = a.tab.ent[e].nsplit;
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
   const int64_t ml_hstride = static_cast<int64_t>(a.part_stride) * 2;
   merge_partials<D, G, kMergeThreads>(a.part_ml + qh0 * ml_hstride, ml_hstride, a.part_o + qh0 * a.part_stride * D,
@@ -992,8 +994,8 @@ __global__ __launch_bounds__(kMergeThreads) void fast_merge_kernel(FastArgs a) {
 __global__ __launch_bounds__(256) void support_kernel(SupportArgs a) {
   const int e = blockIdx.x / a.n_kv_heads;
   const int g = blockIdx.x - e * a.n_kv_heads;
-  const int b = a.tab.seq[e];
-  const int t = a.tab.ctx[e];
+  const int b = a.tab.ent[e].seq;
+  const int t = a.tab.ent[e].ctx;
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const SupportGeom sg = support_geom(t, a.n_sink, a.n_recent, a.top_k, a.sel_cnt, bg);
   const int32_t* sel_row = a.sel_idx + bg * a.top_k;
@@ -1010,8 +1012,8 @@ template <int RB>
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int e = blockIdx.x / a.n_kv_heads;
   const int g = blockIdx.x - e * a.n_kv_heads;
-  const int b = a.tab.seq[e];
-  const int t = a.tab.ctx[e];
+  const int b = a.tab.ent[e].seq;
+  const int t = a.tab.ent[e].ctx;
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   constexpr int NP = RB / 16;
   for (int i = threadIdx.x; i < 2 * NP; i += 64) {
@@ -1090,10 +1092,13 @@ int fast_chunk_rows() { return (kFastThreads / 64) * fast_tiles() * 16; }
 
 template <typename E, int D, int G, int TILES>
 static void fast_partial_launch(const FastArgs& a, int grid, hipStream_t s) {
+  const bool one = a.tab.n == 1;
   if (a.packed_k != nullptr) {
-    launch(fast_packed_kernel<E, D, G, TILES>, grid, kFastThreads, s, a);
+    if (one) launch(fast_packed_kernel<E, D, G, TILES, true>, grid, kFastThreads, s, a);
+    else launch(fast_packed_kernel<E, D, G, TILES, false>, grid, kFastThreads, s, a);
   } else {
-    launch(fast_partial_kernel<E, D, G, TILES>, grid, kFastThreads, s, a);
+    if (one) launch(fast_partial_kernel<E, D, G, TILES, true>, grid, kFastThreads, s, a);
+    else launch(fast_partial_kernel<E, D, G, TILES, false>, grid, kFastThreads, s, a);
   }
 }
 
@@ -1128,17 +1133,22 @@ hipError_t launch_fast_partial(const FastArgs& a, int dtype, int head_dim, int g
                          : fast_partial_g<F32, 64>(a, group, grid, s);
 }
 
-template <int D>
-static hipError_t fast_merge_g(const FastArgs& a, int group, hipStream_t s) {
+template <int D, bool ONE>
+static hipError_t fast_merge_one(const FastArgs& a, int group, hipStream_t s) {
   const int grid = a.tab.n * a.n_kv_heads;
   switch (group) {
-    case 1: launch(fast_merge_kernel<D, 1>, grid, kMergeThreads, s, a); break;
-    case 2: launch(fast_merge_kernel<D, 2>, grid, kMergeThreads, s, a); break;
-    case 4: launch(fast_merge_kernel<D, 4>, grid, kMergeThreads, s, a); break;
-    case 8: launch(fast_merge_kernel<D, 8>, grid, kMergeThreads, s, a); break;
+    case 1: launch(fast_merge_kernel<D, 1, ONE>, grid, kMergeThreads, s, a); break;
+    case 2: launch(fast_merge_kernel<D, 2, ONE>, grid, kMergeThreads, s, a); break;
+    case 4: launch(fast_merge_kernel<D, 4, ONE>, grid, kMergeThreads, s, a); break;
+    case 8: launch(fast_merge_kernel<D, 8, ONE>, grid, kMergeThreads, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t fast_merge_g(const FastArgs& a, int group, hipStream_t s) {
+  return a.tab.n == 1 ? fast_merge_one<D, true>(a, group, s) : fast_merge_one<D, false>(a, group, s);
 }
 
 hipError_t launch_fast_merge(const FastArgs& a, int head_dim, int group, hipStream_t s) {

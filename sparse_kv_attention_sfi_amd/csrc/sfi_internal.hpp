@@ -27,12 +27,20 @@ constexpr int kMergeThreads = 1024;  // fast-step chunk merge
 constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a merge accepts
 constexpr int kSlowTargetWgs = 1024;  // slow partial workgroups aimed at per launch
 
+// One launch's rows.  A row's fields sit together in one 16-byte record, so
+// a workgroup fetches them with one scalar load.
+struct SeqEntry {
+  int32_t seq;     // batch row
+  int32_t ctx;     // context length T_b
+  int32_t nsplit;  // workgroups per KV head of this row
+  int32_t pad;
+};
+
 struct SeqTable {
-  int32_t n;                              // entries used
-  int32_t seq[kMaxSeqPerLaunch];          // batch row
-  int32_t ctx[kMaxSeqPerLaunch];          // context length T_b
-  int32_t nsplit[kMaxSeqPerLaunch];       // workgroups per KV head of this row
-  int32_t wg_begin[kMaxSeqPerLaunch + 1]; // prefix over entries of Hkv * nsplit
+  int32_t n;  // entries used
+  int32_t pad[3];
+  SeqEntry ent[kMaxSeqPerLaunch];
+  int32_t wg_begin[kMaxSeqPerLaunch + 1];  // prefix over entries of Hkv * nsplit
 };
 
 // ---- slow step -----------------------------------------------------------

@@ -73,11 +73,11 @@ __device__ __forceinline__ HeadCtx head_ctx(const SelectArgs& a) {
   const int wg = blockIdx.x;
   h.e = find_entry(a.tab, wg);
   const int local = wg - a.tab.wg_begin[h.e];
-  h.M = a.tab.nsplit[h.e];
+  h.M = a.tab.ent[h.e].nsplit;
   h.g = local / h.M;
   h.c = local - h.g * h.M;
-  h.b = a.tab.seq[h.e];
-  h.T = a.tab.ctx[h.e];
+  h.b = a.tab.ent[h.e].seq;
+  h.T = a.tab.ent[h.e].ctx;
   h.bg = static_cast<int64_t>(h.b) * a.n_kv_heads + h.g;
   h.n = max(0, h.T - a.n_recent - a.n_sink);
   h.keep_all = h.n <= a.top_k || a.top_k == 0;
@@ -212,7 +212,7 @@ __device__ uint64_t radix_resolve(Src src, int count, int match, uint64_t prefix
 __global__ __launch_bounds__(256) void select_clear_kernel(SelectArgs a) {
   const int e = blockIdx.x / a.n_kv_heads;
   const int g = blockIdx.x - e * a.n_kv_heads;
-  const int64_t bg = static_cast<int64_t>(a.tab.seq[e]) * a.n_kv_heads + g;
+  const int64_t bg = static_cast<int64_t>(a.tab.ent[e].seq) * a.n_kv_heads + g;
   uint4* h4 = reinterpret_cast<uint4*>(a.hist + bg * kSelBins);
   for (int i = threadIdx.x; i < kSelBins / 4; i += 256) h4[i] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x == 0) a.list_n[bg] = 0;

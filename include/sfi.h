@@ -25,7 +25,10 @@
  *  - Every function returns an sfi_status (0 = SFI_OK, negative = error)
  *    unless stated otherwise.  All arguments are validated before anything is
  *    enqueued: on an error nothing is launched and no output is touched;
- *    sfi_last_error() then holds a message (per calling thread).
+ *    sfi_last_error() then holds a message (per calling thread).  The one
+ *    exception is SFI_ERR_HIP from a launch after validation passed: kernels
+ *    the call enqueued before it stay enqueued, and the outputs of the listed
+ *    rows are then unspecified.
  *  - Pointers documented as "device" must point to device memory of the
  *    current HIP device; "host" pointers are read during the call only.
  *    The caller owns every buffer.  The library allocates no device memory.

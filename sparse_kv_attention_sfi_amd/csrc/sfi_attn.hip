@@ -92,7 +92,9 @@ struct Attn {
   //               logit_base[h * head_stride + r] for rows r < valid_rows,
   //               staged through Pw so that each lane writes four consecutive
   //               rows of one head with a single 16-byte store
-  template <int TILES>
+  // FRESH: the state is still the empty one from init() (one call per wave),
+  // so the running max becomes the block max and nothing needs rescaling.
+  template <int TILES, bool FRESH = false>
   __device__ __forceinline__ void consume(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
                                           const uint4 (&vb)[TILES * 16 / kRPL],
                                           const bool (&kvalid)[TILES], float* Pw, float scale_log2,
@@ -153,8 +155,8 @@ struct Attn {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float bm = lane_bcast(mx[h & 3], 16 * (h >> 2));
-      m_new[h] = fmaxf(m_run[h], bm);
-      alpha[h] = (m_new[h] == m_run[h]) ? 1.f : fast_exp2(m_run[h] - m_new[h]);
+      m_new[h] = FRESH ? bm : fmaxf(m_run[h], bm);
+      alpha[h] = (FRESH || m_new[h] == m_run[h]) ? 1.f : fast_exp2(m_run[h] - m_new[h]);
       rescale |= (alpha[h] != 1.f);
     }
     // probabilities relative to the new max
@@ -322,31 +324,37 @@ __device__ __forceinline__ void merge_waves_to_global(const float* sm, const flo
 }
 
 // merge_waves_to_global for states stored by finish_wave_lds (RG row groups
-// per wave).
+// per wave).  Each thread owns four consecutive columns of one head: it scales
+// the NW wave states once and reads and stores 16-byte vectors.
 template <int D, int G, int NW, int RG>
 __device__ __forceinline__ void merge_wave_groups_to_global(const float* sm, const float* sl, const float* so,
                                                             float* ml, int64_t ml_stride, float* o,
                                                             int64_t o_stride, int tid, int nthreads) {
-  for (int idx = tid; idx < G * D; idx += nthreads) {
-    const int h = idx / D, d = idx - h * D;
+  constexpr int Q = D / 4;  // column quads per head
+  for (int idx = tid; idx < G * Q; idx += nthreads) {
+    const int h = idx / Q, d = 4 * (idx - h * Q);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * G + h]);
-    float acc = 0.f, L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float mw = sm[w * G + h];
         if (mw == -INFINITY) continue;
         const float sc = fast_exp2(mw - M);
-        float part = 0.f;
+        float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) part += so[((w * RG + rg) * G + h) * D + d];
-        acc += part * sc;
+        for (int rg = 0; rg < RG; ++rg) {
+          const float4 v = *reinterpret_cast<const float4*>(so + ((w * RG + rg) * G + h) * D + d);
+          part.x += v.x; part.y += v.y; part.z += v.z; part.w += v.w;
+        }
+        acc.x += part.x * sc; acc.y += part.y * sc; acc.z += part.z * sc; acc.w += part.w * sc;
         L += sl[w * G + h] * sc;
       }
     }
-    o[h * o_stride + d] = acc;
+    *reinterpret_cast<float4*>(o + h * o_stride + d) = acc;
     if (d == 0) {
       ml[h * ml_stride] = M;
       ml[h * ml_stride + 1] = L;
@@ -815,7 +823,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
     }
     // a wave whose rows are all outside the support keeps the empty state
     if (__ballot(any) != 0) {
-      st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr,
+      st.template consume<TILES, true>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr,
                                  0, 0, lane);
     }
   }
@@ -908,7 +916,8 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
 #pragma unroll
   for (int tt = 0; tt < TILES; ++tt) kvalid[tt] = (w0 + 16 * tt + kr) < size;
   if (w0 < size) {
-    st.template consume<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, 0, lane);
+    st.template consume<TILES, true>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, 0,
+                                     lane);
   }
   st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
   __syncthreads();

@@ -72,14 +72,20 @@ struct Attn {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) l_lane[e] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) cacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Value of per-head array x for the head this lane's item e belongs to.
+  // Value of per-head array x for the head this lane's item e belongs to.  For
+  // G = 8 the two candidates are selected bitwise: a plain select of x[e] and
+  // x[4 + e] is turned into one load at a lane-dependent offset, which puts x
+  // in scratch memory.
   __device__ __forceinline__ static float for_item(const float (&x)[G], int lane, int e) {
     if constexpr (G <= 4) {
       return x[e < G ? e : 0];
     } else {
-      return (lane & 16) ? x[4 + e] : x[e];
+      const uint32_t hi = 0u - static_cast<uint32_t>((lane >> 4) & 1);
+      return __uint_as_float((__float_as_uint(x[e]) & ~hi) | (__float_as_uint(x[4 + e]) & hi));
     }
   }
 
@@ -92,16 +98,12 @@ struct Attn {
   //               logit_base[h * head_stride + r] for rows r < valid_rows,
   //               staged through Pw so that each lane writes four consecutive
   //               rows of one head with a single 16-byte store
-  // FRESH: the state is still the empty one from init() (one call per wave),
-  // so the running max becomes the block max and nothing needs rescaling.
-  template <int TILES, bool FRESH = false>
-  __device__ __forceinline__ void consume(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
-                                          const uint4 (&vb)[TILES * 16 / kRPL],
-                                          const bool (&kvalid)[TILES], float* Pw, float scale_log2,
-                                          float* logit_base, int64_t head_stride, int valid_rows, int lane) {
-    constexpr int NV = TILES * 16 / kRPL;
-    // logits
-    float x[TILES][4];
+  // Logits of TILES 16-row tiles in the log2 domain (-inf for rows outside the
+  // support): x[t][e] of lane l is head 4 * (l / 16) + e, row 16 t + l % 16.
+  template <int TILES>
+  __device__ __forceinline__ void logits(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
+                                         const bool (&kvalid)[TILES], float scale_log2,
+                                         float (&x)[TILES][4]) const {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -110,6 +112,60 @@ struct Attn {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[t][e] = kvalid[t] ? c[e] * scale_log2 : -INFINITY;
     }
+  }
+
+  // Online-softmax step over the block: new running max, p = exp2(x - max),
+  // the lane sums, and the factors alpha that rescale the old state.  Returns
+  // whether any alpha differs from 1.  FRESH: the state is still the empty one
+  // from init() (one call per wave), so the running max becomes the block max.
+  template <int TILES, bool FRESH>
+  __device__ __forceinline__ bool softmax_step(const float (&x)[TILES][4], float (&p)[TILES][4],
+                                               float (&alpha)[G], int lane) {
+    float mx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = x[0][e];
+#pragma unroll
+      for (int t = 1; t < TILES; ++t) v = fmaxf(v, x[t][e]);
+      mx[e] = row16_max(v);
+    }
+    float m_new[G];
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float bm = lane_bcast(mx[h & 3], 16 * (h >> 2));
+      m_new[h] = FRESH ? bm : fmaxf(m_run[h], bm);
+      alpha[h] = (FRESH || m_new[h] == m_run[h]) ? 1.f : fast_exp2(m_run[h] - m_new[h]);
+      rescale |= (alpha[h] != 1.f);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mn = for_item(m_new, lane, e);
+      const float al = for_item(alpha, lane, e);
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        p[t][e] = fast_exp2(x[t][e] - mn);
+        s += p[t][e];
+      }
+      l_lane[e] = l_lane[e] * al + s;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_run[h] = m_new[h];
+    return rescale;
+  }
+
+  // One block of TILES 16-row tiles: logits, online softmax and P.V on VALU.
+  // With logit_base, the block's logits are also stored to
+  // logit_base[h * head_stride + r] for rows r < valid_rows.
+  template <int TILES, bool FRESH = false>
+  __device__ __forceinline__ void consume(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
+                                          const uint4 (&vb)[TILES * 16 / kRPL],
+                                          const bool (&kvalid)[TILES], float* Pw, float scale_log2,
+                                          float* logit_base, int64_t head_stride, int valid_rows, int lane) {
+    constexpr int NV = TILES * 16 / kRPL;
+    float x[TILES][4];
+    logits<TILES>(qa, kb, kvalid, scale_log2, x);
     const int grp = lane >> 4;
     if (logit_base != nullptr) {
       constexpr int ROWS = TILES * 16;
@@ -141,38 +197,9 @@ struct Attn {
         }
       }
     }
-    // block max per head, new running max, rescale factors (wave-uniform)
-    float mx[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v = x[0][e];
-#pragma unroll
-      for (int t = 1; t < TILES; ++t) v = fmaxf(v, x[t][e]);
-      mx[e] = row16_max(v);
-    }
-    float m_new[G], alpha[G];
-    bool rescale = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float bm = lane_bcast(mx[h & 3], 16 * (h >> 2));
-      m_new[h] = FRESH ? bm : fmaxf(m_run[h], bm);
-      alpha[h] = (FRESH || m_new[h] == m_run[h]) ? 1.f : fast_exp2(m_run[h] - m_new[h]);
-      rescale |= (alpha[h] != 1.f);
-    }
-    // probabilities relative to the new max
     float p[TILES][4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float mn = for_item(m_new, lane, e);
-      const float al = for_item(alpha, lane, e);
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        p[t][e] = fast_exp2(x[t][e] - mn);
-        s += p[t][e];
-      }
-      l_lane[e] = l_lane[e] * al + s;
-    }
+    float alpha[G];
+    const bool rescale = softmax_step<TILES, FRESH>(x, p, alpha, lane);
     // stage P in LDS: row r, head h at Pw[r * G + h]
     wave_sync();
     if (grp < kGroups) {
@@ -218,8 +245,127 @@ struct Attn {
 #pragma unroll
         for (int d = 0; d < kEpp; ++d) acc[h][d] = fmaf(pr[h], vf[d], acc[h][d]);
     }
+  }
+
+  // ---- P.V on MFMA (bf16 only; one call per wave, blocks of 32-row groups) --
+  // out[h][d] = sum_r P[h][r] V[r][d] as 16x16x32 bf16 MFMAs with heads on M,
+  // rows on K and 16 columns on N.  P enters as two bf16 terms (its truncation
+  // and the truncated remainder, together within 2^-15 of P); V is exact.  V's
+  // rows are staged in LDS and read back with the gfx950 transposing read
+  // ds_read_b64_tr_b16: within each 16-lane group, lane 4 s + e receives
+  // element e of the 8-byte words read by lanes s, 4 + s, 8 + s and 12 + s, so
+  // when lane 16 q + 4 j + s reads columns 16 nb + 4 s .. + 3 of row 8 q + j,
+  // lane 16 q + n receives column 16 nb + n of rows 8 q .. 8 q + 3 (the MFMA's
+  // B operand layout).  The 32-byte column pair c of row r is stored at pair
+  // c ^ swz(r), so the 16 rows of one read fall evenly on the LDS banks.
+  static constexpr int kNB = D / 16;  // 16-column blocks
+  f32x4_t cacc[kNB];                 // C[4 * (lane / 16) + i][16 nb + lane % 16]
+
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (kPPR == 16) {
+      return (r & 3) + 4 * ((r >> 3) & 1);
+    } else {
+      return ((r >> 1) & 1) + 2 * ((r >> 3) & 1);
+    }
+  }
+
+  template <int TILES>
+  __device__ __forceinline__ void consume_pv_mfma(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
+                                                  const uint4 (&vb)[TILES * 16 / kRPL],
+                                                  const bool (&kvalid)[TILES], float* Pw, char* Vw,
+                                                  float scale_log2, int lane) {
+    static_assert(Elem<E>::kBytes == 2 && TILES % 2 == 0, "bf16, whole 32-row groups");
+    constexpr int ROWS = TILES * 16;
+    constexpr int NV = ROWS / kRPL;
+    constexpr int NKB = ROWS / 32;
+    float x[TILES][4], p[TILES][4], alpha[G];
+    logits<TILES>(qa, kb, kvalid, scale_log2, x);
+    softmax_step<TILES, true>(x, p, alpha, lane);
+    const int grp = lane >> 4, n = lane & 15;
+    // stage P as [head][row] and V rows (swizzled) in this wave's LDS
+    if (grp < kGroups) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) m_run[h] = m_new[h];
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * grp + e < G) Pw[(4 * grp + e) * ROWS + 16 * t + n] = p[t][e];
+    }
+    {
+      const int vr = lane / kPPR, vp = lane % kPPR;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int r = vr + kRPL * i;
+        *reinterpret_cast<uint4*>(Vw + r * kRowBytes + 32 * ((vp >> 1) ^ swz(r)) + 16 * (vp & 1)) = vb[i];
+      }
+    }
+    wave_sync();
+    const int q = grp;  // this lane's 8-row group within each 32-row block
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) {
+      // A operand: head n, rows 32 kb32 + 8 q .. + 7, as truncation + remainder
+      uint32_t ahi[4] = {0u, 0u, 0u, 0u}, alo[4] = {0u, 0u, 0u, 0u};
+      if (n < G) {
+        const float* src = Pw + n * ROWS + 32 * kb32 + 8 * q;
+        const float4 p0 = *reinterpret_cast<const float4*>(src);
+        const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t b0 = __float_as_uint(pv[2 * k]), b1 = __float_as_uint(pv[2 * k + 1]);
+          const uint32_t r0 = __float_as_uint(pv[2 * k] - __uint_as_float(b0 & 0xffff0000u));
+          const uint32_t r1 = __float_as_uint(pv[2 * k + 1] - __uint_as_float(b1 & 0xffff0000u));
+          ahi[k] = (b0 >> 16) | (b1 & 0xffff0000u);
+          alo[k] = (r0 >> 16) | (r1 & 0xffff0000u);
+        }
+      }
+      bf16x8_t a_hi, a_lo;
+      __builtin_memcpy(&a_hi, ahi, 16);
+      __builtin_memcpy(&a_lo, alo, 16);
+      // B operand per column block: column 16 nb + n of rows 32 kb32 + 8 q .. + 7,
+      // as two transposing reads of four rows each
+      const int jr = (lane >> 2) & 3, sc = lane & 3;
+      const int r0 = 32 * kb32 + 8 * q + jr, r1 = r0 + 4;
+      const char* row0 = Vw + r0 * kRowBytes + 8 * sc;
+      const char* row1 = Vw + r1 * kRowBytes + 8 * sc;
+      const int sw0 = swz(r0), sw1 = swz(r1);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const v4i16_t lo4 = lds_read_tr16(row0 + 32 * (nb ^ sw0));
+        const v4i16_t hi4 = lds_read_tr16(row1 + 32 * (nb ^ sw1));
+        bf16x8_t b;
+        __builtin_memcpy(&b, &lo4, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(&b) + 8, &hi4, 8);
+        cacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b, cacc[nb], 0, 0, 0);
+        cacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b, cacc[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // The MFMA path's wave state to LDS: sm[w * G + h], sl[w * G + h] and this
+  // wave's output slot so_w[h * D + d].
+  __device__ __forceinline__ void finish_wave_mfma(float* sm, float* sl, float* so_w, int w, int lane) {
+    float lt[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = row16_sum(l_lane[h & 3]);
+      lt[h] = lane_bcast(v, 16 * (h >> 2));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm[w * G + h] = m_run[h];
+        sl[w * G + h] = lt[h];
+      }
+    }
+    const int q = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q + i;
+      if (h < G) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) so_w[h * D + 16 * nb + n] = cacc[nb][i];
+      }
+    }
   }
 
   // Reduce this wave's state and store it in LDS slot `w`:
@@ -323,13 +469,15 @@ __device__ __forceinline__ void merge_waves_to_global(const float* sm, const flo
   }
 }
 
-// merge_waves_to_global for states stored by finish_wave_lds (RG row groups
-// per wave).  Each thread owns four consecutive columns of one head: it scales
-// the NW wave states once and reads and stores 16-byte vectors.
+// merge_waves_to_global for wave states of RG row groups each, wave w's at
+// so[w * wave_stride + (rg * G + h) * D + d] (finish_wave_lds: wave_stride =
+// RG * G * D; finish_wave_mfma: RG = 1).  Each thread owns four consecutive
+// columns of one head: it scales the NW wave states once and reads and stores
+// 16-byte vectors.
 template <int D, int G, int NW, int RG>
 __device__ __forceinline__ void merge_wave_groups_to_global(const float* sm, const float* sl, const float* so,
-                                                            float* ml, int64_t ml_stride, float* o,
-                                                            int64_t o_stride, int tid, int nthreads) {
+                                                            int wave_stride, float* ml, int64_t ml_stride,
+                                                            float* o, int64_t o_stride, int tid, int nthreads) {
   constexpr int Q = D / 4;  // column quads per head
   for (int idx = tid; idx < G * Q; idx += nthreads) {
     const int h = idx / Q, d = 4 * (idx - h * Q);
@@ -347,7 +495,7 @@ __device__ __forceinline__ void merge_wave_groups_to_global(const float* sm, con
         float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-          const float4 v = *reinterpret_cast<const float4*>(so + ((w * RG + rg) * G + h) * D + d);
+          const float4 v = *reinterpret_cast<const float4*>(so + w * wave_stride + (rg * G + h) * D + d);
           part.x += v.x; part.y += v.y; part.z += v.z; part.w += v.w;
         }
         acc.x += part.x * sc; acc.y += part.y * sc; acc.z += part.z * sc; acc.w += part.w * sc;
@@ -757,6 +905,41 @@ __device__ __forceinline__ int support_pos(const SupportGeom& s, int p, int t,
   return -1;
 }
 
+// Fast-step P.V runs on MFMA for bf16 caches when every wave covers whole
+// 32-row groups, else on VALU.
+template <typename E, int TILES>
+constexpr bool fast_pv_mfma() {
+  return Elem<E>::kBytes == 2 && TILES % 2 == 0;
+}
+
+// Tail of a fast-step workgroup: every wave's state to LDS, then the merge of
+// the NW wave states into the chunk's partial slot.  On the MFMA path a wave's
+// output slot reuses its own V staging rows (its reads of them are complete).
+template <typename A, int D, int G, int NW, int ROWS, bool MFMA>
+__device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v, int wave,
+                                            int lane, int tid, const FastArgs& a, int64_t qh0, int chunk) {
+  constexpr int kWaveBytes = ROWS * A::kRowBytes;
+  if constexpr (MFMA) {
+    wave_sync();
+    st.finish_wave_mfma(s_m, s_l, reinterpret_cast<float*>(s_v + wave * kWaveBytes), wave, lane);
+  } else {
+    st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
+  }
+  __syncthreads();
+  const int64_t slot = qh0 * a.part_stride + chunk;
+  float* ml = a.part_ml + slot * 2;
+  float* o = a.part_o + slot * D;
+  const int64_t ml_stride = static_cast<int64_t>(a.part_stride) * 2;
+  const int64_t o_stride = static_cast<int64_t>(a.part_stride) * D;
+  if constexpr (MFMA) {
+    merge_wave_groups_to_global<D, G, NW, 1>(s_m, s_l, reinterpret_cast<const float*>(s_v), kWaveBytes / 4, ml,
+                                             ml_stride, o, o_stride, tid, kFastThreads);
+  } else {
+    merge_wave_groups_to_global<D, G, NW, A::kRowGroups>(s_m, s_l, s_o, A::kRowGroups * G * D, ml, ml_stride, o,
+                                                         o_stride, tid, kFastThreads);
+  }
+}
+
 template <typename E, int D, int G, int TILES, bool ONE>
 __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
   using A = Attn<E, D, G>;
@@ -766,8 +949,10 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
   constexpr int CH = NW * ROWS;     // rows per workgroup
   constexpr int NV = ROWS / A::kRPL;
 
+  constexpr bool kMfma = fast_pv_mfma<E, TILES>();
   __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
-  __shared__ __attribute__((aligned(16))) float s_o[NW * A::kRowGroups * G * D];
+  __shared__ __attribute__((aligned(16))) float s_o[kMfma ? 4 : NW * A::kRowGroups * G * D];
+  __shared__ __attribute__((aligned(16))) char s_v[kMfma ? NW * ROWS * A::kRowBytes : 16];
   __shared__ float s_m[NW * G], s_l[NW * G];
   __shared__ int s_pos[CH];
 
@@ -823,16 +1008,16 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
     }
     // a wave whose rows are all outside the support keeps the empty state
     if (__ballot(any) != 0) {
-      st.template consume<TILES, true>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr,
-                                 0, 0, lane);
+      if constexpr (kMfma) {
+        st.template consume_pv_mfma<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, s_v + wave * ROWS * RB,
+                                           a.scale_log2, lane);
+      } else {
+        st.template consume<TILES, true>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, 0,
+                                         lane);
+      }
     }
   }
-  st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
-  __syncthreads();
-  const int64_t slot = qh0 * a.part_stride + chunk;
-  merge_wave_groups_to_global<D, G, NW, A::kRowGroups>(s_m, s_l, s_o, a.part_ml + slot * 2,
-                                  static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
-                                  static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
+  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, wave, lane, tid, a, qh0, chunk);
 }
 
 // Fast step over the packed support: the selected rows were copied into a
@@ -850,8 +1035,10 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   constexpr int NW = kFastThreads / 64;
   constexpr int NV = ROWS / A::kRPL;
 
+  constexpr bool kMfma = fast_pv_mfma<E, TILES>();
   __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
-  __shared__ __attribute__((aligned(16))) float s_o[NW * A::kRowGroups * G * D];
+  __shared__ __attribute__((aligned(16))) float s_o[kMfma ? 4 : NW * A::kRowGroups * G * D];
+  __shared__ __attribute__((aligned(16))) char s_v[kMfma ? NW * ROWS * A::kRowBytes : 16];
   __shared__ float s_m[NW * G], s_l[NW * G];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -916,15 +1103,15 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
 #pragma unroll
   for (int tt = 0; tt < TILES; ++tt) kvalid[tt] = (w0 + 16 * tt + kr) < size;
   if (w0 < size) {
-    st.template consume<TILES, true>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, 0,
-                                     lane);
+    if constexpr (kMfma) {
+      st.template consume_pv_mfma<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, s_v + wave * ROWS * RB,
+                                         a.scale_log2, lane);
+    } else {
+      st.template consume<TILES, true>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, a.scale_log2, nullptr, 0, 0,
+                                       lane);
+    }
   }
-  st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
-  __syncthreads();
-  const int64_t slot = qh0 * a.part_stride + chunk;
-  merge_wave_groups_to_global<D, G, NW, A::kRowGroups>(s_m, s_l, s_o, a.part_ml + slot * 2,
-                                  static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
-                                  static_cast<int64_t>(a.part_stride) * D, tid, kFastThreads);
+  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, wave, lane, tid, a, qh0, chunk);
 }
 
 // Copies the selected K/V rows of each (sequence, KV head) into the packed

@@ -77,6 +77,16 @@ __device__ __forceinline__ f32x4_t mfma_piece(F32, const uint4& q, const uint4& 
   return c;
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16) of the 8 bytes at `p`, an
+// address in LDS.  Within each 16-lane group, lane 4 s + e receives element e
+// (of four 16-bit elements) of the words read by lanes s, 4 + s, 8 + s and
+// 12 + s.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+__device__ __forceinline__ v4i16_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+}
+
 // DPP lane exchanges inside a row of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -89,15 +89,6 @@ struct Attn {
     }
   }
 
-  // Consume one block of TILES * 16 rows.
-  //   kb[t][kk] : K pieces in MFMA layout (row 16 t + lane % 16)
-  //   vb[i]     : V pieces in row layout (row lane / PPR + RPL * i)
-  //   kvalid[t] : row 16 t + lane % 16 exists
-  //   Pw        : this wave's LDS staging area, TILES * 16 * G floats
-  //   logit_base: if non-null, the block's logits go to
-  //               logit_base[h * head_stride + r] for rows r < valid_rows,
-  //               staged through Pw so that each lane writes four consecutive
-  //               rows of one head with a single 16-byte store
   // Logits of TILES 16-row tiles in the log2 domain (-inf for rows outside the
   // support): x[t][e] of lane l is head 4 * (l / 16) + e, row 16 t + l % 16.
   template <int TILES>
@@ -155,9 +146,15 @@ struct Attn {
     return rescale;
   }
 
-  // One block of TILES 16-row tiles: logits, online softmax and P.V on VALU.
-  // With logit_base, the block's logits are also stored to
-  // logit_base[h * head_stride + r] for rows r < valid_rows.
+  // Consume one block of TILES * 16 rows: logits, online softmax, P.V on VALU.
+  //   kb[t][kk] : K pieces in MFMA layout (row 16 t + lane % 16)
+  //   vb[i]     : V pieces in row layout (row lane / PPR + RPL * i)
+  //   kvalid[t] : row 16 t + lane % 16 exists
+  //   Pw        : this wave's LDS staging area, TILES * 16 * G floats
+  //   logit_base: if non-null, the block's logits go to
+  //               logit_base[h * head_stride + r] for rows r < valid_rows,
+  //               staged through Pw so that each lane writes four consecutive
+  //               rows of one head with a single 16-byte store
   template <int TILES, bool FRESH = false>
   __device__ __forceinline__ void consume(const uint4 (&qa)[kNL], const uint4 (&kb)[TILES][kNL],
                                           const uint4 (&vb)[TILES * 16 / kRPL],

@@ -60,7 +60,7 @@ extern "C" {
 #endif
 
 #define SFI_VERSION_MAJOR 0
-#define SFI_VERSION_MINOR 2
+#define SFI_VERSION_MINOR 3
 
 typedef enum {
   SFI_OK = 0,
@@ -127,9 +127,11 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int3
 /* Launch plan of sfi_slow_step / sfi_slow_step_select for these rows: writes
  * to splits_host[i] (host int32 [n_seq]) how many split-K partials the slow
  * step forms for each of the KV heads of sequence seq_ids_host[i], which sets
- * how much partial state its merge reads.  Launches nothing. */
+ * how much partial state its merge reads.  with_mass != 0 plans a step that
+ * writes mass (sfi_slow_step with mass, sfi_slow_step_select), whose splits
+ * may be shorter; 0 plans the dense-only step.  Launches nothing. */
 int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int32_t n_seq,
-                      int32_t* splits_host);
+                      int32_t with_mass, int32_t* splits_host);
 
 /* Launch plan of sfi_fast_step / sfi_fast_step_packed for these rows: writes
  * to chunks_host[i] (host int32 [n_seq]) how many partials (one per chunk of

@@ -69,7 +69,7 @@ def lib():
             "sfi_kv_append": (I32, [D, P(I32), I32, VP, VP, VP]),
             "sfi_pack_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP]),
             "sfi_fast_step_packed": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
-            "sfi_slow_plan": (I32, [D, P(I32), I32, P(I32)]),
+            "sfi_slow_plan": (I32, [D, P(I32), I32, I32, P(I32)]),
             "sfi_fast_plan": (I32, [D, S, P(I32), I32, P(I32)]),
             "sfi_slow_step_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "sfi_slow_step_select_async": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP, VP]),
@@ -209,12 +209,13 @@ def sfi_slow_step(kv: KVDesc, seq_ids, q, out, mass=None, ws=None, stream=None):
                                _stream(stream)), "sfi_slow_step")
 
 
-def sfi_slow_plan(kv: KVDesc, seq_ids):
-    """Split-K partials per KV head the slow step forms for each listed row."""
+def sfi_slow_plan(kv: KVDesc, seq_ids, with_mass=True):
+    """Split-K partials per KV head the slow step forms for each listed row
+    (with_mass: the step that writes mass, else the dense-only step)."""
     _, ids, n = _ids(seq_ids)
     out = np.zeros(max(n, 1), dtype=np.int32)
-    _check(lib().sfi_slow_plan(C.byref(kv.desc), ids, n, out.ctypes.data_as(C.POINTER(C.c_int32))),
-           "sfi_slow_plan")
+    _check(lib().sfi_slow_plan(C.byref(kv.desc), ids, n, 1 if with_mass else 0,
+                               out.ctypes.data_as(C.POINTER(C.c_int32))), "sfi_slow_plan")
     return out[:n].tolist()
 
 

@@ -316,8 +316,10 @@ int32_t for_each_group(const int32_t* ids, int32_t n, F&& f) {
 // ---- launch planning ------------------------------------------------------
 // Slow step: split-K partial over the whole history, then the combine
 // (output merge + mass).  Fills the launch arguments of one id group.
+// with_mass: the step writes mass (its partial kernel stores logits); mass
+// may still be NULL when only the launch table is wanted.
 void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const void* q, float* out, float* mass,
-               char* w, SlowArgs& a, CombineArgs& c) {
+               bool with_mass, char* w, SlowArgs& a, CombineArgs& c) {
   const SlowLayout L = slow_layout(desc);
   const int G = desc->n_q_heads / desc->n_kv_heads;
   const int unit = slow_unit_rows(desc);
@@ -342,8 +344,12 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
     rows += static_cast<int64_t>(desc->ctx_len_host[ids[i]]) * desc->n_kv_heads;
     t_max = std::max<int64_t>(t_max, desc->ctx_len_host[ids[i]]);
   }
-  // at most kMaxMergeSlots splits per head (the merge stages them in LDS)
-  const int64_t per = std::max(ceil_div(rows, target), ceil_div(t_max, kMaxMergeSlots));
+  // at most kMaxMergeSlots splits per head (the merge stages them in LDS);
+  // with mass, splits of at most kLogitBufRows rows where that limit allows,
+  // so that the partial kernel can buffer each split's logits
+  int64_t want = ceil_div(rows, target);
+  if (with_mass) want = std::min<int64_t>(want, kLogitBufRows);
+  const int64_t per = std::max(want, ceil_div(t_max, kMaxMergeSlots));
   a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
   a.tab.n = cnt;
   a.tab.wg_begin[0] = 0;
@@ -356,7 +362,7 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
     a.tab.ent[i].ctx = T;
     a.tab.ent[i].nsplit = static_cast<int32_t>(ceil_div(T, a.split_rows));
     a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
-    c.mass_blocks[i] = mass ? static_cast<int32_t>(ceil_div(T, kMassChunk)) : 0;
+    c.mass_blocks[i] = with_mass ? static_cast<int32_t>(ceil_div(T, kMassChunk)) : 0;
     c.tab.ent[i].seq = b;
     c.tab.ent[i].ctx = T;
     c.tab.ent[i].nsplit = a.tab.ent[i].nsplit;
@@ -495,12 +501,13 @@ int32_t sfi_slow_step(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SlowArgs a{};
     CombineArgs c{};
-    plan_slow(desc, ids, cnt, q, out, mass, w, a, c);
+    plan_slow(desc, ids, cnt, q, out, mass, mass != nullptr, w, a, c);
     return run_slow(desc, a, c, cnt, s);
   });
 }
 
-int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n_seq, int32_t* splits) {
+int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n_seq, int32_t with_mass,
+                      int32_t* splits) {
   int32_t st;
   if ((st = check_desc(desc)) != SFI_OK) return st;
   if (desc->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
@@ -511,7 +518,7 @@ int32_t sfi_slow_plan(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SlowArgs a{};
     CombineArgs c{};
-    plan_slow(desc, ids, cnt, nullptr, nullptr, nullptr, nullptr, a, c);
+    plan_slow(desc, ids, cnt, nullptr, nullptr, nullptr, with_mass != 0, nullptr, a, c);
     for (int i = 0; i < cnt; ++i) splits[done + i] = a.tab.ent[i].nsplit;
     done += cnt;
     return SFI_OK;
@@ -597,7 +604,7 @@ static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_
     // kernels run after the combine has consumed the logits and partials
     SlowArgs a{};
     CombineArgs c{};
-    plan_slow(desc, ids, cnt, q, out, mass, w, a, c);
+    plan_slow(desc, ids, cnt, q, out, mass, mass != nullptr, w, a, c);
     a.clear_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
     a.clear_list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
     c.sel_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);

@@ -539,6 +539,8 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
   __shared__ __attribute__((aligned(16))) float s_o[NW * G * D];
   __shared__ float s_m[NW * G], s_l[NW * G];
+  // the split's logits, [head][row], written out in one pass at the end
+  __shared__ __attribute__((aligned(16))) float s_lg[G * kLogitBufRows];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -573,6 +575,11 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   float* Pw = s_p + wave * ROWS * G;
   const int kr = lane & 15, kg = lane >> 4;
   const int vr = lane / A::kPPR, vp = lane % A::kPPR;
+  // Logits of a split that fits kLogitBufRows collect in LDS and leave in one
+  // contiguous pass per head after the loop: stored block by block, they
+  // interleave with the K/V read stream and cost HBM time far above their
+  // share of bytes.
+  const bool buffered = a.logits != nullptr && a.split_rows <= kLogitBufRows;
 
   for (int r0 = r_begin + wave * ROWS; r0 < r_end; r0 += NW * ROWS) {
     uint4 kb[TILES][A::kNL];
@@ -591,8 +598,30 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
       const int row = min(r0 + vr + A::kRPL * i, r_end - 1);
       vb[i] = ld16_stream(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
     }
-    float* lbase = a.logits ? a.logits + qh0 * a.logit_pitch + r0 : nullptr;
-    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lbase, a.logit_pitch, r_end - r0, lane);
+    float* lbase = a.logits == nullptr ? nullptr
+                   : buffered          ? s_lg + (r0 - r_begin)
+                                       : a.logits + qh0 * a.logit_pitch + r0;
+    st.template consume<TILES>(qa, kb, vb, kvalid, Pw, a.scale_log2, lbase,
+                               buffered ? kLogitBufRows : a.logit_pitch, r_end - r0, lane);
+  }
+  if (buffered) {
+    __syncthreads();
+    const int rows = r_end - r_begin;
+    constexpr int Q = kLogitBufRows / 4;
+    for (int idx = threadIdx.x; idx < G * Q; idx += kSlowThreads) {
+      const int h = idx / Q, r = 4 * (idx - h * Q);
+      if (r < rows) {
+        const float4 v = *reinterpret_cast<const float4*>(s_lg + h * kLogitBufRows + r);
+        float* dst = a.logits + (qh0 + h) * a.logit_pitch + r_begin + r;
+        if (r + 4 <= rows) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          dst[0] = v.x;
+          if (r + 1 < rows) dst[1] = v.y;
+          if (r + 2 < rows) dst[2] = v.z;
+        }
+      }
+    }
   }
   st.finish_wave(s_m, s_l, s_o, wave, lane);
   __syncthreads();

@@ -26,6 +26,7 @@ constexpr int kFastThreads = 256;    // 4 waves, gather kernel
 constexpr int kMergeThreads = 1024;  // fast-step chunk merge
 constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a merge accepts
 constexpr int kSlowTargetWgs = 1024;  // slow partial workgroups aimed at per launch
+constexpr int kLogitBufRows = 1024;   // slow partial: a split's logits are buffered in LDS up to this size
 
 // One launch's rows.  A row's fields sit together in one 16-byte record, so
 // a workgroup fetches them with one scalar load.

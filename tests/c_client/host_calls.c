@@ -49,7 +49,7 @@ int main(void) {
                               (int32_t*)0x70000, (int32_t*)0x80000, NULL, NULL, (void*)0x50000, need - 1,
                               NULL) == SFI_ERR_WORKSPACE);
   int32_t splits[2] = {0, 0};
-  EXPECT(sfi_slow_plan(&d, ids, 2, splits) == SFI_OK && splits[0] >= 1 && splits[1] >= 1);
+  EXPECT(sfi_slow_plan(&d, ids, 2, 1, splits) == SFI_OK && splits[0] >= 1 && splits[1] >= 1);
 
   /* the scheduler: geometric spans of mean 18 for 3 sequences, seed 7 */
   sfi_sched* s = NULL;

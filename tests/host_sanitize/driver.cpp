@@ -111,9 +111,9 @@ static void validation() {
   }
   CHECK(sfi_workspace_bytes(&d, &sp, 42) == 0);
   int32_t splits[1] = {-1}, chunks[1] = {-1};
-  CHECK(sfi_slow_plan(&d, id0, 1, splits) == SFI_OK && splits[0] >= 1);
+  CHECK(sfi_slow_plan(&d, id0, 1, 1, splits) == SFI_OK && splits[0] >= 1);
   CHECK(sfi_fast_plan(&d, &sp, id0, 1, chunks) == SFI_OK && chunks[0] >= 1);
-  CHECK(sfi_slow_plan(&d, id_bad, 1, splits) == SFI_ERR_INVALID_ARG);
+  CHECK(sfi_slow_plan(&d, id_bad, 1, 0, splits) == SFI_ERR_INVALID_ARG);
   CHECK(sfi_fast_plan(&d, &sp_bad, id0, 1, chunks) == SFI_ERR_INVALID_ARG);
   setenv("SFI_FAULT_INJECT", "select", 1);
   CHECK(sfi_select(&d, &sp, id0, 1, ffake, ifake, ifake, fake, 1u << 30, nullptr) == SFI_ERR_INJECTED);

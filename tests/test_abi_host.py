@@ -209,21 +209,32 @@ def test_slow_plan_covers_every_row():
         desc, keep = _desc(batch=len(ctx), hq=4 * hkv, hkv=hkv, d=d, dtype=dt, cap=cap, ctx=ctx)
         ids = np.arange(len(ctx), dtype=np.int32)
         out = np.full(len(ctx), -1, dtype=np.int32)
-        st = lib.sfi_slow_plan(C.byref(desc), ids.ctypes.data_as(C.POINTER(C.c_int32)), len(ctx),
-                               out.ctypes.data_as(C.POINTER(C.c_int32)))
-        assert st == 0
         unit = 4 * 16384 // (d * (2 if dt == B.SFI_BF16 else 4))   # 4 waves x one 16 KiB block each
-        for t, n in zip(ctx, out):
-            assert 1 <= n <= 512 and n <= -(-t // unit), (t, n)
+        for with_mass in (0, 1):
+            st = lib.sfi_slow_plan(C.byref(desc), ids.ctypes.data_as(C.POINTER(C.c_int32)), len(ctx), with_mass,
+                                   out.ctypes.data_as(C.POINTER(C.c_int32)))
+            assert st == 0
+            for t, n in zip(ctx, out):
+                assert 1 <= n <= 512 and n <= -(-t // unit), (t, n)
+                if with_mass and t <= 512 * 1024:
+                    assert -(-t // n) <= 1024, (t, n)   # splits short enough for the logit buffer
     assert S.sfi_slow_plan is not None
     desc, keep = _desc(batch=1, hq=32, hkv=8, d=128, dtype=B.SFI_BF16, cap=131072, ctx=(131072,))
     one = np.zeros(1, dtype=np.int32)
     out = np.zeros(1, dtype=np.int32)
-    assert lib.sfi_slow_plan(C.byref(desc), one.ctypes.data_as(C.POINTER(C.c_int32)), 1,
+    assert lib.sfi_slow_plan(C.byref(desc), one.ctypes.data_as(C.POINTER(C.c_int32)), 1, 1,
                              out.ctypes.data_as(C.POINTER(C.c_int32))) == 0 and out[0] == 128
+    # four rows of 128K: the dense step keeps 4096-row splits, the step with mass 1024-row ones
+    desc4, keep4 = _desc(batch=4, hq=32, hkv=8, d=128, dtype=B.SFI_BF16, cap=131072, ctx=(131072,) * 4)
+    four = np.arange(4, dtype=np.int32)
+    out4 = np.zeros(4, dtype=np.int32)
+    assert lib.sfi_slow_plan(C.byref(desc4), four.ctypes.data_as(C.POINTER(C.c_int32)), 4, 0,
+                             out4.ctypes.data_as(C.POINTER(C.c_int32))) == 0 and list(out4) == [32] * 4
+    assert lib.sfi_slow_plan(C.byref(desc4), four.ctypes.data_as(C.POINTER(C.c_int32)), 4, 1,
+                             out4.ctypes.data_as(C.POINTER(C.c_int32))) == 0 and list(out4) == [128] * 4
     desc, keep = _desc(ctx=(100,))
     bad = np.array([3], dtype=np.int32)
-    assert lib.sfi_slow_plan(C.byref(desc), bad.ctypes.data_as(C.POINTER(C.c_int32)), 1,
+    assert lib.sfi_slow_plan(C.byref(desc), bad.ctypes.data_as(C.POINTER(C.c_int32)), 1, 1,
                              out.ctypes.data_as(C.POINTER(C.c_int32))) == B.SFI_ERR_INVALID_ARG
 
 

@@ -116,7 +116,59 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="end with one device copy of MIB MiB (calibrates memory-traffic counters)")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then "
+                        "WRITE_SIZE, each ending with --copy-probe) into the traffic summary bench.py reads")
     return p.parse_args()
+
+
+def traffic_summary(fetch_dir, write_dir, copy_mib, out_json):
+    """Per-dispatch HBM bytes of every library kernel from two rocprofv3
+    counter runs: the median reading over each kernel's dispatches, scaled by
+    the factor that maps the run's last dispatch (the --copy-probe copy of
+    copy_mib MiB) to its known size.  Writes out_json and returns it."""
+    import csv
+    import glob
+    import statistics
+
+    def read(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter_collection.csv under {d}")
+        rows = []
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        last = rows[-1]
+        factor = copy_mib * float(1 << 20) / (last[2] * 1024.0)
+        per = {}
+        for _, name, val in rows[:-1]:
+            name = name[5:] if name.startswith("void ") else name
+            if name.startswith("sfi::"):
+                per.setdefault(name, []).append(val * 1024.0 * factor)
+        return per, factor, last[2] / 1024.0
+
+    fetch, f_fac, f_copy = read(fetch_dir, "FETCH_SIZE")
+    write, w_fac, w_copy = read(write_dir, "WRITE_SIZE")
+    kernels = {}
+    for name in sorted(set(fetch) | set(write)):
+        kernels[name] = {"group": kernel_group(name),
+                         "dispatches_fetch": len(fetch.get(name, [])),
+                         "fetch_bytes": statistics.median(fetch[name]) if name in fetch else 0.0,
+                         "dispatches_write": len(write.get(name, [])),
+                         "write_bytes": statistics.median(write[name]) if name in write else 0.0}
+    out = {"about": "HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (two runs): median "
+                    "over dispatches of each kernel, scaled by the factor that maps the reading of a "
+                    f"{copy_mib} MiB device copy made at the end of the same run to {copy_mib} MiB",
+           "calibration": {"copy_mib": copy_mib, "fetch_reading_mib": f_copy, "fetch_factor": f_fac,
+                           "write_reading_mib": w_copy, "write_factor": w_fac},
+           "csrc_digest": csrc_digest(), "kernels": kernels}
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
 
 
 def log(*a):
@@ -125,6 +177,10 @@ def log(*a):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        t = traffic_summary(*args.traffic_summary, args.copy_probe or 256, TRAFFIC_FILE)
+        print(json.dumps(t["calibration"]))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the path shards by KV head or "
                           "sequence with no per-step communication, but no multi-GPU run is built",

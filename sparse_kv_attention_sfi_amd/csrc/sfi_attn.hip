@@ -576,9 +576,9 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   const int kr = lane & 15, kg = lane >> 4;
   const int vr = lane / A::kPPR, vp = lane % A::kPPR;
   // Logits of a split that fits kLogitBufRows collect in LDS and leave in one
-  // contiguous pass per head after the loop: stored block by block, they
-  // interleave with the K/V read stream and cost HBM time far above their
-  // share of bytes.
+  // contiguous pass per head after the loop, written through to memory:
+  // stored block by block, or left dirty in L2, they interleave with the K/V
+  // read stream and cost HBM time far above their share of bytes.
   const bool buffered = a.logits != nullptr && a.split_rows <= kLogitBufRows;
 
   for (int r0 = r_begin + wave * ROWS; r0 < r_end; r0 += NW * ROWS) {
@@ -612,13 +612,13 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
       const int h = idx / Q, r = 4 * (idx - h * Q);
       if (r < rows) {
         const float4 v = *reinterpret_cast<const float4*>(s_lg + h * kLogitBufRows + r);
-        float* dst = a.logits + (qh0 + h) * a.logit_pitch + r_begin + r;
+        float* dst = a.logits + (qh0 + h) * a.logit_pitch + r_begin;  // this split's logits of head h
         if (r + 4 <= rows) {
-          *reinterpret_cast<float4*>(dst) = v;
+          st16_wt(dst, 4 * rows, 4 * r, v);
         } else {
-          dst[0] = v.x;
-          if (r + 1 < rows) dst[1] = v.y;
-          if (r + 2 < rows) dst[2] = v.z;
+          st4_wt(dst + r, v.x);
+          if (r + 1 < rows) st4_wt(dst + r + 1, v.y);
+          if (r + 2 < rows) st4_wt(dst + r + 2, v.z);
         }
       }
     }

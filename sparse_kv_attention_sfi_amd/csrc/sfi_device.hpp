@@ -37,6 +37,28 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Write-through stores (system coherence, sc0 sc1).  Bulk results written
+// while a kernel streams reads (the slow step's logits) go out to memory as
+// they are stored instead of staying dirty in the XCD's L2, whose later
+// write-back competes with the read stream.
+//
+// st16_wt: 16 bytes at byte offset `off` of the buffer [base, base + bytes),
+// one buffer_store_dwordx4 per lane (a store outside the range is dropped by
+// the buffer's range check).  0x00020000 is the gfx9 buffer descriptor's
+// word 3 for untyped 32-bit data; 17 = sc0 | sc1 cache-policy bits.
+__device__ __forceinline__ void st16_wt(float* base, int32_t bytes, int32_t off, float4 v) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), bytes, 0x00020000);
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4 d = {static_cast<int>(__float_as_uint(v.x)), static_cast<int>(__float_as_uint(v.y)),
+                static_cast<int>(__float_as_uint(v.z)), static_cast<int>(__float_as_uint(v.w))};
+  __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 17);
+}
+// st4_wt: one float (a relaxed system-scope atomic store: global_store_dword
+// with sc0 sc1).
+__device__ __forceinline__ void st4_wt(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __device__ __forceinline__ float4 ld16_stream_f(const float* p) {
   const uint4 u = ld16_stream(p);
   return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));

@@ -37,10 +37,11 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Write-through stores (system coherence, sc0 sc1).  Bulk results written
-// while a kernel streams reads (the slow step's logits) go out to memory as
-// they are stored instead of staying dirty in the XCD's L2, whose later
-// write-back competes with the read stream.
+// Write-through stores (system coherence, sc0 sc1): the data goes out to
+// memory as it is stored instead of staying dirty in the XCD's L2 until an
+// eviction.  Used for the slow step's logits, written while the kernel
+// streams K and V, where it measured faster than write-back stores; the
+// other bulk outputs keep plain stores, which measured as fast or faster.
 //
 // st16_wt: 16 bytes at byte offset `off` of the buffer [base, base + bytes),
 // one buffer_store_dwordx4 per lane (a store outside the range is dropped by

@@ -408,8 +408,10 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   const int cnt_d1 = a.list_n[h.bg];
   const uint64_t* glist = a.list + h.bg * kSelListCap;
   const uint64_t first = glist[tid];  // always inside the list; used if tid < cnt_d1
-  int before = 0;  // kept keys of the chunks before this one (this thread's share)
-  for (int c = tid; c < h.c; c += kSelThreads) before += a.chunk_above[h.bg * kSelMaxChunks + c];
+  // keys above the threshold bin in the chunks before this one (this
+  // thread's share), requested with the first round trip
+  int above_before = 0;
+  for (int c = tid; c < h.c; c += kSelThreads) above_before += a.chunk_above[h.bg * kSelMaxChunks + c];
   const float inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
   const ScoreParams sp = score_params(a, h, inv2h);
   // keys of the first pass, computed while the list is still on its way
@@ -421,7 +423,9 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
   const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
   uint64_t kstar;
+  int before;  // kept keys of the chunks before this one (this thread's share)
   if (cnt_d1 <= kSelListCap) {
+    before = above_before;  // plus the threshold-bin keys at or above K* before the chunk
     for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
     __syncthreads();
     kstar = cnt_d1 <= kSelThreads
@@ -438,6 +442,8 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     __syncthreads();
     kstar = radix_resolve([&](int i) { return cand_key(sp, i); }, h.n, cnt_d1, pfx, pmask, 64 - kSelDigitBits,
                           need, s_hist, s_wave, s_res, &s_kstar);
+    // every kept key before the chunk, those above the threshold bin included
+    before = 0;
     for (int i = tid; i < i0; i += kSelThreads) before += cand_key(sp, i) >= kstar;
   }
   int base;

@@ -113,6 +113,33 @@ def test_select_ties_exact(k):
         assert sel[0, g, :cnt[0, g]].tolist() == ora.tolist()
 
 
+@pytest.mark.parametrize("lam", [0.0, 0.1])
+def test_select_threshold_bin_beyond_lds_with_keys_above(lam):
+    """Flat evidence over a long context plus heavy positions spread over every
+    chunk: the k-th key's bin holds far more keys than the Selector resolves
+    in LDS (its radix path over all candidates), while keys above that bin
+    sit in every chunk, so each chunk's output offset has both kinds of keys
+    before it.  Checked against the oracle, set and order."""
+    rng = np.random.default_rng(11)
+    T, ns, W, k, Hkv = 60000, 16, 256, 2048, 2
+    n = T - ns - W
+    f = np.full((1, Hkv, T), 1.0, dtype=np.float32)
+    for g in range(Hkv):
+        heavy = rng.choice(n, size=900 + 300 * g, replace=False) + ns
+        f[0, g, heavy] = 3.0
+    f /= f.sum(axis=-1, keepdims=True)
+    kv = _mass_cache(1, Hkv, T, [T])
+    sp = S.support_params(ns, W, k, lam)
+    sel, cnt = _select_gpu(kv, sp, [0], torch.from_numpy(f).cuda())
+    for g in range(Hkv):
+        got = sel[0, g].tolist()
+        assert cnt[0, g] == k and got == sorted(got), g
+        if lam == 0.0:  # fp32 and fp64 scores coincide: the set is unique
+            assert got == O.select(f[0, g].astype(np.float64), T, ns, W, k, lam)[0].tolist(), g
+        else:
+            check_support(np.asarray(got), f[0, g].astype(np.float64), T, ns, W, k, lam, f"g{g}")
+
+
 def test_select_all_equal_and_prior_closed_form():
     """Uniform evidence: with lambda > 0 the choice follows the prior (both ends
     of the candidate range); with lambda = 0 every score ties and the lowest k

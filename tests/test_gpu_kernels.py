@@ -114,14 +114,16 @@ def test_select_ties_exact(k):
 
 
 @pytest.mark.parametrize("lam", [0.0, 0.1])
-def test_select_threshold_bin_beyond_lds_with_keys_above(lam):
-    """Flat evidence over a long context plus heavy positions spread over every
-    chunk: the k-th key's bin holds far more keys than the Selector resolves
-    in LDS (its radix path over all candidates), while keys above that bin
-    sit in every chunk, so each chunk's output offset has both kinds of keys
-    before it.  Checked against the oracle, set and order."""
+@pytest.mark.parametrize("T", [5000, 60000])
+def test_select_large_threshold_bin_with_keys_above(T, lam):
+    """Flat evidence plus heavy positions spread over every chunk.  With
+    lambda = 0 the k-th key's bin holds every flat candidate: at T = 5000 a
+    few thousand keys, resolved by radix levels in LDS; at T = 60000 more
+    than fit in LDS, resolved by radix passes over all candidates.  Keys
+    above that bin sit in every chunk, so each chunk's output offset has both
+    kinds of keys before it.  Checked against the oracle, set and order."""
     rng = np.random.default_rng(11)
-    T, ns, W, k, Hkv = 60000, 16, 256, 2048, 2
+    ns, W, k, Hkv = 16, 256, 2048, 2
     n = T - ns - W
     f = np.full((1, Hkv, T), 1.0, dtype=np.float32)
     for g in range(Hkv):

@@ -54,6 +54,37 @@ def test_slow_without_mass_and_subset_rows():
     assert torch.all(out[1] == 7.0) and torch.all(out[3] == 7.0)    # unlisted rows untouched
 
 
+def test_context_beyond_the_logit_buffer():
+    """600000 rows: with at most 512 splits per head, each split is longer
+    than the 1024 rows whose logits a workgroup buffers in LDS, so the slow
+    partial stores its logits block by block.  Separate calls and the fused
+    refresh (with a Selector over ~600K candidates) against the oracle."""
+    T, Hq, Hkv, D, ns, W, k = 600000, 4, 1, 64, 16, 256, 2048
+    kv, q = random_cache(1, Hq, Hkv, T, D, torch.float32, [T], seed=42, q_scale=2.0)
+    splits = S.sfi_slow_plan(kv, [0])[0]
+    assert splits <= 512 and -(-T // splits) > 1024
+    out, mass = run_slow(kv, q, [0])
+    o_ref, f_ref = oracle_slow(kv, q, 0)
+    assert np.max(np.abs(np64(out[0]) - o_ref)) < OUT_TOL
+    check_mass(np64(mass[0]), f_ref, T)
+    sp = S.support_params(ns, W, k, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    dev = kv.k.device
+    out2 = torch.empty_like(out)
+    mass2 = torch.empty_like(mass)
+    sel = torch.empty(1, Hkv, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, Hkv, dtype=torch.int32, device=dev)
+    pk = torch.empty(1, Hkv, k, D, dtype=torch.float32, device=dev)
+    pv = torch.empty_like(pk)
+    S.sfi_slow_step_select(kv, sp, [0], q, out2, mass2, sel, cnt, pk, pv, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(mass2, mass)
+    got = sel[0, 0, :int(cnt[0, 0])].cpu().numpy()
+    assert int(cnt[0, 0]) == k and np.all(np.diff(got) > 0)
+    check_support(got, f_ref[0], T, ns, W, k, 0.1, "T=600000")
+    assert torch.equal(pk[0, 0], kv.k[0, 0][torch.from_numpy(got).to(dev).long()])
+
+
 def test_slow_deterministic():
     kv, q = random_cache(1, 32, 8, 40000, 128, torch.bfloat16, [39999], seed=3)
     a_out, a_mass = run_slow(kv, q, [0])

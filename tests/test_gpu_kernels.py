@@ -301,6 +301,43 @@ def test_invalid_arguments_raise_before_launch():
         S.sfi_slow_step(kv, [0], q, out, None, S.alloc_workspace(kv))    # ctx beyond capacity
 
 
+@pytest.mark.parametrize("G,k", [(4, 10000), (8, 5000), (1, 33000)])
+def test_fast_step_large_support(G, k):
+    """Supports of 5K to 33K rows per KV head: more chunk partials per head
+    than the merge gathers in its first round trip (64 for G = 4, 32 for
+    G = 8, 256 for G = 1), so the merge loops.  Fused refresh, then packed
+    and gather fast steps against each other and the oracle."""
+    Hkv, ns, W, D = 2, 16, 256, 128
+    ctx = [k + 9000, k // 2 + 400]
+    B = len(ctx)
+    kv, q = random_cache(B, G * Hkv, Hkv, max(ctx), D, torch.bfloat16, ctx, seed=G + k, q_scale=2.0)
+    dev = kv.k.device
+    sp = S.support_params(ns, W, k, 0.1)
+    chunks = S.sfi_fast_plan(kv, sp, [0])[0]
+    assert chunks > {1: 256, 4: 64, 8: 32}[G]
+    ws = S.alloc_workspace(kv, sp)
+    ids = list(range(B))
+    out = torch.empty(B, G * Hkv, D, device=dev)
+    mass = torch.empty(B, Hkv, max(ctx), device=dev)
+    sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    pk = torch.empty(B, Hkv, k, D, dtype=torch.bfloat16, device=dev)
+    pv = torch.empty_like(pk)
+    S.sfi_slow_step_select(kv, sp, ids, q, out, mass, sel, cnt, pk, pv, ws)
+    out_g = torch.full_like(out, float("nan"))
+    out_p = torch.full_like(out, float("nan"))
+    S.sfi_fast_step(kv, sp, ids, q, sel, cnt, out_g, ws)
+    S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out_p, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_g, out_p)
+    for b in range(B):
+        T = ctx[b]
+        c = cnt[b].cpu().numpy()
+        sels = [sel[b, g, :c[g]].cpu().numpy().astype(np.int64) for g in range(Hkv)]
+        ref = O.fast_step(np64(q[b]), np64(kv.k[b, :, :T]), np64(kv.v[b, :, :T]), T, ns, W, sels)
+        assert np.max(np.abs(np64(out_p[b]) - ref)) < OUT_TOL
+
+
 # ------------------------------------------------------------------ packed support
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])

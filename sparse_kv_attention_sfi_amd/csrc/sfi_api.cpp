@@ -323,7 +323,9 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
   const SlowLayout L = slow_layout(desc);
   const int G = desc->n_q_heads / desc->n_kv_heads;
   const int unit = slow_unit_rows(desc);
-  const int target = std::max(64, env_int("SFI_SLOW_TARGET_WGS", kSlowTargetWgs));
+  // workgroups the split-K partial aims at; SFI_SLOW_TARGET_WGS overrides it
+  // for tuning (read once per process)
+  static const int target = std::max(64, env_int("SFI_SLOW_TARGET_WGS", kSlowTargetWgs));
   a.k = desc->k;
   a.v = desc->v;
   a.q = q;

@@ -85,6 +85,46 @@ def test_context_beyond_the_logit_buffer():
     assert torch.equal(pk[0, 0], kv.k[0, 0][torch.from_numpy(got).to(dev).long()])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_explicit_logit_scale(dtype):
+    """A caller-given logit scale (not 1/sqrt(D)) reaches the slow partial, the
+    mass, the Selector and both fast steps."""
+    T, Hq, Hkv, D, ns, W, k, scale = 5000, 16, 4, 128, 8, 64, 300, 0.21
+    kv0, q = random_cache(1, Hq, Hkv, T, D, DT[dtype], [T], seed=21, q_scale=1.0)
+    kv = S.KVDesc(kv0.k, kv0.v, [T], Hq, scale=scale)
+    sp = S.support_params(ns, W, k, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    dev = kv.k.device
+    out = torch.empty(1, Hq, D, device=dev)
+    mass = torch.empty(1, Hkv, T, device=dev)
+    sel = torch.empty(1, Hkv, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, Hkv, dtype=torch.int32, device=dev)
+    pk = torch.empty(1, Hkv, k, D, dtype=DT[dtype], device=dev)
+    pv = torch.empty_like(pk)
+    S.sfi_slow_step_select(kv, sp, [0], q, out, mass, sel, cnt, pk, pv, ws)
+    out_p = torch.empty_like(out)
+    out_g = torch.empty_like(out)
+    S.sfi_fast_step_packed(kv, sp, [0], q, pk, pv, cnt, out_p, ws)
+    S.sfi_fast_step(kv, sp, [0], q, sel, cnt, out_g, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_g)
+    K64, V64, q64 = np64(kv.k[0]), np64(kv.v[0]), np64(q[0])
+    o_ref, P = O.dense_attention(q64, K64, V64, scale=scale)
+    f_ref = O.group_mass(P, Hkv)
+    assert np.max(np.abs(np64(out[0]) - o_ref)) < OUT_TOL
+    check_mass(np64(mass[0]), f_ref, "scale")
+    sels = []
+    for g in range(Hkv):
+        got = sel[0, g, :int(cnt[0, g])].cpu().numpy()
+        check_support(got, f_ref[g], T, ns, W, k, 0.1, f"g{g}")
+        sels.append(got.astype(np.int64))
+    ref = O.fast_step(q64, K64, V64, T, ns, W, sels, scale=scale)
+    assert np.max(np.abs(np64(out_p[0]) - ref)) < OUT_TOL
+    # the default scale gives a different result on these inputs
+    o_def, _ = O.dense_attention(q64, K64, V64)
+    assert np.max(np.abs(o_def - o_ref)) > 10 * OUT_TOL
+
+
 def test_slow_deterministic():
     kv, q = random_cache(1, 32, 8, 40000, 128, torch.bfloat16, [39999], seed=3)
     a_out, a_mass = run_slow(kv, q, [0])

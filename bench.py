@@ -116,6 +116,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="end with one device copy of MIB MiB (calibrates memory-traffic counters)")
+    p.add_argument("--stream-probe", type=int, default=2048, metavar="MIB",
+                   help="time a device copy of MIB MiB on the same GPU, for the slow partial's bandwidth as a "
+                        "fraction of a plain streaming copy (0: skip)")
     p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then "
                         "WRITE_SIZE, each ending with --copy-probe) into the traffic summary bench.py reads")
@@ -476,6 +479,12 @@ def main():
     }
     if args.batch_check:
         result["fast_step_batch"] = fast_batch_check(w, sp, args.batch_check, dev)
+    if args.stream_probe:
+        sc = stream_copy_probe(args.stream_probe, dev)
+        for key, k in (("slow_partial", kern.get("slow_partial")), ("dense_slow_partial", dense_kern.get("slow_partial"))):
+            if k:
+                sc[f"{key}_vs_copy"] = alg["slow_partial"] / (k["avg_us"] * 1e-6) / 1e9 / sc["GBps"]
+        result["stream_copy"] = sc
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, sp, args.cpu_budget)
     if args.copy_probe:
@@ -624,6 +633,33 @@ def run_batched(args, w, dev):
         "slow_row_fraction": slow_rows / (K * B),
     }
     print(json.dumps(result))
+
+
+def stream_copy_probe(mib, dev, reps=10):
+    """A plain device-to-device copy of `mib` MiB (torch copy_), timed with
+    events on the copy's stream: the streaming bandwidth this GPU reaches
+    with a read and a write per byte, the practical ceiling the slow step's
+    read stream is compared with."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    ts.sort()
+    us = ts[len(ts) // 2]
+    gbps = 2.0 * n * 4 / (us * 1e-6) / 1e9
+    del src, dst
+    return {"mib": mib, "us": us, "GBps": gbps, "frac": gbps / HBM_PEAK_GBS,
+            "bytes_per_copy": "read + write"}
 
 
 def fast_batch_check(w, sp, batch, dev, ctx=32768, calls=20):

@@ -87,6 +87,15 @@ def measured_traffic(group, workload_name):
 METRIC = "decode-attn steps/sec/layer (slow, fast, blended) + HBM GB/s frac @128K ctx"
 
 
+def traffic_rate(traffic, avg_us):
+    """Measured HBM bytes per launch over the launch's average duration (the
+    DRAM-side rate, beside the algorithmic-byte rate), or nothing."""
+    if traffic is None or not avg_us:
+        return {}
+    gbps = traffic / (avg_us * 1e-6) / 1e9
+    return {"traffic_GBps": gbps, "traffic_frac": gbps / HBM_PEAK_GBS}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -464,7 +473,8 @@ def main():
         "cold_cache_check": cold,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d.get("frac"), "traffic": measured_traffic(dominant, w.name),
-                     "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"]},
+                     "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"],
+                     **traffic_rate(measured_traffic(dominant, w.name), d["avg_us"])},
         "roofline_dense_slow_partial": ({"bound": "hbm", "achieved": alg["slow_partial"] / (dense_kern["slow_partial"]["avg_us"] * 1e-6) / 1e9,
                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": alg["slow_partial"] / (dense_kern["slow_partial"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -474,7 +484,8 @@ def main():
                                         if "slow_partial" in dense_kern else None),
         **{f"roofline_{n}": {"bound": "hbm", "achieved": kern[n]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": kern[n]["frac"], "traffic": measured_traffic(n, w.name),
-                             "alg_bytes_per_launch": kern[n]["alg_bytes"], "avg_launch_us": kern[n]["avg_us"]}
+                             "alg_bytes_per_launch": kern[n]["alg_bytes"], "avg_launch_us": kern[n]["avg_us"],
+                             **traffic_rate(measured_traffic(n, w.name), kern[n]["avg_us"])}
            for n in ("slow_partial", "fast_partial") if n in kern and n != dominant},
     }
     if args.batch_check:

@@ -72,3 +72,10 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_traffic_rate():
+    r = bench.traffic_rate(4e9, 1e3)           # 4 GB in 1 ms
+    assert r["traffic_GBps"] == pytest.approx(4000.0)
+    assert r["traffic_frac"] == pytest.approx(4000.0 / bench.HBM_PEAK_GBS)
+    assert bench.traffic_rate(None, 5.0) == {}

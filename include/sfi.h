@@ -47,7 +47,9 @@
  *    one (fresh allocations and whole-row views of them do).  A misaligned
  *    buffer fails validation with SFI_ERR_INVALID_ARG.
  *  - Supported shapes: head_dim 64 or 128; Hq / Hkv in {1, 2, 4, 8};
- *    kv_dtype SFI_F32 or SFI_BF16; 1 <= ctx_len[b] <= kv_capacity.
+ *    kv_dtype SFI_F32 or SFI_BF16; 1 <= ctx_len[b] <= kv_capacity <= 2^30;
+ *    batch <= 65536; n_kv_heads <= 256.  Support parameters: n_sink and
+ *    n_recent <= 2^30, top_k <= 2^24.
  */
 #ifndef SFI_H_
 #define SFI_H_

@@ -60,6 +60,10 @@ int32_t check_desc(const sfi_kv_desc* d) {
   if (d->batch < 1) return fail(SFI_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
   if (d->n_q_heads < 1 || d->n_kv_heads < 1)
     return fail(SFI_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", d->n_q_heads, d->n_kv_heads);
+  // bounds that keep every workspace size and launch-grid count in range
+  if (d->batch > kMaxBatch) return fail(SFI_ERR_INVALID_ARG, "batch %d exceeds %d", d->batch, kMaxBatch);
+  if (d->n_kv_heads > kMaxKvHeads)
+    return fail(SFI_ERR_UNSUPPORTED, "n_kv_heads %d exceeds %d", d->n_kv_heads, kMaxKvHeads);
   if (d->n_q_heads % d->n_kv_heads != 0)
     return fail(SFI_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", d->n_q_heads,
                 d->n_kv_heads);
@@ -123,6 +127,8 @@ int32_t check_params(const sfi_support_params* sp) {
   if (sp->n_sink < 0 || sp->n_recent < 0 || sp->top_k < 0)
     return fail(SFI_ERR_INVALID_ARG, "n_sink, n_recent and top_k must be >= 0");
   if (sp->top_k > (1 << 24)) return fail(SFI_ERR_INVALID_ARG, "top_k %d too large", sp->top_k);
+  if (sp->n_sink > (1 << 30) || sp->n_recent > (1 << 30))
+    return fail(SFI_ERR_INVALID_ARG, "n_sink and n_recent must be <= 2^30");
   if (!(sp->lambda >= 0.f && sp->lambda <= 1.f))
     return fail(SFI_ERR_INVALID_ARG, "lambda must lie in [0, 1]");
   return SFI_OK;

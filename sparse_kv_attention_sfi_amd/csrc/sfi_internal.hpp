@@ -14,6 +14,11 @@ namespace sfi {
 // launches.  The table travels in the kernel-argument block.
 constexpr int kMaxSeqPerLaunch = 64;
 
+// Largest batch and KV-head count a descriptor may name: with them every
+// workspace size fits 64 bits and every launch grid 32 bits.
+constexpr int kMaxBatch = 65536;
+constexpr int kMaxKvHeads = 256;
+
 // Workgroup shapes.
 constexpr int kSlowThreads = 256;    // 4 waves, split-K partial kernel
 constexpr int kCombineThreads = 1024; // merge + mass kernel

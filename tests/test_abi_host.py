@@ -97,6 +97,8 @@ def test_validation_rejects_before_launch():
         dict(cap=0),                # capacity
         dict(ctx=(101,)),           # ctx beyond capacity
         dict(ctx=(0,)),             # empty context
+        dict(hq=512, hkv=512),      # more KV heads than supported
+        dict(batch=70000),          # batch beyond the supported bound
     ]
     for kw in cases:
         desc, keep = _desc(**kw)
@@ -118,6 +120,10 @@ def test_validation_rejects_before_launch():
     sp = B.sfi_support_params(4, 16, 8, 1.5)
     st = lib.sfi_select(C.byref(desc), C.byref(sp), pid, 1, fake, fake, fake, fake, 1 << 40, None)
     assert st == B.SFI_ERR_INVALID_ARG                         # lambda outside [0, 1]
+    for ns, w in ((1 << 31) - 1, 16), (4, (1 << 31) - 1):
+        spw = B.sfi_support_params(ns, w, 8, 0.1)          # window arithmetic would overflow int32
+        st = lib.sfi_select(C.byref(desc), C.byref(spw), pid, 1, fake, fake, fake, fake, 1 << 40, None)
+        assert st == B.SFI_ERR_INVALID_ARG
     sp0 = B.sfi_support_params(0, 0, 0, 0.1)
     st = lib.sfi_fast_step(C.byref(desc), C.byref(sp0), pid, 1, fake, fake, fake, fake, fake, 1 << 40, None)
     assert st == B.SFI_ERR_INVALID_ARG                         # empty support

@@ -128,6 +128,8 @@ def test_validation_rejects_before_launch():
     st = lib.sfi_fast_step(C.byref(desc), C.byref(sp0), pid, 1, fake, fake, fake, fake, fake, 1 << 40, None)
     assert st == B.SFI_ERR_INVALID_ARG                         # empty support
     assert lib.sfi_slow_step(C.byref(desc), pid, 0, fake, fake, None, fake, 0, None) == 0   # nothing to do
+    full, kf = _desc(cap=100, ctx=(100,))                    # no room for another row
+    assert lib.sfi_kv_append(C.byref(full), pid, 1, fake, fake, None) == B.SFI_ERR_INVALID_ARG
     sp = B.sfi_support_params(4, 16, 8, 0.1)
     fused = lib.sfi_slow_step_select
     assert fused(C.byref(desc), C.byref(sp), pid, 1, fake, fake, None, fake, fake, None, None, fake, 1 << 40,

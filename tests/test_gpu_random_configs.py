@@ -1,6 +1,7 @@
 """Seeded random sweep over the whole path: for each drawn configuration
 (dtype, head dim, query/KV heads, ragged batch, sinks, window, top-k, lambda,
-query scale, an unordered subset of rows) one fused refresh and one fast step
+query scale from 0, where every position ties, to 4, an unordered subset of
+rows) one fused refresh and one fast step
 of each kind run on the GPU and are checked against the oracle: dense output,
 mass, support, packed rows, and the fast output over the GPU's own support
 (once that support has passed the support check)."""
@@ -14,7 +15,7 @@ from tests.gpu_helpers import OUT_TOL, check_mass, check_support, np64, oracle_s
 
 pytestmark = pytest.mark.gpu
 
-N_CONFIGS = 64
+N_CONFIGS = 80
 
 
 def draw(seed):
@@ -34,7 +35,7 @@ def draw(seed):
     ids = [int(x) for x in r.permutation(B)[:int(r.integers(1, B + 1))]]
     return dict(dtype=torch.bfloat16 if r.random() < 0.6 else torch.float32, D=int(r.choice([64, 128])),
                 Hkv=Hkv, G=G, cap=cap, ctx=ctx, ns=ns, W=W, k=k, lam=float(r.choice([0.0, 0.1, 0.37, 1.0])),
-                q_scale=float(r.choice([0.5, 2.0, 4.0])), ids=ids)
+                q_scale=float(r.choice([0.0, 0.1, 0.5, 2.0, 4.0])), ids=ids)
 
 
 @pytest.mark.parametrize("seed", range(N_CONFIGS))

@@ -4,7 +4,8 @@ query scale from 0, where every position ties, to 4, an unordered subset of
 rows) one fused refresh and one fast step
 of each kind run on the GPU and are checked against the oracle: dense output,
 mass, support, packed rows, and the fast output over the GPU's own support
-(once that support has passed the support check)."""
+(once that support has passed the support check).  A second, wider set adds
+contexts up to 300K rows, batches beyond one launch group and larger top-k."""
 import numpy as np
 import pytest
 import torch
@@ -38,9 +39,47 @@ def draw(seed):
                 q_scale=float(r.choice([0.0, 0.1, 0.5, 2.0, 4.0])), ids=ids)
 
 
+N_WIDE = 40
+
+
+def draw_wide(seed):
+    """Wider ranges: contexts up to 300K rows (few rows), or batches of up to
+    71 rows (more than one launch group of 64), top-k up to 20000, windows up
+    to 2000, 100 sinks."""
+    r = np.random.default_rng(50000 + seed)
+    Hkv = int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([1, 2, 4, 8]))
+    big = r.random() < 0.4
+    lo, hi = (20000, 300000) if big else (64, 20000)
+    cap = int(np.exp(r.uniform(np.log(lo), np.log(hi))))
+    B = int(r.integers(1, 4)) if big else int(r.integers(1, 72))
+    if B > 8 and Hkv * G > 16:
+        Hkv, G = 2, 4
+    ctx = [int(x) for x in r.integers(1, cap + 1, size=B)]
+    if r.random() < 0.5:
+        ctx[int(r.integers(0, B))] = cap
+    ns = int(r.choice([0, 1, 4, 16, 100]))
+    W = int(r.choice([0, 1, 64, 256, 511, 2000]))
+    k = int(r.choice([0, 1, 17, 256, 2048, 5000, 20000]))
+    if ns + W + k == 0:
+        k = 8
+    ids = [int(x) for x in r.permutation(B)[:int(r.integers(1, B + 1))]]
+    return dict(dtype=torch.bfloat16 if r.random() < 0.6 else torch.float32, D=int(r.choice([64, 128])),
+                Hkv=Hkv, G=G, cap=cap, ctx=ctx, ns=ns, W=W, k=k, lam=float(r.choice([0.0, 0.1, 0.37, 1.0])),
+                q_scale=float(r.choice([0.0, 0.1, 0.5, 2.0, 4.0])), ids=ids)
+
+
 @pytest.mark.parametrize("seed", range(N_CONFIGS))
 def test_random_config_against_oracle(seed):
-    c = draw(seed)
+    _run(draw(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(N_WIDE))
+def test_wide_random_config_against_oracle(seed):
+    _run(draw_wide(seed), 50000 + seed)
+
+
+def _run(c, seed):
     print("config", seed, {key: v for key, v in c.items() if key != "ctx"}, "ctx", c["ctx"], flush=True)
     B, Hkv, G, D, k = len(c["ctx"]), c["Hkv"], c["G"], c["D"], c["k"]
     kv, q = random_cache(B, G * Hkv, Hkv, c["cap"], D, c["dtype"], c["ctx"], seed=seed, q_scale=c["q_scale"])

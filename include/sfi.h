@@ -107,10 +107,13 @@ typedef struct {
  * for SFI_OP_SLOW.  Returns 0 and sets sfi_last_error() on invalid input. */
 size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp, int32_t op);
 
-/* Zero-fills a workspace (device, ws_bytes).  Optional: every call prepares
- * the parts of the workspace it uses (the Selector's per-head histogram and
- * list counter are cleared by the first kernel of each call that builds
- * them).  Workspaces must not be shared by calls that may run concurrently. */
+/* Zero-fills a workspace (device, ws_bytes).  Call it once on a new
+ * workspace before its first fast step: the fast step counts finished support
+ * chunks per (sequence, KV head) in the workspace, needs those counters at
+ * zero and leaves them at zero.  Every other part is prepared by the call
+ * that uses it (the Selector's per-head histogram and list counter are
+ * cleared by the first kernel of each call that builds them).  Workspaces
+ * must not be shared by calls that may run concurrently. */
 int32_t sfi_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Slow step (dense decode attention over the whole history).
@@ -283,10 +286,13 @@ typedef enum {
   SFI_K_SLOW_PARTIAL = 0, /* split-K dense partials (+ logit scratch) */
   SFI_K_SLOW_COMBINE = 1, /* split merge + per-position mass */
   SFI_K_SELECT = 2,       /* Selector (all of its kernels of one call together) */
-  SFI_K_FAST = 3,         /* sparse attention over support chunks (gather or packed) */
+  SFI_K_FAST = 3,         /* the fast step: sparse attention over support chunks (gather
+                             or packed); a launch that fits the GPU in one pass also
+                             merges the chunks in the same kernel */
   SFI_K_APPEND = 4,
   SFI_K_PACK = 5,         /* packing of the selected rows */
-  SFI_K_FAST_MERGE = 6,   /* merge of the fast step's chunk partials */
+  SFI_K_FAST_MERGE = 6,   /* merge of the fast step's chunk states, for launches with more
+                             workgroups than the GPU has compute units */
   SFI_K_COUNT = 7
 } sfi_kernel_id;
 int32_t sfi_profile_enable(int32_t on);

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -142,17 +143,20 @@ float logit_scale(const sfi_kv_desc* d) {
 // ---- workspace layout -----------------------------------------------------
 // [ header | op scratch ].  The header holds the Selector's per-head
 // bookkeeping (top-digit histogram, list counter), cleared by the first kernel
-// of every call that builds a histogram; it sits at a fixed offset so slow,
-// select and fast calls may share one workspace.
+// of every call that builds a histogram, and the fast step's per-head chunk
+// counters, zero from sfi_workspace_init and left at zero by every fast step;
+// it sits at a fixed offset so slow, select and fast calls may share one
+// workspace.
 struct Header {
-  size_t sel_hist, sel_list_n, end;
+  size_t sel_hist, sel_list_n, fast_ticket, end;
 };
 Header header_layout(const sfi_kv_desc* d) {
   const size_t bh = static_cast<size_t>(d->batch) * d->n_kv_heads;
   Header H;
   H.sel_hist = 0;
   H.sel_list_n = H.sel_hist + align_up(bh * 4096 * sizeof(uint32_t));
-  H.end = H.sel_list_n + align_up(bh * sizeof(int32_t));
+  H.fast_ticket = H.sel_list_n + align_up(bh * sizeof(int32_t));
+  H.end = H.fast_ticket + align_up(bh * kTicketStride * sizeof(int32_t));
   return H;
 }
 size_t header_bytes(const sfi_kv_desc* d) { return header_layout(d).end; }
@@ -275,6 +279,20 @@ bool stream_event(int role, hipEvent_t* out) {
     return false;
   }
   *out = e;
+  return true;
+}
+
+// Compute units of the current device (queried once per device).
+bool compute_units(int* out) {
+  static std::atomic<int> cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return false;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
   return true;
 }
 
@@ -719,10 +737,17 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
       a.tab.ent[i].nsplit = fast_chunks(sp, desc->ctx_len_host[b], crow);
       a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
     }
+    // a launch that fits the chip in one pass merges its chunks in the same
+    // kernel; a larger one hands them to the merge kernel
+    const int grid = a.tab.wg_begin[cnt];
+    int cus = 0;
+    if (!compute_units(&cus)) return fail(SFI_ERR_HIP, "could not query the device's compute units");
+    const bool fused = grid <= cus;
+    a.ticket = fused ? reinterpret_cast<int32_t*>(w + header_layout(desc).fast_ticket) : nullptr;
     hipError_t e = timed(SFI_K_FAST, s, [&] {
-      return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, a.tab.wg_begin[cnt], s);
+      return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, grid, s);
     });
-    if (e == hipSuccess)
+    if (e == hipSuccess && !fused)
       e = timed(SFI_K_FAST_MERGE, s, [&] { return launch_fast_merge(a, desc->head_dim, G, s); });
     return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
   });

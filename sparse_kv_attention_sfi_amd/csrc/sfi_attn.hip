@@ -466,15 +466,15 @@ __device__ __forceinline__ void merge_waves_to_global(const float* sm, const flo
   }
 }
 
-// merge_waves_to_global for wave states of RG row groups each, wave w's at
-// so[w * wave_stride + (rg * G + h) * D + d] (finish_wave_lds: wave_stride =
+// Merge of the NW wave states of a workgroup, each of RG row groups, wave w's
+// at so[w * wave_stride + (rg * G + h) * D + d] (finish_wave_lds: wave_stride =
 // RG * G * D; finish_wave_mfma: RG = 1).  Each thread owns four consecutive
-// columns of one head: it scales the NW wave states once and reads and stores
-// 16-byte vectors.
-template <int D, int G, int NW, int RG>
-__device__ __forceinline__ void merge_wave_groups_to_global(const float* sm, const float* sl, const float* so,
-                                                            int wave_stride, float* ml, int64_t ml_stride,
-                                                            float* o, int64_t o_stride, int tid, int nthreads) {
+// columns of one head: it scales the NW wave states once and reads 16-byte
+// vectors, then hands emit(h, d, acc, M, L) the merged un-normalised output
+// quad at column d, the head's running max and its sum.
+template <int D, int G, int NW, int RG, typename Emit>
+__device__ __forceinline__ void merge_wave_groups(const float* sm, const float* sl, const float* so,
+                                                  int wave_stride, int tid, int nthreads, Emit emit) {
   constexpr int Q = D / 4;  // column quads per head
   for (int idx = tid; idx < G * Q; idx += nthreads) {
     const int h = idx / Q, d = 4 * (idx - h * Q);
@@ -499,11 +499,7 @@ __device__ __forceinline__ void merge_wave_groups_to_global(const float* sm, con
         L += sl[w * G + h] * sc;
       }
     }
-    *reinterpret_cast<float4*>(o + h * o_stride + d) = acc;
-    if (d == 0) {
-      ml[h * ml_stride] = M;
-      ml[h * ml_stride + 1] = L;
-    }
+    emit(h, d, acc, M, L);
   }
 }
 
@@ -607,12 +603,13 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   if (buffered) {
     __syncthreads();
     const int rows = r_end - r_begin;
-    constexpr int Q = kLogitBufRows / 4;
-    for (int idx = threadIdx.x; idx < G * Q; idx += kSlowThreads) {
-      const int h = idx / Q, r = 4 * (idx - h * Q);
-      if (r < rows) {
+    // head h is uniform across the workgroup, so the buffer descriptor of its
+    // logit row is too (one scalar descriptor per store instruction)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = a.logits + (qh0 + h) * a.logit_pitch + r_begin;  // this split's logits of head h
+      for (int r = 4 * threadIdx.x; r < rows; r += 4 * kSlowThreads) {
         const float4 v = *reinterpret_cast<const float4*>(s_lg + h * kLogitBufRows + r);
-        float* dst = a.logits + (qh0 + h) * a.logit_pitch + r_begin;  // this split's logits of head h
         if (r + 4 <= rows) {
           st16_wt(dst, 4 * rows, 4 * r, v);
         } else {
@@ -938,12 +935,120 @@ constexpr bool fast_pv_mfma() {
   return Elem<E>::kBytes == 2 && TILES % 2 == 0;
 }
 
+// Shared memory of the fast step's tail: the last workgroup of a head merges
+// the chunk states of its kFastThreads / (G * D / 4) slot subsets through it.
+struct FastTailSmem {
+  float m[kFastThreads];
+  float l[kFastThreads];
+  float4 o[kFastThreads];
+  int last;
+};
+
+// Merge of the nchunk chunk states of the G query heads of one (sequence, KV
+// head) into the output, renormalised over the whole support.  Thread
+// (sub, h, c4) merges slots sub, sub + NSUB, ... of head h's column quad c4
+// online (running max), in batches whose loads are issued together; the NSUB
+// subset states are then combined through LDS.  COHERENT: the states were
+// published by other workgroups of the running kernel and are read with
+// device-coherent loads; otherwise a previous kernel wrote them.  Both the
+// in-kernel merge and the merge kernel run this code with kFastThreads
+// threads, so they give the same bits.
+template <int D, int G, bool COHERENT>
+__device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t qh0, int nchunk, FastTailSmem& sh,
+                                                 int tid) {
+  constexpr int C4 = D / 4;
+  constexpr int NC = G * C4;  // column quads of the group: 16 ... 256
+  constexpr int NSUB = kFastThreads / NC;
+  static_assert(NSUB >= 1 && NSUB * NC == kFastThreads, "whole column quads per thread");
+  constexpr int kBatch = 16;
+  const int col = tid % NC, sub = tid / NC;
+  const int h = col / C4, c4 = col - h * C4;
+  // one buffer descriptor per workgroup (its G heads' rows), so every load
+  // takes a scalar descriptor; lanes differ only in their offsets
+  const float* mlg = a.part_ml + qh0 * a.part_stride * 2;
+  const float* og = a.part_o + qh0 * a.part_stride * D;
+  const int ml_bytes = G * a.part_stride * 8, o_bytes = G * a.part_stride * D * 4;
+  const int ml_off = h * a.part_stride * 8, o_off = (h * a.part_stride * D + 4 * c4) * 4;
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = sub; s0 < nchunk; s0 += kBatch * NSUB) {
+    float2 ml[kBatch];
+    float4 o[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sl = s0 + u * NSUB;
+      if (sl < nchunk) {
+        if constexpr (COHERENT) {
+          ml[u] = ld8_dev(mlg, ml_bytes, ml_off + sl * 8);
+          o[u] = ld16_dev(og, o_bytes, o_off + sl * D * 4);
+        } else {
+          ml[u] = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(mlg) + ml_off + sl * 8);
+          o[u] = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(og) + o_off + sl * D * 4);
+        }
+      } else {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, ml[u].x);
+    if (mb == -INFINITY) continue;
+    if (M != mb) {
+      const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mb);
+      acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+      L *= sc;
+      M = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (ml[u].x == -INFINITY) continue;
+      const float w = fast_exp2(ml[u].x - M);
+      acc.x += w * o[u].x; acc.y += w * o[u].y; acc.z += w * o[u].z; acc.w += w * o[u].w;
+      L += w * ml[u].y;
+    }
+  }
+  if constexpr (NSUB > 1) {
+    sh.m[tid] = M;
+    sh.l[tid] = L;
+    sh.o[tid] = acc;
+    __syncthreads();
+    if (sub != 0) return;
+#pragma unroll
+    for (int u = 1; u < NSUB; ++u) {
+      const float mu = sh.m[u * NC + col];
+      if (mu == -INFINITY) continue;
+      const float mn = fmaxf(M, mu);
+      const float s_old = M == -INFINITY ? 0.f : fast_exp2(M - mn), s_new = fast_exp2(mu - mn);
+      const float4 ou = sh.o[u * NC + col];
+      acc.x = acc.x * s_old + ou.x * s_new; acc.y = acc.y * s_old + ou.y * s_new;
+      acc.z = acc.z * s_old + ou.z * s_new; acc.w = acc.w * s_old + ou.w * s_new;
+      L = L * s_old + sh.l[u * NC + col] * s_new;
+      M = mn;
+    }
+  }
+  const float il = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<float4*>(a.out + (qh0 + h) * D + 4 * c4) = make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+}
+
 // Tail of a fast-step workgroup: every wave's state to LDS, then the merge of
-// the NW wave states into the chunk's partial slot.  On the MFMA path a wave's
-// output slot reuses its own V staging rows (its reads of them are complete).
+// the NW wave states.  A support of one chunk writes the output directly.
+// Otherwise the chunk state is published for the merge:
+//  * launches that fit the chip in one pass (a.ticket set) merge in the same
+//    kernel: the workgroup publishes with device-coherent stores, waits for
+//    them to complete and takes a ticket from the head's counter; the one
+//    that draws the last ticket merges every chunk state into the output and
+//    resets the counter to zero for the next call.  Nothing waits on another
+//    workgroup, and no L2 write-back or invalidate is needed.
+//  * larger launches store plainly and fast_merge_kernel merges afterwards:
+//    there the wait for the stores and the ticket would hold a CU slot that
+//    the next workgroup could already use.
+// On the MFMA path a wave's output slot reuses its own V staging rows (its
+// reads of them are complete).
 template <typename A, int D, int G, int NW, int ROWS, bool MFMA>
-__device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v, int wave,
-                                            int lane, int tid, const FastArgs& a, int64_t qh0, int chunk) {
+__device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v, FastTailSmem& sh,
+                                            int wave, int lane, int tid, const FastArgs& a, int64_t bg, int64_t qh0,
+                                            int chunk, int nchunk) {
   constexpr int kWaveBytes = ROWS * A::kRowBytes;
   if constexpr (MFMA) {
     wave_sync();
@@ -952,18 +1057,45 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
     st.finish_wave_lds(s_m, s_l, s_o, wave, lane);
   }
   __syncthreads();
-  const int64_t slot = qh0 * a.part_stride + chunk;
-  float* ml = a.part_ml + slot * 2;
-  float* o = a.part_o + slot * D;
-  const int64_t ml_stride = static_cast<int64_t>(a.part_stride) * 2;
-  const int64_t o_stride = static_cast<int64_t>(a.part_stride) * D;
-  if constexpr (MFMA) {
-    merge_wave_groups_to_global<D, G, NW, 1>(s_m, s_l, reinterpret_cast<const float*>(s_v), kWaveBytes / 4, ml,
-                                             ml_stride, o, o_stride, tid, kFastThreads);
-  } else {
-    merge_wave_groups_to_global<D, G, NW, A::kRowGroups>(s_m, s_l, s_o, A::kRowGroups * G * D, ml, ml_stride, o,
-                                                         o_stride, tid, kFastThreads);
+  const float* so = MFMA ? reinterpret_cast<const float*>(s_v) : s_o;
+  constexpr int kStride = MFMA ? kWaveBytes / 4 : A::kRowGroups * G * D;
+  constexpr int RG = MFMA ? 1 : A::kRowGroups;
+  if (nchunk == 1) {
+    merge_wave_groups<D, G, NW, RG>(s_m, s_l, so, kStride, tid, kFastThreads,
+                                    [&](int h, int d, float4 acc, float, float L) {
+                                      const float il = L > 0.f ? 1.f / L : 0.f;
+                                      *reinterpret_cast<float4*>(a.out + (qh0 + h) * D + d) =
+                                          make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+                                    });
+    return;
   }
+  // one buffer descriptor per workgroup (its G heads' rows)
+  float* mlg = a.part_ml + qh0 * a.part_stride * 2;
+  float* og = a.part_o + qh0 * a.part_stride * D;
+  if (a.ticket == nullptr) {
+    merge_wave_groups<D, G, NW, RG>(s_m, s_l, so, kStride, tid, kFastThreads,
+                                    [&](int h, int d, float4 acc, float M, float L) {
+                                      *reinterpret_cast<float4*>(og + (h * a.part_stride + chunk) * D + d) = acc;
+                                      if (d == 0)
+                                        *reinterpret_cast<float2*>(mlg + (h * a.part_stride + chunk) * 2) =
+                                            make_float2(M, L);
+                                    });
+    return;
+  }
+  const int ml_bytes = G * a.part_stride * 8, o_bytes = G * a.part_stride * D * 4;
+  merge_wave_groups<D, G, NW, RG>(s_m, s_l, so, kStride, tid, kFastThreads,
+                                  [&](int h, int d, float4 acc, float M, float L) {
+                                    st16_dev(og, o_bytes, ((h * a.part_stride + chunk) * D + d) * 4, acc);
+                                    if (d == 0) st8_dev(mlg, ml_bytes, (h * a.part_stride + chunk) * 8, make_float2(M, L));
+                                  });
+  wait_vmem();  // this thread's chunk-state stores have completed
+  __syncthreads();
+  int32_t* ticket = a.ticket + bg * kTicketStride;
+  if (tid == 0) sh.last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nchunk - 1;
+  __syncthreads();
+  if (!sh.last) return;
+  fast_merge_slots<D, G, true>(a, qh0, nchunk, sh, tid);
+  if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename E, int D, int G, int TILES, bool ONE>
@@ -981,6 +1113,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
   __shared__ __attribute__((aligned(16))) char s_v[kMfma ? NW * ROWS * A::kRowBytes : 16];
   __shared__ float s_m[NW * G], s_l[NW * G];
   __shared__ int s_pos[CH];
+  __shared__ FastTailSmem s_tail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
@@ -1043,7 +1176,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
       }
     }
   }
-  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, wave, lane, tid, a, qh0, chunk);
+  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a, bg, qh0, chunk, nchunk);
 }
 
 // Fast step over the packed support: the selected rows were copied into a
@@ -1066,6 +1199,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   __shared__ __attribute__((aligned(16))) float s_o[kMfma ? 4 : NW * A::kRowGroups * G * D];
   __shared__ __attribute__((aligned(16))) char s_v[kMfma ? NW * ROWS * A::kRowBytes : 16];
   __shared__ float s_m[NW * G], s_l[NW * G];
+  __shared__ FastTailSmem s_tail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
@@ -1128,6 +1262,12 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   bool kvalid[TILES];
 #pragma unroll
   for (int tt = 0; tt < TILES; ++tt) kvalid[tt] = (w0 + 16 * tt + kr) < size;
+  // Rows past the support (packed slots cnt .. kmax - 1 were not written by
+  // this span's selection) get zero V: their probability is zero, but 0 * V
+  // would still turn a non-finite stale value into NaN.
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (w0 + vr + A::kRPL * i >= size) vb[i] = make_uint4(0u, 0u, 0u, 0u);
   if (w0 < size) {
     if constexpr (kMfma) {
       st.template consume_pv_mfma<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, s_v + wave * ROWS * RB,
@@ -1137,7 +1277,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
                                        lane);
     }
   }
-  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, wave, lane, tid, a, qh0, chunk);
+  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a, bg, qh0, chunk, nchunk);
 }
 
 // Copies the selected K/V rows of each (sequence, KV head) into the packed
@@ -1195,19 +1335,19 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 }
 
-// Merge of the chunk partials of one (sequence, KV head): the output of its G
-// query heads, renormalised over the whole support.
+// Merge of the chunk states of one (sequence, KV head) after a fast-step
+// launch that published them with plain stores: the output of its G query
+// heads, renormalised over the whole support.
 template <int D, int G, bool ONE>
-__global__ __launch_bounds__(kMergeThreads) void fast_merge_kernel(FastArgs a) {
-  __shared__ MergeSmem<G, kMergeThreads> s_merge;
+__global__ __launch_bounds__(kFastThreads) void fast_merge_kernel(FastArgs a) {
+  __shared__ FastTailSmem s_tail;
   const int e = ONE ? 0 : blockIdx.x / a.n_kv_heads;
   const int g = ONE ? blockIdx.x : blockIdx.x - e * a.n_kv_heads;
   const int b = a.tab.ent[e].seq;
   const int nchunk = a.tab.ent[e].nsplit;
+  if (nchunk == 1) return;  // the partial kernel wrote the output
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
-  const int64_t ml_hstride = static_cast<int64_t>(a.part_stride) * 2;
-  merge_partials<D, G, kMergeThreads>(a.part_ml + qh0 * ml_hstride, ml_hstride, a.part_o + qh0 * a.part_stride * D,
-                                      static_cast<int64_t>(a.part_stride) * D, nchunk, a.out + qh0 * D, s_merge);
+  fast_merge_slots<D, G, false>(a, qh0, nchunk, s_tail, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1359,10 +1499,10 @@ template <int D, bool ONE>
 static hipError_t fast_merge_one(const FastArgs& a, int group, hipStream_t s) {
   const int grid = a.tab.n * a.n_kv_heads;
   switch (group) {
-    case 1: launch(fast_merge_kernel<D, 1, ONE>, grid, kMergeThreads, s, a); break;
-    case 2: launch(fast_merge_kernel<D, 2, ONE>, grid, kMergeThreads, s, a); break;
-    case 4: launch(fast_merge_kernel<D, 4, ONE>, grid, kMergeThreads, s, a); break;
-    case 8: launch(fast_merge_kernel<D, 8, ONE>, grid, kMergeThreads, s, a); break;
+    case 1: launch(fast_merge_kernel<D, 1, ONE>, grid, kFastThreads, s, a); break;
+    case 2: launch(fast_merge_kernel<D, 2, ONE>, grid, kFastThreads, s, a); break;
+    case 4: launch(fast_merge_kernel<D, 4, ONE>, grid, kFastThreads, s, a); break;
+    case 8: launch(fast_merge_kernel<D, 8, ONE>, grid, kFastThreads, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

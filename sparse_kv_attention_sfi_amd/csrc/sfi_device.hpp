@@ -60,6 +60,41 @@ __device__ __forceinline__ void st4_wt(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Device-coherent accesses: cache policy sc1, the bits the gfx950 memory model
+// gives relaxed agent-scope atomic loads and stores, so a store is visible to
+// a later sc1 load from any XCD without an L2 write-back or invalidate.  The
+// fast step's workgroups publish their partial states this way and the last
+// one of a head reads them back this way.  `bytes` bounds the buffer that
+// starts at `base`; accesses at byte offset `off`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+constexpr int kCpolDevice = 16;  // sc1
+__device__ __forceinline__ void st16_dev(float* base, int32_t bytes, int32_t off, float4 v) {
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4 d = {static_cast<int>(__float_as_uint(v.x)), static_cast<int>(__float_as_uint(v.y)),
+                static_cast<int>(__float_as_uint(v.z)), static_cast<int>(__float_as_uint(v.w))};
+  __builtin_amdgcn_raw_buffer_store_b128(d, buf_rsrc(base, bytes), off, 0, kCpolDevice);
+}
+__device__ __forceinline__ void st8_dev(float* base, int32_t bytes, int32_t off, float2 v) {
+  typedef int i2 __attribute__((ext_vector_type(2)));
+  const i2 d = {static_cast<int>(__float_as_uint(v.x)), static_cast<int>(__float_as_uint(v.y))};
+  __builtin_amdgcn_raw_buffer_store_b64(d, buf_rsrc(base, bytes), off, 0, kCpolDevice);
+}
+__device__ __forceinline__ float4 ld16_dev(const float* base, int32_t bytes, int32_t off) {
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4 d = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(base, bytes), off, 0, kCpolDevice);
+  return make_float4(__int_as_float(d.x), __int_as_float(d.y), __int_as_float(d.z), __int_as_float(d.w));
+}
+__device__ __forceinline__ float2 ld8_dev(const float* base, int32_t bytes, int32_t off) {
+  typedef int i2 __attribute__((ext_vector_type(2)));
+  const i2 d = __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(base, bytes), off, 0, kCpolDevice);
+  return make_float2(__int_as_float(d.x), __int_as_float(d.y));
+}
+// s_waitcnt vmcnt(0): this wave's earlier vector memory accesses, stores
+// included, have completed (expcnt and lgkmcnt fields left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float4 ld16_stream_f(const float* p) {
   const uint4 u = ld16_stream(p);
   return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));

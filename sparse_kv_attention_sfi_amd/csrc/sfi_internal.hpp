@@ -27,11 +27,11 @@ constexpr int kSelThreads = 512;     // Selector workgroups
 constexpr int kSelListCap = 8192;    // threshold-bin keys resolved in LDS
 constexpr int kSelMaxChunks = 1024;  // candidate chunks per (sequence, KV head)
 constexpr int kSelMinChunk = 4096;   // candidates per chunk (at least)
-constexpr int kFastThreads = 256;    // 4 waves, gather kernel
-constexpr int kMergeThreads = 1024;  // fast-step chunk merge
+constexpr int kFastThreads = 256;    // 4 waves, fast-step kernels
 constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a merge accepts
 constexpr int kSlowTargetWgs = 1024;  // slow partial workgroups aimed at per launch
 constexpr int kLogitBufRows = 1024;   // slow partial: a split's logits are buffered in LDS up to this size
+constexpr int kTicketStride = 32;     // fast-step chunk counters, one per 128-byte line
 
 // One launch's rows.  A row's fields sit together in one 16-byte record, so
 // a workgroup fetches them with one scalar load.
@@ -131,8 +131,10 @@ struct FastArgs {
   const void* q;
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
-  float* part_ml;   // [B][Hq][part_stride][2]
+  float* part_ml;   // [B][Hq][part_stride][2]  chunk states (device-coherent)
   float* part_o;    // [B][Hq][part_stride][D]
+  int32_t* ticket;  // [B * Hkv][kTicketStride] chunks finished (element 0), zero between calls;
+                    // nullptr: publish plainly for fast_merge_kernel
   float* out;
   int64_t t_cap;
   int32_t n_q_heads;

@@ -197,6 +197,27 @@ int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* 
                              const void* packed_k, const void* packed_v, const int32_t* sel_cnt,
                              float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* sfi_fast_step_packed without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  It launches the same kernels with the same launch
+ * shape (so it writes the same bits) and allocates nothing: its chunk states
+ * and per-head counters live in a fixed scratch array of the library,
+ * SFI_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held until the process
+ * ends.  Its address is looked up on the first call on each device; that
+ * call also enqueues a small kernel on `stream` that zeroes the counters.
+ * Every call on a GPU shares that GPU's array: calls that may overlap in time
+ * on one GPU (other streams, other threads) race and must not be issued.
+ * Limits (SFI_ERR_UNSUPPORTED before anything is enqueued): n_seq <= 64,
+ * n_seq * n_kv_heads <= 1024, and n_seq * n_q_heads * chunks * (head_dim + 2)
+ * * 4 bytes of chunk states (chunks: ceil((n_sink + n_recent + top_k) / 128),
+ * the fast step's largest plan) within the array after its 128 KiB of
+ * counters. */
+#define SFI_NOALLOC_SCRATCH_BYTES (16u << 20)
+int32_t sfi_fast_step_packed_noalloc(const sfi_kv_desc* desc, const sfi_support_params* sp,
+                                     const int32_t* seq_ids_host, int32_t n_seq, const void* q,
+                                     const void* packed_k, const void* packed_v,
+                                     const int32_t* sel_cnt, float* out, void* stream);
+
 /* The slow step and the Selector in one call, with the selected rows packed
  * as they are chosen: the whole refresh that opens a span ("Slow-Fast
  * Inference ...", gist.science technical summary, 2.A and 2.B; packing: 3

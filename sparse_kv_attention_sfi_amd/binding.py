@@ -69,6 +69,7 @@ def lib():
             "sfi_kv_append": (I32, [D, P(I32), I32, VP, VP, VP]),
             "sfi_pack_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP]),
             "sfi_fast_step_packed": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
+            "sfi_fast_step_packed_noalloc": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP]),
             "sfi_slow_plan": (I32, [D, P(I32), I32, I32, P(I32)]),
             "sfi_fast_plan": (I32, [D, S, P(I32), I32, P(I32)]),
             "sfi_slow_step_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
@@ -321,6 +322,22 @@ def sfi_fast_step_packed(kv: KVDesc, sp, seq_ids, q, packed_k, packed_v, sel_cnt
     _check(lib().sfi_fast_step_packed(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(packed_k),
                                       _ptr(packed_v), _ptr(sel_cnt), _ptr(out), _ptr(ws), nbytes,
                                       _stream(stream)), "sfi_fast_step_packed")
+
+
+def sfi_fast_step_packed_noalloc(kv: KVDesc, sp, seq_ids, q, packed_k, packed_v, sel_cnt, out, stream=None):
+    """sfi_fast_step_packed with the library's fixed per-device scratch in
+    place of a workspace (the call allocates nothing)."""
+    import torch
+    B, Hq, Hkv, D = kv.batch, kv.n_q_heads, kv.n_kv_heads, kv.head_dim
+    _need(q, kv.dtype, (B, Hq, D), "q")
+    _need(out, torch.float32, (B, Hq, D), "out")
+    _need(packed_k, kv.dtype, (B, Hkv, sp.top_k, D), "packed_k")
+    _need(packed_v, kv.dtype, (B, Hkv, sp.top_k, D), "packed_v")
+    _need(sel_cnt, torch.int32, (B, Hkv), "sel_cnt")
+    _, ids, n = _ids(seq_ids)
+    _check(lib().sfi_fast_step_packed_noalloc(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(packed_k),
+                                              _ptr(packed_v), _ptr(sel_cnt), _ptr(out), _stream(stream)),
+           "sfi_fast_step_packed_noalloc")
 
 
 def sfi_kv_append(kv: KVDesc, seq_ids, k_new, v_new, stream=None):

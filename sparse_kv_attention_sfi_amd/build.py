@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsfi.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["sfi_attn.hip", "sfi_select.hip", "sfi_api.cpp", "sfi_sched.cpp"]
+SOURCES = ["sfi_attn.hip", "sfi_select.hip", "sfi_static.hip", "sfi_api.cpp", "sfi_sched.cpp"]
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -21,9 +21,11 @@
 
 namespace sfi {
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
+// Records the message for sfi_last_error() (per calling thread) and returns
+// the status.
 int32_t fail(int32_t status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -33,6 +35,8 @@ int32_t fail(int32_t status, const char* fmt, ...) {
   g_last_error = buf;
   return status;
 }
+
+namespace {
 
 int32_t hip_fail(hipError_t e, const char* what) {
   return fail(SFI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -123,6 +127,26 @@ int32_t check_seqs(const sfi_kv_desc* d, const int32_t* ids, int32_t n, bool nee
   return SFI_OK;
 }
 
+// check_seqs for at most kMaxSeqPerLaunch ids, with the context lengths
+// required, without allocating (pairwise duplicate test).
+int32_t check_seqs_small(const sfi_kv_desc* d, const int32_t* ids, int32_t n, int32_t min_ctx, int64_t max_ctx) {
+  if (n < 0) return fail(SFI_ERR_INVALID_ARG, "n_seq must be >= 0 (got %d)", n);
+  if (n > kMaxSeqPerLaunch) return fail(SFI_ERR_UNSUPPORTED, "n_seq %d exceeds %d", n, kMaxSeqPerLaunch);
+  if (n == 0) return SFI_OK;
+  if (ids == nullptr) return fail(SFI_ERR_INVALID_ARG, "seq_ids_host is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = ids[i];
+    if (b < 0 || b >= d->batch) return fail(SFI_ERR_INVALID_ARG, "seq id %d out of range [0, %d)", b, d->batch);
+    for (int32_t j = 0; j < i; ++j)
+      if (ids[j] == b) return fail(SFI_ERR_INVALID_ARG, "seq id %d listed twice", b);
+    const int32_t t = d->ctx_len_host[b];
+    if (t < min_ctx || t > max_ctx)
+      return fail(SFI_ERR_INVALID_ARG, "ctx_len[%d] = %d out of range [%d, %lld]", b, t, min_ctx,
+                  static_cast<long long>(max_ctx));
+  }
+  return SFI_OK;
+}
+
 int32_t check_params(const sfi_support_params* sp) {
   if (sp == nullptr) return fail(SFI_ERR_INVALID_ARG, "support params are NULL");
   if (sp->n_sink < 0 || sp->n_recent < 0 || sp->top_k < 0)
@@ -147,6 +171,9 @@ float logit_scale(const sfi_kv_desc* d) {
 // counters, zero from sfi_workspace_init and left at zero by every fast step;
 // it sits at a fixed offset so slow, select and fast calls may share one
 // workspace.
+// Rows whose fast-step chunk states a workspace holds at once: one launch group.
+size_t fast_rows(const sfi_kv_desc* d) { return static_cast<size_t>(std::min(d->batch, kMaxSeqPerLaunch)); }
+
 struct Header {
   size_t sel_hist, sel_list_n, fast_ticket, end;
 };
@@ -156,7 +183,7 @@ Header header_layout(const sfi_kv_desc* d) {
   H.sel_hist = 0;
   H.sel_list_n = H.sel_hist + align_up(bh * 4096 * sizeof(uint32_t));
   H.fast_ticket = H.sel_list_n + align_up(bh * sizeof(int32_t));
-  H.end = H.fast_ticket + align_up(bh * kTicketStride * sizeof(int32_t));
+  H.end = H.fast_ticket + align_up(fast_rows(d) * d->n_kv_heads * kTicketStride * sizeof(int32_t));
   return H;
 }
 size_t header_bytes(const sfi_kv_desc* d) { return header_layout(d).end; }
@@ -219,7 +246,7 @@ struct FastLayout {
 };
 FastLayout fast_layout(const sfi_kv_desc* d, const sfi_support_params* sp) {
   FastLayout L;
-  const size_t heads = static_cast<size_t>(d->batch) * d->n_q_heads;
+  const size_t heads = fast_rows(d) * d->n_q_heads;
   const size_t stride = static_cast<size_t>(fast_part_stride(sp));
   L.part_ml = header_bytes(d);
   L.part_o = L.part_ml + align_up(heads * stride * 2 * sizeof(float));
@@ -267,7 +294,6 @@ thread_local LaunchTiming* g_timing = nullptr;
 // one event per role can be re-recorded by every call.  They live until the
 // process ends: destroying them from a thread-exit destructor could run after
 // the HIP runtime has shut down.
-constexpr int kMaxDevices = 64;
 
 bool stream_event(int role, hipEvent_t* out) {
   thread_local hipEvent_t ev[kMaxDevices][2] = {};
@@ -678,15 +704,20 @@ int32_t sfi_slow_step_select_async(const sfi_kv_desc* desc, const sfi_support_pa
                                ws_bytes, static_cast<hipStream_t>(stream), static_cast<hipStream_t>(select_stream));
 }
 
-static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
-                              int32_t n_seq, const void* q, const int32_t* sel_idx, const void* packed_k,
-                              const void* packed_v, const int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes,
-                              void* stream) {
+// Arguments of a fast step other than its scratch memory.  small_ids: the
+// allocation-free check of at most kMaxSeqPerLaunch ids (no host heap use).
+static int32_t check_fast(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                          int32_t n_seq, const void* q, const int32_t* sel_idx, const void* packed_k,
+                          const void* packed_v, const int32_t* sel_cnt, const float* out, bool small_ids) {
   int32_t st;
   if ((st = check_desc(desc)) != SFI_OK) return st;
   if ((st = check_kv(desc)) != SFI_OK) return st;
   if ((st = check_params(sp)) != SFI_OK) return st;
-  if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) return st;
+  if (small_ids) {
+    if ((st = check_seqs_small(desc, seq_ids, n_seq, 1, desc->kv_capacity)) != SFI_OK) return st;
+  } else if ((st = check_seqs(desc, seq_ids, n_seq, true, 1, desc->kv_capacity)) != SFI_OK) {
+    return st;
+  }
   if (n_seq == 0) return SFI_OK;
   if (q == nullptr || out == nullptr || sel_cnt == nullptr)
     return fail(SFI_ERR_INVALID_ARG, "q / out / sel_cnt is NULL");
@@ -702,54 +733,75 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
   if (static_cast<int64_t>(sp->n_sink) + sp->n_recent + sp->top_k > static_cast<int64_t>(crow) * kMaxMergeSlots)
     return fail(SFI_ERR_UNSUPPORTED, "support of %lld rows exceeds %d",
                 static_cast<long long>(sp->n_sink) + sp->n_recent + sp->top_k, crow * kMaxMergeSlots);
+  return SFI_OK;
+}
+
+// One launch group of a fast step: the sparse-attention kernel, and the merge
+// kernel when the launch does not fit the GPU in one pass.  part_ml / part_o /
+// ticket: the chunk states and per-head counters (zero) for up to cnt rows.
+static int32_t launch_fast_group(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* ids,
+                                 int32_t cnt, const void* q, const int32_t* sel_idx, const void* packed_k,
+                                 const void* packed_v, const int32_t* sel_cnt, float* out, float* part_ml,
+                                 float* part_o, int32_t* ticket, hipStream_t s, bool timing) {
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  const int crow = fast_chunk_rows();
+  FastArgs a{};
+  a.k = desc->k;
+  a.v = desc->v;
+  a.packed_k = packed_k;
+  a.packed_v = packed_v;
+  a.q = q;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.part_ml = part_ml;
+  a.part_o = part_o;
+  a.out = out;
+  a.t_cap = desc->kv_capacity;
+  a.n_q_heads = desc->n_q_heads;
+  a.n_kv_heads = desc->n_kv_heads;
+  a.n_sink = sp->n_sink;
+  a.n_recent = sp->n_recent;
+  a.top_k = sp->top_k;
+  a.chunk_rows = crow;
+  a.part_stride = fast_part_stride(sp);
+  a.scale_log2 = logit_scale(desc);
+  a.tab.n = cnt;
+  a.tab.wg_begin[0] = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const int b = ids[i];
+    a.tab.ent[i].seq = b;
+    a.tab.ent[i].ctx = desc->ctx_len_host[b];
+    a.tab.ent[i].nsplit = fast_chunks(sp, desc->ctx_len_host[b], crow);
+    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
+  }
+  // a launch that fits the chip in one pass merges its chunks in the same
+  // kernel; a larger one hands them to the merge kernel
+  const int grid = a.tab.wg_begin[cnt];
+  int cus = 0;
+  if (!compute_units(&cus)) return fail(SFI_ERR_HIP, "could not query the device's compute units");
+  const bool fused = grid <= cus;
+  a.ticket = fused ? ticket : nullptr;
+  auto partial = [&] { return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, grid, s); };
+  auto merge = [&] { return launch_fast_merge(a, desc->head_dim, G, s); };
+  hipError_t e = timing ? timed(SFI_K_FAST, s, partial) : partial();
+  if (e == hipSuccess && !fused) e = timing ? timed(SFI_K_FAST_MERGE, s, merge) : merge();
+  return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
+}
+
+static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                              int32_t n_seq, const void* q, const int32_t* sel_idx, const void* packed_k,
+                              const void* packed_v, const int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  int32_t st = check_fast(desc, sp, seq_ids, n_seq, q, sel_idx, packed_k, packed_v, sel_cnt, out, false);
+  if (st != SFI_OK || n_seq == 0) return st;
   const FastLayout L = fast_layout(desc, sp);
   if ((st = check_ws(ws, ws_bytes, L.end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = desc->n_q_heads / desc->n_kv_heads;
   char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
-    FastArgs a{};
-    a.k = desc->k;
-    a.v = desc->v;
-    a.packed_k = packed_k;
-    a.packed_v = packed_v;
-    a.q = q;
-    a.sel_idx = sel_idx;
-    a.sel_cnt = sel_cnt;
-    a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
-    a.part_o = reinterpret_cast<float*>(w + L.part_o);
-    a.out = out;
-    a.t_cap = desc->kv_capacity;
-    a.n_q_heads = desc->n_q_heads;
-    a.n_kv_heads = desc->n_kv_heads;
-    a.n_sink = sp->n_sink;
-    a.n_recent = sp->n_recent;
-    a.top_k = sp->top_k;
-    a.chunk_rows = crow;
-    a.part_stride = fast_part_stride(sp);
-    a.scale_log2 = logit_scale(desc);
-    a.tab.n = cnt;
-    a.tab.wg_begin[0] = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const int b = ids[i];
-      a.tab.ent[i].seq = b;
-      a.tab.ent[i].ctx = desc->ctx_len_host[b];
-      a.tab.ent[i].nsplit = fast_chunks(sp, desc->ctx_len_host[b], crow);
-      a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + desc->n_kv_heads * a.tab.ent[i].nsplit;
-    }
-    // a launch that fits the chip in one pass merges its chunks in the same
-    // kernel; a larger one hands them to the merge kernel
-    const int grid = a.tab.wg_begin[cnt];
-    int cus = 0;
-    if (!compute_units(&cus)) return fail(SFI_ERR_HIP, "could not query the device's compute units");
-    const bool fused = grid <= cus;
-    a.ticket = fused ? reinterpret_cast<int32_t*>(w + header_layout(desc).fast_ticket) : nullptr;
-    hipError_t e = timed(SFI_K_FAST, s, [&] {
-      return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, grid, s);
-    });
-    if (e == hipSuccess && !fused)
-      e = timed(SFI_K_FAST_MERGE, s, [&] { return launch_fast_merge(a, desc->head_dim, G, s); });
-    return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
+    return launch_fast_group(desc, sp, ids, cnt, q, sel_idx, packed_k, packed_v, sel_cnt, out,
+                             reinterpret_cast<float*>(w + L.part_ml), reinterpret_cast<float*>(w + L.part_o),
+                             reinterpret_cast<int32_t*>(w + header_layout(desc).fast_ticket), s, true);
   });
 }
 
@@ -767,6 +819,33 @@ int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* 
     return fail(SFI_ERR_INVALID_ARG, "packed_k / packed_v is NULL");
   return fast_step_impl(desc, sp, seq_ids, n_seq, q, nullptr, packed_k, packed_v, sel_cnt, out, ws, ws_bytes,
                         stream);
+}
+
+int32_t sfi_fast_step_packed_noalloc(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                                     int32_t n_seq, const void* q, const void* packed_k, const void* packed_v,
+                                     const int32_t* sel_cnt, float* out, void* stream) {
+  if ((packed_k == nullptr || packed_v == nullptr) && sp != nullptr && sp->top_k > 0)
+    return fail(SFI_ERR_INVALID_ARG, "packed_k / packed_v is NULL");
+  int32_t st = check_fast(desc, sp, seq_ids, n_seq, q, nullptr, packed_k, packed_v, sel_cnt, out, true);
+  if (st != SFI_OK || n_seq == 0) return st;
+  // the chunk states of n_seq rows, after the counter block
+  const size_t heads = static_cast<size_t>(n_seq) * desc->n_q_heads;
+  const size_t stride = static_cast<size_t>(fast_part_stride(sp));
+  const size_t ml_bytes = align_up(heads * stride * 2 * sizeof(float));
+  const size_t o_bytes = align_up(heads * stride * desc->head_dim * sizeof(float));
+  if (static_cast<size_t>(n_seq) * desc->n_kv_heads > kNoAllocCounters)
+    return fail(SFI_ERR_UNSUPPORTED, "n_seq * n_kv_heads = %zu exceeds %d (the fixed scratch's counters)",
+                static_cast<size_t>(n_seq) * desc->n_kv_heads, kNoAllocCounters);
+  if (kNoAllocCounterBytes + ml_bytes + o_bytes > SFI_NOALLOC_SCRATCH_BYTES)
+    return fail(SFI_ERR_UNSUPPORTED, "the chunk states of this call need %zu bytes; the fixed scratch holds %zu",
+                kNoAllocCounterBytes + ml_bytes + o_bytes, static_cast<size_t>(SFI_NOALLOC_SCRATCH_BYTES));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = nullptr;
+  if ((st = noalloc_scratch(s, &w)) != SFI_OK) return st;
+  return launch_fast_group(desc, sp, seq_ids, n_seq, q, nullptr, packed_k, packed_v, sel_cnt, out,
+                           reinterpret_cast<float*>(w + kNoAllocCounterBytes),
+                           reinterpret_cast<float*>(w + kNoAllocCounterBytes + ml_bytes),
+                           reinterpret_cast<int32_t*>(w), s, false);
 }
 
 int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,

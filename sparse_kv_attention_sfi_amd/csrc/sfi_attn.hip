@@ -954,8 +954,8 @@ struct FastTailSmem {
 // in-kernel merge and the merge kernel run this code with kFastThreads
 // threads, so they give the same bits.
 template <int D, int G, bool COHERENT>
-__device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t qh0, int nchunk, FastTailSmem& sh,
-                                                 int tid) {
+__device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t eg, int64_t qh0, int nchunk,
+                                                 FastTailSmem& sh, int tid) {
   constexpr int C4 = D / 4;
   constexpr int NC = G * C4;  // column quads of the group: 16 ... 256
   constexpr int NSUB = kFastThreads / NC;
@@ -965,8 +965,8 @@ __device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t qh0,
   const int h = col / C4, c4 = col - h * C4;
   // one buffer descriptor per workgroup (its G heads' rows), so every load
   // takes a scalar descriptor; lanes differ only in their offsets
-  const float* mlg = a.part_ml + qh0 * a.part_stride * 2;
-  const float* og = a.part_o + qh0 * a.part_stride * D;
+  const float* mlg = a.part_ml + eg * G * a.part_stride * 2;
+  const float* og = a.part_o + eg * G * a.part_stride * D;
   const int ml_bytes = G * a.part_stride * 8, o_bytes = G * a.part_stride * D * 4;
   const int ml_off = h * a.part_stride * 8, o_off = (h * a.part_stride * D + 4 * c4) * 4;
   float M = -INFINITY, L = 0.f;
@@ -1047,7 +1047,7 @@ __device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t qh0,
 // reads of them are complete).
 template <typename A, int D, int G, int NW, int ROWS, bool MFMA>
 __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v, FastTailSmem& sh,
-                                            int wave, int lane, int tid, const FastArgs& a, int64_t bg, int64_t qh0,
+                                            int wave, int lane, int tid, const FastArgs& a, int64_t eg, int64_t qh0,
                                             int chunk, int nchunk) {
   constexpr int kWaveBytes = ROWS * A::kRowBytes;
   if constexpr (MFMA) {
@@ -1070,8 +1070,8 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
     return;
   }
   // one buffer descriptor per workgroup (its G heads' rows)
-  float* mlg = a.part_ml + qh0 * a.part_stride * 2;
-  float* og = a.part_o + qh0 * a.part_stride * D;
+  float* mlg = a.part_ml + eg * G * a.part_stride * 2;
+  float* og = a.part_o + eg * G * a.part_stride * D;
   if (a.ticket == nullptr) {
     merge_wave_groups<D, G, NW, RG>(s_m, s_l, so, kStride, tid, kFastThreads,
                                     [&](int h, int d, float4 acc, float M, float L) {
@@ -1090,11 +1090,11 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
                                   });
   wait_vmem();  // this thread's chunk-state stores have completed
   __syncthreads();
-  int32_t* ticket = a.ticket + bg * kTicketStride;
+  int32_t* ticket = a.ticket + eg * kTicketStride;
   if (tid == 0) sh.last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nchunk - 1;
   __syncthreads();
   if (!sh.last) return;
-  fast_merge_slots<D, G, true>(a, qh0, nchunk, sh, tid);
+  fast_merge_slots<D, G, true>(a, eg, qh0, nchunk, sh, tid);
   if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1176,7 +1176,8 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
       }
     }
   }
-  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a, bg, qh0, chunk, nchunk);
+  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a,
+                                        static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk);
 }
 
 // Fast step over the packed support: the selected rows were copied into a
@@ -1277,7 +1278,8 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
                                        lane);
     }
   }
-  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a, bg, qh0, chunk, nchunk);
+  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a,
+                                        static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk);
 }
 
 // Copies the selected K/V rows of each (sequence, KV head) into the packed
@@ -1347,7 +1349,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_merge_kernel(FastArgs a) {
   const int nchunk = a.tab.ent[e].nsplit;
   if (nchunk == 1) return;  // the partial kernel wrote the output
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
-  fast_merge_slots<D, G, false>(a, qh0, nchunk, s_tail, threadIdx.x);
+  fast_merge_slots<D, G, false>(a, static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, nchunk, s_tail, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -131,9 +131,11 @@ struct FastArgs {
   const void* q;
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
-  float* part_ml;   // [B][Hq][part_stride][2]  chunk states (device-coherent)
-  float* part_o;    // [B][Hq][part_stride][D]
-  int32_t* ticket;  // [B * Hkv][kTicketStride] chunks finished (element 0), zero between calls;
+  // chunk states and counters are indexed by the row's entry in the launch
+  // table (not its batch row), so they scale with kMaxSeqPerLaunch only
+  float* part_ml;   // [entries][Hq][part_stride][2]
+  float* part_o;    // [entries][Hq][part_stride][D]
+  int32_t* ticket;  // [entries * Hkv][kTicketStride] chunks finished (element 0), zero between calls;
                     // nullptr: publish plainly for fast_merge_kernel
   float* out;
   int64_t t_cap;
@@ -186,6 +188,19 @@ struct AppendArgs {
   int32_t n_kv_heads;
   SeqTable tab;
 };
+
+// Devices the host runtime keeps per-device state for.
+constexpr int kMaxDevices = 64;
+
+// Fixed per-device scratch of sfi_fast_step_packed_noalloc: kNoAllocCounters
+// fast-step chunk counters (one per 128-byte line) first, then the chunk
+// states of one call.  noalloc_scratch returns the calling device's address
+// of it, looked up (and its counters cleared on `s`) on the first call on that
+// device; it allocates nothing.
+constexpr int kNoAllocCounters = 1024;
+constexpr size_t kNoAllocCounterBytes = static_cast<size_t>(kNoAllocCounters) * kTicketStride * sizeof(int32_t);
+int32_t noalloc_scratch(hipStream_t s, char** out);
+int32_t fail(int32_t status, const char* fmt, ...);
 
 // Launchers (defined next to their kernels).  They only enqueue; arguments
 // were validated by the caller.  Return the launch's hipError_t.

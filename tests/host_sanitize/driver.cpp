@@ -61,6 +61,32 @@ static void scheduler() {
   CHECK(sfi_sched_create(0, 0, SFI_SPAN_FIXED, 4.0, 0, &s) != SFI_OK);
 }
 
+static void noalloc_limits() {
+  std::vector<int32_t> ctx(65, 100), ids(65);
+  for (int i = 0; i < 65; ++i) ids[i] = i;
+  void* fake = reinterpret_cast<void*>(0x3000);
+  float* ffake = reinterpret_cast<float*>(0x3000);
+  int32_t* ifake = reinterpret_cast<int32_t*>(0x3000);
+  const sfi_support_params sp = {4, 16, 8, 0.1f}, big = {16, 256, 65000, 0.1f};
+  const sfi_kv_desc d65 = desc(65, 8, 2, 64, SFI_F32, 100, ctx.data());
+  CHECK(sfi_fast_step_packed_noalloc(&d65, &sp, ids.data(), 65, fake, fake, fake, ifake, ffake, nullptr) ==
+        SFI_ERR_UNSUPPORTED);
+  const sfi_kv_desc d64 = desc(64, 32, 32, 64, SFI_F32, 100, ctx.data());
+  CHECK(sfi_fast_step_packed_noalloc(&d64, &sp, ids.data(), 64, fake, fake, fake, ifake, ffake, nullptr) ==
+        SFI_ERR_UNSUPPORTED);
+  std::vector<int32_t> ctx16(16, 70000);
+  const sfi_kv_desc d16 = desc(16, 256, 32, 128, SFI_BF16, 70000, ctx16.data());
+  CHECK(sfi_fast_step_packed_noalloc(&d16, &big, ids.data(), 16, fake, fake, fake, ifake, ffake, nullptr) ==
+        SFI_ERR_UNSUPPORTED);
+  const int32_t dup[2] = {1, 1};
+  const sfi_kv_desc d2 = desc(2, 8, 2, 64, SFI_F32, 100, ctx.data());
+  CHECK(sfi_fast_step_packed_noalloc(&d2, &sp, dup, 2, fake, fake, fake, ifake, ffake, nullptr) ==
+        SFI_ERR_INVALID_ARG);
+  // a call that passes validation reaches the scratch lookup (a stub here)
+  CHECK(sfi_fast_step_packed_noalloc(&d2, &sp, ids.data(), 2, fake, fake, fake, ifake, ffake, nullptr) ==
+        SFI_ERR_HIP);
+}
+
 static void validation() {
   const int32_t ctx1[1] = {100};
   const int32_t ctx2[2] = {100, 100};
@@ -136,6 +162,7 @@ static void strings_and_timing() {
 int main() {
   scheduler();
   validation();
+  noalloc_limits();
   strings_and_timing();
   if (g_fail == 0) std::printf("host checks passed\n");
   return g_fail == 0 ? 0 : 1;

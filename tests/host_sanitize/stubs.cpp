@@ -14,4 +14,5 @@ hipError_t launch_pack(const PackArgs&, int, int, int, hipStream_t) { return hip
 hipError_t launch_append(const AppendArgs&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_fill_zero(void*, size_t, hipStream_t) { return hipErrorInvalidValue; }
 int fast_chunk_rows() { return 128; }
+int32_t noalloc_scratch(hipStream_t, char**) { return SFI_ERR_HIP; }
 }  // namespace sfi

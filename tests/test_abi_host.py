@@ -162,6 +162,8 @@ def test_misaligned_buffers_rejected_before_launch():
         "out": lambda: lib.sfi_fast_step(C.byref(desc), C.byref(sp), pid, 1, a, a, a, m8, a, big, None),
         "packed_v": lambda: lib.sfi_fast_step_packed(C.byref(desc), C.byref(sp), pid, 1, a, a, m8, a, a, a, big,
                                                      None),
+        "packed_k": lambda: lib.sfi_fast_step_packed_noalloc(C.byref(desc), C.byref(sp), pid, 1, a, m8, a, a, a,
+                                                             None),
         "sel_cnt": lambda: lib.sfi_pack_support(C.byref(desc), C.byref(sp), pid, 1, a, m2, a, a, None),
         "k_new": lambda: lib.sfi_kv_append(C.byref(_desc(ctx=(99,))[0]), pid, 1, m8, a, None),
         "support_out": lambda: lib.sfi_debug_support(C.byref(desc), C.byref(sp), pid, 1, a, a, m2, a, 64, None),
@@ -261,3 +263,39 @@ def test_fast_plan_chunks_cover_the_support():
     assert sizes == [2320, 2320, 300, 5]
     # 4 waves x 2 tiles x 16 rows = 128 support rows per workgroup by default
     assert out.tolist() == [max(1, -(-s // 128)) for s in sizes]
+
+
+def test_noalloc_fast_step_rejects_what_its_fixed_scratch_cannot_hold():
+    """The fast step without a workspace fails with SFI_ERR_UNSUPPORTED, before
+    anything is enqueued, when the rows, the counters or the chunk states
+    exceed its fixed per-device scratch (fake device addresses: never
+    touched)."""
+    lib = S.lib()
+    a = C.c_void_p(0x3000)
+    call = lib.sfi_fast_step_packed_noalloc
+    # 65 rows: more than one launch group
+    desc, keep = _desc(batch=65, ctx=(100,) * 65)
+    ids = np.arange(65, dtype=np.int32)
+    sp = B.sfi_support_params(4, 16, 8, 0.1)
+    assert call(C.byref(desc), C.byref(sp), ids.ctypes.data_as(C.POINTER(C.c_int32)), 65, a, a, a, a, a,
+                None) == B.SFI_ERR_UNSUPPORTED
+    assert b"64" in lib.sfi_last_error()
+    # 64 rows x 32 KV heads: more chunk counters than the scratch has
+    desc, keep = _desc(batch=64, hq=32, hkv=32, ctx=(100,) * 64)
+    ids = np.arange(64, dtype=np.int32)
+    assert call(C.byref(desc), C.byref(sp), ids.ctypes.data_as(C.POINTER(C.c_int32)), 64, a, a, a, a, a,
+                None) == B.SFI_ERR_UNSUPPORTED
+    assert b"counters" in lib.sfi_last_error()
+    # 16 rows of 256 query heads with a 65536-row support: 136 MB of chunk states
+    desc, keep = _desc(batch=16, hq=256, hkv=32, d=128, dtype=B.SFI_BF16, cap=70000, ctx=(70000,) * 16)
+    ids = np.arange(16, dtype=np.int32)
+    big = B.sfi_support_params(16, 256, 65000, 0.1)
+    assert call(C.byref(desc), C.byref(big), ids.ctypes.data_as(C.POINTER(C.c_int32)), 16, a, a, a, a, a,
+                None) == B.SFI_ERR_UNSUPPORTED
+    assert b"fixed scratch holds" in lib.sfi_last_error()
+    # a duplicate id is caught without the heap-allocating check
+    desc, keep = _desc(batch=2, ctx=(100, 100))
+    dup = np.array([1, 1], dtype=np.int32)
+    assert call(C.byref(desc), C.byref(sp), dup.ctypes.data_as(C.POINTER(C.c_int32)), 2, a, a, a, a, a,
+                None) == B.SFI_ERR_INVALID_ARG
+    assert b"twice" in lib.sfi_last_error()

@@ -62,7 +62,7 @@ extern "C" {
 #endif
 
 #define SFI_VERSION_MAJOR 0
-#define SFI_VERSION_MINOR 3
+#define SFI_VERSION_MINOR 4
 
 typedef enum {
   SFI_OK = 0,
@@ -77,7 +77,18 @@ typedef enum { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
 
 typedef enum { SFI_OP_SLOW = 0, SFI_OP_SELECT = 1, SFI_OP_FAST = 2, SFI_OP_SLOW_SELECT = 3 } sfi_op;
 
-/* One layer's KV cache and the current context lengths. */
+/* One layer's KV cache and the current context lengths.
+ *
+ * Context lengths live on the host (ctx_len_host), or on the device
+ * (ctx_len, "the growing history" of the decode loop: "Slow-Fast Inference
+ * ...", fugumt.com abstract).  With ctx_len == NULL the host values are the
+ * lengths and every call reads them when it is made.  With ctx_len set the
+ * kernels read each row's length from device memory when they run, so one
+ * captured graph serves a history that grows between replays:
+ * sfi_kv_append advances ctx_len[b] by one on the device, and the host values
+ * are only upper bounds the launches are planned for (grid sizes, splits):
+ * every call needs 1 <= ctx_len[b] <= ctx_len_host[b] <= kv_capacity when it
+ * runs, and clamps ctx_len[b] into [1, ctx_len_host[b]]. */
 typedef struct {
   int32_t batch;               /* B */
   int32_t n_q_heads;           /* Hq */
@@ -87,8 +98,9 @@ typedef struct {
   int64_t kv_capacity;         /* T_cap: rows allocated per (b, kv head) */
   void* k;                     /* device [B][Hkv][T_cap][D]; read-only except sfi_kv_append */
   void* v;                     /* device [B][Hkv][T_cap][D]; read-only except sfi_kv_append */
-  const int32_t* ctx_len_host; /* host [B]: valid rows of each sequence (T_b) */
+  const int32_t* ctx_len_host; /* host [B]: valid rows of each sequence (T_b), or their bounds */
   float scale;                 /* logit scale; 0 selects 1/sqrt(D) */
+  int32_t* ctx_len;            /* device [B] (4-byte aligned) or NULL; see above */
 } sfi_kv_desc;
 
 /* The sparse state kept for fast steps: n_sink sink tokens, a recent window
@@ -260,9 +272,13 @@ int32_t sfi_slow_step_select_async(const sfi_kv_desc* desc, const sfi_support_pa
                                    void* stream, void* select_stream);
 
 /* Appends one token per listed sequence: writes k_new[b][g][:] and
- * v_new[b][g][:] (device [B][Hkv][D], kv_dtype) into row ctx_len[b] of
- * desc->k and desc->v.  Requires ctx_len[b] < kv_capacity.  The caller then
- * increments its ctx_len[b]. */
+ * v_new[b][g][:] (device [B][Hkv][D], kv_dtype) into row T_b of desc->k and
+ * desc->v, T_b the sequence's context length.
+ *  - host lengths (desc->ctx_len == NULL): requires ctx_len_host[b] <
+ *    kv_capacity; the caller then increments its ctx_len_host[b].
+ *  - device lengths: T_b = desc->ctx_len[b], read when the kernel runs, and
+ *    the kernel then sets desc->ctx_len[b] = T_b + 1; a row with T_b >=
+ *    kv_capacity is left unchanged. */
 int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids_host, int32_t n_seq,
                       const void* k_new, const void* v_new, void* stream);
 

@@ -36,7 +36,7 @@ class sfi_kv_desc(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("kv_dtype", C.c_int32), ("kv_capacity", C.c_int64),
                 ("k", C.c_void_p), ("v", C.c_void_p), ("ctx_len_host", C.POINTER(C.c_int32)),
-                ("scale", C.c_float)]
+                ("scale", C.c_float), ("ctx_len", C.c_void_p)]
 
 
 class sfi_support_params(C.Structure):
@@ -115,11 +115,14 @@ def _ids(seq_ids):
 
 
 class KVDesc:
-    """One layer's KV cache [B, Hkv, T_cap, D] plus host context lengths.
+    """One layer's KV cache [B, Hkv, T_cap, D] plus context lengths.
 
-    Keeps the ctypes descriptor and the host ctx_len array alive."""
+    ctx_len: host context lengths, or with ``ctx_dev`` (a device int32
+    tensor [B] holding the lengths the kernels read when they run, which
+    sfi_kv_append advances) their upper bounds.  Keeps the ctypes descriptor,
+    the host array and the device tensor alive."""
 
-    def __init__(self, k, v, ctx_len, n_q_heads, scale=0.0):
+    def __init__(self, k, v, ctx_len, n_q_heads, scale=0.0, ctx_dev=None):
         import torch
         if k.shape != v.shape or k.dim() != 4:
             raise ValueError("k and v must both be [B, Hkv, T_cap, D]")
@@ -131,10 +134,14 @@ class KVDesc:
         B, Hkv, cap, D = k.shape
         self.ctx = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int32).reshape(B))
         self.dtype = k.dtype
+        if ctx_dev is not None:
+            _need(ctx_dev, torch.int32, (B,), "ctx_dev")
+        self.ctx_dev = ctx_dev
         self.desc = sfi_kv_desc(B, int(n_q_heads), Hkv, D,
                                 SFI_BF16 if k.dtype == torch.bfloat16 else SFI_F32, cap,
                                 k.data_ptr(), v.data_ptr(),
-                                self.ctx.ctypes.data_as(C.POINTER(C.c_int32)), float(scale))
+                                self.ctx.ctypes.data_as(C.POINTER(C.c_int32)), float(scale),
+                                None if ctx_dev is None else ctx_dev.data_ptr())
 
     @property
     def batch(self):

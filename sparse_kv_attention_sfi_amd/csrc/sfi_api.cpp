@@ -103,6 +103,7 @@ int32_t check_aligned(std::initializer_list<std::pair<const void*, const char*>>
 int32_t check_kv(const sfi_kv_desc* d) {
   if (d->k == nullptr || d->v == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->k / desc->v is NULL");
   if (d->ctx_len_host == nullptr) return fail(SFI_ERR_INVALID_ARG, "desc->ctx_len_host is NULL");
+  if (const int32_t st = check_aligned({{d->ctx_len, "desc->ctx_len"}}, kIntAlign); st != SFI_OK) return st;
   return check_aligned({{d->k, "desc->k"}, {d->v, "desc->v"}}, kVecAlign);
 }
 
@@ -404,8 +405,10 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
   const int64_t per = std::max(want, ceil_div(t_max, kMaxMergeSlots));
   a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
   a.tab.n = cnt;
+  a.tab.ctx_dev = desc->ctx_len;
   a.tab.wg_begin[0] = 0;
   c.tab.n = cnt;
+  c.tab.ctx_dev = desc->ctx_len;
   c.tab.wg_begin[0] = 0;
   for (int i = 0; i < cnt; ++i) {
     const int b = ids[i];
@@ -469,12 +472,18 @@ void plan_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const in
   const int64_t chunk = std::max<int64_t>(kSelMinChunk, ceil_div(ceil_div(n_max, kSelMaxChunks), 512) * 512);
   a.chunk = static_cast<int32_t>(chunk);
   a.tab.n = cnt;
+  a.tab.ctx_dev = desc->ctx_len;
   a.tab.wg_begin[0] = 0;
   for (int i = 0; i < cnt; ++i) {
     const int64_t T = desc->ctx_len_host[ids[i]];
     const int64_t n = std::max<int64_t>(0, T - sp->n_sink - sp->n_recent);
     const bool keep_all = n <= sp->top_k || sp->top_k == 0;
-    const int64_t M = keep_all ? std::max<int64_t>(1, ceil_div(sp->top_k, chunk)) : ceil_div(n, chunk);
+    const int64_t m_keep = std::max<int64_t>(1, ceil_div(sp->top_k, chunk));
+    // device context lengths may be shorter than the bound n was taken from:
+    // the grid then covers both the keep-all emission and the bound's chunks
+    const int64_t M = desc->ctx_len != nullptr ? std::max(m_keep, ceil_div(n, chunk))
+                      : keep_all              ? m_keep
+                                              : ceil_div(n, chunk);
     a.tab.ent[i].seq = ids[i];
     a.tab.ent[i].ctx = static_cast<int32_t>(T);
     a.tab.ent[i].nsplit = static_cast<int32_t>(M);
@@ -766,6 +775,7 @@ static int32_t launch_fast_group(const sfi_kv_desc* desc, const sfi_support_para
   a.part_stride = fast_part_stride(sp);
   a.scale_log2 = logit_scale(desc);
   a.tab.n = cnt;
+  a.tab.ctx_dev = desc->ctx_len;
   a.tab.wg_begin[0] = 0;
   for (int i = 0; i < cnt; ++i) {
     const int b = ids[i];
@@ -876,6 +886,7 @@ int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp, 
     a.n_recent = sp->n_recent;
     a.top_k = sp->top_k;
     a.tab.n = cnt;
+    a.tab.ctx_dev = desc->ctx_len;
     a.tab.wg_begin[0] = 0;
     for (int i = 0; i < cnt; ++i) {
       const int64_t t = desc->ctx_len_host[ids[i]];
@@ -897,7 +908,10 @@ int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
   int32_t st;
   if ((st = check_desc(desc)) != SFI_OK) return st;
   if ((st = check_kv(desc)) != SFI_OK) return st;
-  if ((st = check_seqs(desc, seq_ids, n_seq, true, 0, desc->kv_capacity - 1)) != SFI_OK) return st;
+  // with device context lengths the host values are only bounds: the kernel
+  // skips a row whose device length has reached the capacity
+  const int64_t max_t = desc->ctx_len != nullptr ? desc->kv_capacity : desc->kv_capacity - 1;
+  if ((st = check_seqs(desc, seq_ids, n_seq, true, 0, max_t)) != SFI_OK) return st;
   if (n_seq == 0) return SFI_OK;
   if (k_new == nullptr || v_new == nullptr) return fail(SFI_ERR_INVALID_ARG, "k_new / v_new is NULL");
   if ((st = check_aligned({{k_new, "k_new"}, {v_new, "v_new"}}, kVecAlign)) != SFI_OK) return st;
@@ -911,15 +925,16 @@ int32_t sfi_kv_append(const sfi_kv_desc* desc, const int32_t* seq_ids, int32_t n
     a.t_cap = desc->kv_capacity;
     a.n_kv_heads = desc->n_kv_heads;
     a.tab.n = cnt;
+    a.tab.ctx_dev = desc->ctx_len;
     for (int i = 0; i < cnt; ++i) {
       a.tab.ent[i].seq = ids[i];
       a.tab.ent[i].ctx = desc->ctx_len_host[ids[i]];
       a.tab.ent[i].nsplit = 1;
-      a.tab.wg_begin[i] = i * desc->n_kv_heads;
+      a.tab.wg_begin[i] = i;
     }
-    a.tab.wg_begin[cnt] = cnt * desc->n_kv_heads;
+    a.tab.wg_begin[cnt] = cnt;
     const hipError_t e = timed(SFI_K_APPEND, s, [&] {
-      return launch_append(a, desc->kv_dtype, desc->head_dim, cnt * desc->n_kv_heads, s);
+      return launch_append(a, desc->kv_dtype, desc->head_dim, cnt, s);
     });
     return e == hipSuccess ? SFI_OK : hip_fail(e, "append launch");
   });
@@ -954,6 +969,7 @@ int32_t sfi_debug_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
     a.top_k = sp->top_k;
     a.cap_per_head = cap_per_head;
     a.tab.n = cnt;
+    a.tab.ctx_dev = desc->ctx_len;
     for (int i = 0; i < cnt; ++i) {
       a.tab.ent[i].seq = ids[i];
       a.tab.ent[i].ctx = desc->ctx_len_host[ids[i]];

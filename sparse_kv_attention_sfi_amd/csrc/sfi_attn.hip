@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   const int g = local / nsplit;
   const int split = local - g * nsplit;
   const int b = a.tab.ent[e].seq;
-  const int T = a.tab.ent[e].ctx;
+  const int T = row_ctx(a.tab, e);
   const int r_begin = split * a.split_rows;
   const int r_end = min(T, r_begin + a.split_rows);
   if (a.clear_hist != nullptr && split == 0) {
@@ -816,7 +816,7 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
   const int g = local / per_g;
   const int r = local - g * per_g;
   const int b = a.tab.ent[e].seq;
-  const int T = a.tab.ent[e].ctx;
+  const int T = row_ctx(a.tab, e);
   const int nsplit = a.tab.ent[e].nsplit;
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
   const int64_t ml_hstride = static_cast<int64_t>(a.part_stride) * 2;
@@ -1125,7 +1125,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
   const int g = local / nchunk;
   const int chunk = local - g * nchunk;
   const int b = a.tab.ent[e].seq;
-  const int t = a.tab.ent[e].ctx;
+  const int t = row_ctx(a.tab, e);
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const SupportGeom sg = support_geom(t, a.n_sink, a.n_recent, a.top_k, a.sel_cnt, bg);
   const int32_t* sel_row = a.sel_idx + bg * a.top_k;
@@ -1210,7 +1210,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   const int g = local / nchunk;
   const int chunk = local - g * nchunk;
   const int b = a.tab.ent[e].seq;
-  const int t = a.tab.ent[e].ctx;
+  const int t = row_ctx(a.tab, e);
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const int ns_eff = min(a.n_sink, t);
   const int w_lo = max(a.n_sink, t - a.n_recent);
@@ -1295,7 +1295,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   const int g = local / nchunk;
   const int chunk = local - g * nchunk;
   const int b = a.tab.ent[e].seq;
-  const int t = a.tab.ent[e].ctx;
+  const int t = row_ctx(a.tab, e);
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const int kmax = min(a.top_k, max(0, t - a.n_sink - a.n_recent));
   const int cnt = min(max(a.sel_cnt[bg], 0), kmax);
@@ -1359,7 +1359,7 @@ __global__ __launch_bounds__(256) void support_kernel(SupportArgs a) {
   const int e = blockIdx.x / a.n_kv_heads;
   const int g = blockIdx.x - e * a.n_kv_heads;
   const int b = a.tab.ent[e].seq;
-  const int t = a.tab.ent[e].ctx;
+  const int t = row_ctx(a.tab, e);
   const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
   const SupportGeom sg = support_geom(t, a.n_sink, a.n_recent, a.top_k, a.sel_cnt, bg);
   const int32_t* sel_row = a.sel_idx + bg * a.top_k;
@@ -1372,21 +1372,30 @@ __global__ __launch_bounds__(256) void support_kernel(SupportArgs a) {
 // ---------------------------------------------------------------------------
 // KV append and workspace clearing
 // ---------------------------------------------------------------------------
+// Appends one token to each listed row: K/V of every KV head go to row t of
+// the cache, t = the row's context length.  With device context lengths the
+// row's value is read once by the whole workgroup and then advanced by one in
+// place (a full cache, t >= T_cap, is left unchanged).
 template <int RB>
-__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
-  const int e = blockIdx.x / a.n_kv_heads;
-  const int g = blockIdx.x - e * a.n_kv_heads;
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ int s_t;
+  const int e = blockIdx.x;
   const int b = a.tab.ent[e].seq;
-  const int t = a.tab.ent[e].ctx;
-  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  if (threadIdx.x == 0) s_t = a.tab.ctx_dev != nullptr ? a.tab.ctx_dev[b] : a.tab.ent[e].ctx;
+  __syncthreads();
+  const int t = s_t;
+  if (t < 0 || t >= a.t_cap) return;
   constexpr int NP = RB / 16;
-  for (int i = threadIdx.x; i < 2 * NP; i += 64) {
-    const bool isv = i >= NP;
-    const int pc = isv ? i - NP : i;
+  for (int i = threadIdx.x; i < a.n_kv_heads * 2 * NP; i += 256) {
+    const int g = i / (2 * NP), r = i - g * 2 * NP;
+    const bool isv = r >= NP;
+    const int pc = isv ? r - NP : r;
+    const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
     const char* src = static_cast<const char*>(isv ? a.v_new : a.k_new) + bg * RB + 16 * pc;
     char* dst = static_cast<char*>(isv ? a.v : a.k) + (bg * a.t_cap + t) * RB + 16 * pc;
     *reinterpret_cast<uint4*>(dst) = ld16(src);
   }
+  if (a.tab.ctx_dev != nullptr && threadIdx.x == 0) const_cast<int32_t*>(a.tab.ctx_dev)[b] = t + 1;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t words) {
@@ -1538,9 +1547,9 @@ hipError_t launch_pack(const PackArgs& a, int dtype, int head_dim, int grid, hip
 hipError_t launch_append(const AppendArgs& a, int dtype, int head_dim, int grid, hipStream_t s) {
   const int rb = head_dim * (dtype == SFI_BF16 ? 2 : 4);
   switch (rb) {
-    case 128: launch(append_kernel<128>, grid, 64, s, a); break;
-    case 256: launch(append_kernel<256>, grid, 64, s, a); break;
-    case 512: launch(append_kernel<512>, grid, 64, s, a); break;
+    case 128: launch(append_kernel<128>, grid, 256, s, a); break;
+    case 256: launch(append_kernel<256>, grid, 256, s, a); break;
+    case 512: launch(append_kernel<512>, grid, 256, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -177,6 +177,15 @@ __device__ __forceinline__ float lane_bcast(float x, int lane) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Context length of launch-table entry e: the device value when the table
+// carries one (clamped to [1, the planned bound]), else the planned one.
+template <typename Table>
+__device__ __forceinline__ int row_ctx(const Table& t, int e) {
+  const int bound = t.ent[e].ctx;
+  if (t.ctx_dev == nullptr) return bound;
+  return min(max(t.ctx_dev[t.ent[e].seq], 1), bound);
+}
+
 // Locate the table entry owning workgroup `wg` (tables are short).
 template <typename Table>
 __device__ __forceinline__ int find_entry(const Table& t, int wg) {

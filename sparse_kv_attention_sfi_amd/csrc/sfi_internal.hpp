@@ -44,7 +44,11 @@ struct SeqEntry {
 
 struct SeqTable {
   int32_t n;  // entries used
-  int32_t pad[3];
+  int32_t pad;
+  // device context lengths [B] or nullptr; when set, a row's context length
+  // is read here and its entry's ctx is the upper bound the launch was
+  // planned for (row_ctx clamps to [1, bound])
+  const int32_t* ctx_dev;
   SeqEntry ent[kMaxSeqPerLaunch];
   int32_t wg_begin[kMaxSeqPerLaunch + 1];  // prefix over entries of Hkv * nsplit
 };

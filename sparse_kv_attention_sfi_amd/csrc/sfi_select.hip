@@ -77,7 +77,7 @@ __device__ __forceinline__ HeadCtx head_ctx(const SelectArgs& a) {
   h.g = local / h.M;
   h.c = local - h.g * h.M;
   h.b = a.tab.ent[h.e].seq;
-  h.T = a.tab.ent[h.e].ctx;
+  h.T = row_ctx(a.tab, h.e);
   h.bg = static_cast<int64_t>(h.b) * a.n_kv_heads + h.g;
   h.n = max(0, h.T - a.n_recent - a.n_sink);
   h.keep_all = h.n <= a.top_k || a.top_k == 0;
@@ -252,7 +252,9 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
   __shared__ int s_base;
   __shared__ float s_inv2h;
   const HeadCtx h = head_ctx(a);
-  if (h.keep_all) return;
+  // chunks past the candidates exist only when the grid was planned for a
+  // longer context than the row's device length
+  if (h.keep_all || (h.c > 0 && h.c * a.chunk >= h.n)) return;
   const int tid = threadIdx.x;
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
   // each thread owns a contiguous run of kRun candidates per pass, so its
@@ -396,6 +398,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     return;
   }
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
+  if (h.c > 0 && i0 >= h.n) return;  // past the candidates (grid planned for a longer context)
   const float* frow = a.mass + h.bg * a.t_cap + a.n_sink;
   float fv[kRun];
 #pragma unroll

@@ -29,6 +29,7 @@ static sfi_kv_desc desc(int batch, int hq, int hkv, int d, int dtype, long long 
   x.v = reinterpret_cast<void*>(0x2000);
   x.ctx_len_host = ctx;
   x.scale = 0.f;
+  x.ctx_len = nullptr;
   return x;
 }
 

@@ -178,6 +178,10 @@ def test_misaligned_buffers_rejected_before_launch():
     kd.k = 0x1004
     assert lib.sfi_slow_step(C.byref(kd), pid, 1, a, a, None, a, big, None) == B.SFI_ERR_INVALID_ARG
     assert b"desc->k" in lib.sfi_last_error()
+    kd, keep3 = _desc()
+    kd.ctx_len = 0x1002                      # device context lengths off their 4-byte boundary
+    assert lib.sfi_fast_step(C.byref(kd), C.byref(sp), pid, 1, a, a, a, a, a, big, None) == B.SFI_ERR_INVALID_ARG
+    assert b"desc->ctx_len" in lib.sfi_last_error()
 
 
 def test_fault_injection_fails_select_before_launch(monkeypatch):

@@ -21,10 +21,16 @@ second per layer), with inputs resident in HBM.  Each step's queries are
 staged into fixed buffers and the step is replayed as a HIP graph (one for
 slow steps, one for fast steps).
 
-Also reported: per-kernel average durations from HIP events recorded by the
-library around its launches (eager pass over the same steps), the roofline
-of the dominant kernel, the dense-every-step baseline, and the CPU oracle on
-a bounded sample of the same workload.
+Also reported: the blended rate over the workload's whole span schedule
+(``full_schedule``, at the schedule's own slow fraction, beside
+``slow_fraction_timed`` of the --steps window), per-kernel average durations
+from HIP events recorded by the library around its launches (eager pass over
+the same steps), the roofline of the dominant kernel, the dense-every-step
+baseline, the CPU oracle's per-operation medians on the same workload, and
+(``configs``) SFI against dense decode over the whole schedule of every other
+workload: the 32K layer, the batch of 16 mixed contexts and the 32-layer
+growing-history loop, each replayed from graphs captured per slow/fast row
+pattern.
 """
 from __future__ import annotations
 
@@ -121,8 +127,9 @@ def parse():
                    help="independent layer caches cycled per step for single-layer batched workloads (C4)")
     p.add_argument("--batch-check", type=int, default=16, metavar="B",
                    help="also time the fast step for B sequences in one launch (0: skip)")
-    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-workload block (32K layer, batch 16, 32-layer growing history)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="end with one device copy of MIB MiB (calibrates memory-traffic counters)")
     p.add_argument("--stream-probe", type=int, default=2048, metavar="MIB",
@@ -214,7 +221,7 @@ def main():
         run_batched(args, w, dev)
         return
     L, K, W = args.layers, args.steps, args.warmup
-    n_steps = W + K
+    n_steps = max(W + K, w.n_steps)  # the timed window and the workload's whole schedule
 
     # schedule (host scheduler) and the span index of every step
     sched = S.Scheduler(1, w.seed, w.span_mode, w.span_param)
@@ -303,6 +310,7 @@ def main():
     dense_layers()
     torch.cuda.synchronize()
 
+    graphs = None
     if args.mode == "graph":
         graphs = {}
         for name, fn in (("slow", slow_layers), ("fast", fast_layers), ("dense", dense_layers)):
@@ -328,6 +336,21 @@ def main():
     t_blend = time.perf_counter() - t_start
     n_slow_timed = sum(flags[W:W + K])
     log(f"blended: {K} steps ({n_slow_timed} slow) x {L} layers in {t_blend * 1e3:.1f} ms")
+
+    # The whole span schedule of the workload (its w.n_steps steps), replayed
+    # the same way: the blended rate at the schedule's own slow fraction,
+    # whatever share of slow steps the --steps window above happened to hold.
+    full_flags = flags[:w.n_steps]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for t in range(w.n_steps):
+        q_buf.copy_(q_steps[t])
+        run["slow" if full_flags[t] else "fast"]()
+    torch.cuda.synchronize()
+    t_full = time.perf_counter() - t_start
+    full_schedule = {"steps": w.n_steps, "slow_steps": sum(full_flags),
+                     "slow_fraction": sum(full_flags) / w.n_steps,
+                     "blended_steps_per_s_layer": w.n_steps * L / t_full}
 
     # dense-every-step baseline (same queries)
     kd = min(args.dense_steps, n_steps)
@@ -461,6 +484,8 @@ def main():
                    "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode, "fast_path": args.fast,
                    "slow_path": args.slow,
                    "slow_steps_timed": n_slow_timed},
+        "slow_fraction_timed": n_slow_timed / K,
+        "full_schedule": full_schedule,
         "slow_step_us": slow_us or None,
         "fast_step_us": fast_us or None,
         "slow_steps_per_s_layer": 1e6 / slow_us if slow_us else None,
@@ -497,7 +522,12 @@ def main():
                 sc[f"{key}_vs_copy"] = alg["slow_partial"] / (k["avg_us"] * 1e-6) / 1e9 / sc["GBps"]
         result["stream_copy"] = sc
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, sp, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, kvs[0], q_steps[:, 0], flags, n_slow_timed / K)
+    if not args.no_configs:
+        del kvs, q_steps, graphs, run
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["configs"] = config_block(dev, result)
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -508,140 +538,162 @@ def main():
     print(json.dumps(result))
 
 
-def run_batched(args, w, dev):
-    """Batched and growing-history workloads (16 sequences with mixed slow and
-    fast steps; 4 sequences over 32 layers with a KV append every step).  The
-    rows that take a slow step change from step to step and, with appends, so
-    do the context lengths baked into every launch, so the loop runs eagerly:
-    per layer one append, one fused refresh for the rows that start a span and
-    one packed fast step for the others, called through the C ABI with
-    prepared arguments.  The dense baseline runs the same loop with a dense
-    step for every row."""
-    import ctypes as C
+def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=None):
+    """Decode-loop throughput of workload ``w`` over ``layers`` layer caches
+    (the workload's own layers, or independent caches cycled so that no
+    layer's data is still cached at its next step), over the whole span
+    schedule (``n_steps`` steps, the workload's count by default).
 
+    Each decode step runs, for every layer: the KV append (growing-history
+    workloads), the fused refresh for the rows that open a span, and the
+    packed fast step for the others.  Every distinct slow/fast row pattern
+    of the schedule is captured once as a HIP graph and replayed; with
+    appends the context lengths live in device memory (advanced by the
+    append kernel), so a captured step stays valid as the history grows.
+    The dense baseline replays a graph of the same loop with every row
+    dense.  Inputs are resident in HBM; only the query (and appended-row)
+    staging copies run beside the replays."""
     import numpy as np
     import torch
 
     import sparse_kv_attention_sfi_amd as S
-    from sparse_kv_attention_sfi_amd import binding as Bd
     from synth import gen
 
-    lib = S.lib()
     B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
-    # layers: the workload's own count, or (single-layer workloads) independent
-    # caches cycled so that no layer's data is still cached at its next step
-    L = w.n_layers if w.n_layers > 1 else max(1, args.batched_caches)
-    K, W = args.steps, args.warmup
-    n_steps = W + K
+    L = layers
+    n_steps = n_steps or w.n_steps
     sched = S.Scheduler(B, w.seed, w.span_mode, w.span_param)
-    plan = [sched.step() for _ in range(n_steps)]
+    plan = [tuple(tuple(x) for x in sched.step()) for _ in range(n_steps)]
     sched.close()
     flags = [[b in slow for slow, _ in plan] for b in range(B)]
     span_ids = [gen.span_ids_from_flags(f) for f in flags]
     t0 = time.time()
-    kvs, qs, apps = [], [], []
+    kvs, ctx_devs = [], []
+    q_all = torch.empty(n_steps, L, B, Hq, D, dtype=gen.torch_dtype(w.dtype), device=dev)
+    if w.append:
+        kn_all = torch.empty(n_steps, L, B, Hkv, D, dtype=q_all.dtype, device=dev)
+        vn_all = torch.empty_like(kn_all)
     for l in range(L):
-        c = gen.build_cache(w, dev, layer=l, n_spans=None)
-        kvs.append(S.KVDesc(c["K"], c["V"], c["ctx_len"], Hq))
-        qs.append(gen.build_queries(w, dev, span_ids, c, layer=l))
+        c = gen.build_cache(w, dev, layer=l, n_spans=span_ids[0][-1] + 1)
+        T0 = list(c["ctx_len"])
         if w.append:
-            apps.append(gen.append_rows(w, dev, layer=l, n_steps=n_steps))
+            # device lengths advanced by the append kernel; the host values are
+            # the bound every launch is planned for (the schedule's last length)
+            ctx_dev = torch.tensor(T0, dtype=torch.int32, device=dev)
+            kvs.append(S.KVDesc(c["K"], c["V"], [t + n_steps for t in T0], Hq, ctx_dev=ctx_dev))
+            ctx_devs.append((ctx_dev, T0))
+            kn, vn = gen.append_rows(w, dev, layer=l, n_steps=n_steps)
+            kn_all[:, l].copy_(kn)
+            vn_all[:, l].copy_(vn)
+            del kn, vn
+        else:
+            kvs.append(S.KVDesc(c["K"], c["V"], T0, Hq))
+        q_all[:, l].copy_(gen.build_queries(w, dev, span_ids, c, layer=l))
         del c
     torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f}s: {L} layers, batch {B}, ctx {kvs[0].ctx.min()}..{kvs[0].ctx.max()}")
-    ctx0 = [kv.ctx.copy() for kv in kvs]
+    log(f"{log_name or w.name}: inputs ready in {time.time() - t0:.1f}s ({L} layers, batch {B})")
     sp = S.support_params(w.n_sink, w.n_recent, w.top_k, w.lam)
     ws = S.alloc_workspace(kvs[0], sp)
-    ws_ptr, ws_bytes = C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel())
-    out = torch.empty(B, Hq, D, device=dev)
+    out = torch.empty(L, B, Hq, D, device=dev)
     mass = torch.empty(B, Hkv, kvs[0].capacity, device=dev)
-    sel = [torch.empty(B, Hkv, w.top_k, dtype=torch.int32, device=dev) for _ in range(L)]
-    cnt = [torch.zeros(B, Hkv, dtype=torch.int32, device=dev) for _ in range(L)]
-    pk = [torch.empty(B, Hkv, w.top_k, D, dtype=kvs[0].dtype, device=dev) for _ in range(L)]
-    pv = [torch.empty_like(pk[0]) for _ in range(L)]
-    esz = kvs[0].k.element_size()
-    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
-    P = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
-    id_cache = {}
+    sel = torch.empty(L, B, Hkv, w.top_k, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(L, B, Hkv, dtype=torch.int32, device=dev)
+    pk = torch.empty(L, B, Hkv, w.top_k, D, dtype=q_all.dtype, device=dev)
+    pv = torch.empty_like(pk)
+    q_buf = torch.empty_like(q_all[0])
+    if w.append:
+        kn_buf, vn_buf = torch.empty_like(kn_all[0]), torch.empty_like(vn_all[0])
+    all_rows = list(range(B))
 
-    def ids_of(lst):
-        key = tuple(lst)
-        if key not in id_cache:
-            a = np.asarray(lst, dtype=np.int32)
-            id_cache[key] = (a, a.ctypes.data_as(C.POINTER(C.c_int32)), len(lst))
-        return id_cache[key][1:]
-
-    all_ids = ids_of(list(range(B)))
-    lay = [dict(desc=C.byref(kvs[l].desc), q=qs[l].data_ptr(), qstride=qs[l].stride(0) * esz, sel=P(sel[l]),
-                cnt=P(cnt[l]), pk=P(pk[l]), pv=P(pv[l]),
-                kn=apps[l][0].data_ptr() if w.append else 0, vn=apps[l][1].data_ptr() if w.append else 0,
-                astride=apps[l][0].stride(0) * esz if w.append else 0) for l in range(L)]
-    spr, outp, massp = C.byref(sp), P(out), P(mass)
-
-    def ok(st, what):
-        if st != 0:
-            raise RuntimeError(f"{what}: {lib.sfi_last_error().decode()}")
-
-    def step(t, dense=False):
-        slow, fast = plan[t]
-        if dense:
-            slow, fast = list(range(B)), []
+    def step_calls(slow, fast, dense=False):
         for l in range(L):
-            d = lay[l]
-            qp = C.c_void_p(d["q"] + t * d["qstride"])
             if w.append:
-                ok(lib.sfi_kv_append(d["desc"], all_ids[0], all_ids[1], C.c_void_p(d["kn"] + t * d["astride"]),
-                                     C.c_void_p(d["vn"] + t * d["astride"]), stream), "append")
-                kvs[l].ctx += 1
+                S.sfi_kv_append(kvs[l], all_rows, kn_buf[l], vn_buf[l])
+            if dense:
+                S.sfi_slow_step(kvs[l], all_rows, q_buf[l], out[l], None, ws)
+                continue
             if slow:
-                ip, n = ids_of(slow)
-                if dense:
-                    ok(lib.sfi_slow_step(d["desc"], ip, n, qp, outp, None, ws_ptr, ws_bytes, stream), "dense")
-                else:
-                    ok(lib.sfi_slow_step_select(d["desc"], spr, ip, n, qp, outp, massp, d["sel"], d["cnt"], d["pk"],
-                                                d["pv"], ws_ptr, ws_bytes, stream), "slow")
+                S.sfi_slow_step_select(kvs[l], sp, list(slow), q_buf[l], out[l], mass, sel[l], cnt[l], pk[l], pv[l],
+                                       ws)
             if fast:
-                ip, n = ids_of(fast)
-                ok(lib.sfi_fast_step_packed(d["desc"], spr, ip, n, qp, d["pk"], d["pv"], d["cnt"], outp, ws_ptr,
-                                            ws_bytes, stream), "fast")
+                S.sfi_fast_step_packed(kvs[l], sp, list(fast), q_buf[l], pk[l], pv[l], cnt[l], out[l], ws)
 
-    for t in range(W):
-        step(t)
+    def stage(t):
+        q_buf.copy_(q_all[t])
+        if w.append:
+            kn_buf.copy_(kn_all[t])
+            vn_buf.copy_(vn_all[t])
+
+    def restart():
+        for ctx_dev, T0 in ctx_devs:
+            ctx_dev.copy_(torch.tensor(T0, dtype=torch.int32))
+
+    graphs = {}
+    for key in sorted(set(plan)) + [("dense",)]:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            if key == ("dense",):
+                step_calls((), (), dense=True)
+            else:
+                step_calls(*key)
+        graphs[key] = g
+    for t in range(min(warmup, n_steps)):
+        stage(t)
+        graphs[plan[t]].replay()
+    torch.cuda.synchronize()
+    restart()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for t in range(W, W + K):
-        step(t)
+    for t in range(n_steps):
+        stage(t)
+        graphs[plan[t]].replay()
     torch.cuda.synchronize()
     t_sfi = time.perf_counter() - t_start
-    slow_rows = sum(len(plan[t][0]) for t in range(W, W + K))
-    log(f"SFI: {K} steps x {L} layers in {t_sfi * 1e3:.1f} ms ({slow_rows} slow row-steps of {K * B})")
-    # dense baseline: same loop, every row dense (contexts restarted)
-    for l in range(L):
-        kvs[l].ctx[:] = ctx0[l]
-    kd = min(args.dense_steps, n_steps) if args.dense_steps else min(64, n_steps)
-    step(0, dense=True)
+    slow_rows = sum(len(p[0]) for p in plan)
+    kd = min(dense_steps, n_steps)
+    restart()
+    stage(0)
+    graphs[("dense",)].replay()
     torch.cuda.synchronize()
-    for l in range(L):
-        kvs[l].ctx[:] = ctx0[l]
+    restart()
+    torch.cuda.synchronize()
     t_start = time.perf_counter()
     for t in range(kd):
-        step(t, dense=True)
+        stage(t)
+        graphs[("dense",)].replay()
     torch.cuda.synchronize()
     t_dense = time.perf_counter() - t_start
-    value = K * L / t_sfi
+    value = n_steps * L / t_sfi
     dense_rate = kd * L / t_dense
+    res = {"workload": f"{w.name}: B={B}, {Hq}q/{Hkv}kv heads, D={D}, ctx {w.ctx_min}..{w.ctx}, {w.dtype} KV, "
+                       f"sinks {w.n_sink}, recent {w.n_recent}, top-k {w.top_k}, {w.span_mode} spans {w.span_param}"
+                       f"{', KV append every step' if w.append else ''}; {L} layers",
+           "steps": n_steps, "layers": L, "batch": B,
+           "sfi_steps_per_s_layer": value, "sfi_tokens_per_s_layer": value * B,
+           "dense_steps_per_s_layer": dense_rate, "dense_steps_timed": kd,
+           "speedup_vs_dense": value / dense_rate, "slow_row_fraction": slow_rows / (n_steps * B),
+           "graphs": len(graphs), "mode": "graph replay per slow/fast row pattern"
+                                          + (", device context lengths" if w.append else "")}
+    del kvs, q_all, graphs
+    if w.append:
+        del kn_all, vn_all
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_batched(args, w, dev):
+    """The batched and growing-history workloads as the bench line: their
+    whole span schedule (or --steps steps) replayed from captured graphs."""
+    L = w.n_layers if w.n_layers > 1 else max(1, args.batched_caches)
+    r = measure_loop(w, dev, L, args.dense_steps or 64, warmup=args.warmup,
+                     n_steps=args.steps if args.steps < w.n_steps else w.n_steps)
     result = {
-        "metric": METRIC, "value": value, "unit": "decode steps/s/layer", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": 1e3 * t_sfi / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: B={B}, {Hq}q/{Hkv}kv heads, D={D}, ctx {w.ctx_min}..{w.ctx}, "
-                               f"{w.dtype} KV, sinks {w.n_sink}, recent {w.n_recent}, top-k {w.top_k}, "
-                               f"{w.span_mode} spans {w.span_param}, append {w.append}; {L} layers",
-                   "layers": L, "batch": B, "mode": "eager (C ABI calls with prepared arguments)"},
-        "tokens_per_s_layer": value * B,
-        "dense_steps_per_s_layer": dense_rate,
-        "speedup_vs_dense": value / dense_rate,
-        "slow_row_fraction": slow_rows / (K * B),
+        "metric": METRIC, "value": r["sfi_steps_per_s_layer"], "unit": "decode steps/s/layer", "n_gpus": 1,
+        "steps": r["steps"], "warmup": args.warmup, "ms_per_step": 1e3 * r["layers"] / r["sfi_steps_per_s_layer"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": r["workload"], "layers": r["layers"], "batch": r["batch"], "mode": r["mode"]},
+        **{k: v for k, v in r.items() if k not in ("workload", "steps", "layers", "batch", "mode")},
     }
     print(json.dumps(result))
 
@@ -731,32 +783,87 @@ def fast_batch_check(w, sp, batch, dev, ctx=32768, calls=20):
     return res
 
 
-def cpu_baseline(w, kv, q_steps, flags, sp, budget):
-    """The CPU oracle, as it stands, on the first steps of layer 0's schedule
-    until ``budget`` seconds of oracle work have run."""
+def config_block(dev, headline):
+    """SFI against dense decode on every workload beside the headline: the
+    32K layer (128 independent layer caches), the batch of 16 mixed contexts
+    (8 cycled caches) and the 32-layer growing-history loop, each over its
+    whole span schedule, plus the 128K headline's own full-schedule figures."""
+    import synth
+    out = {}
+    hs = headline.get("full_schedule") or {}
+    if hs and headline.get("dense_steps_per_s_layer"):
+        out["C3"] = {"workload": headline["config"]["workload"], "steps": hs["steps"],
+                     "sfi_steps_per_s_layer": hs["blended_steps_per_s_layer"],
+                     "dense_steps_per_s_layer": headline["dense_steps_per_s_layer"],
+                     "speedup_vs_dense": hs["blended_steps_per_s_layer"] / headline["dense_steps_per_s_layer"],
+                     "slow_row_fraction": hs["slow_fraction"]}
+    for name, w, layers in (("C2", synth.C2, 128), ("C4", synth.C4, 8), ("C5", synth.C5, synth.C5.n_layers)):
+        out[name] = measure_loop(w, dev, layers, dense_steps=64, warmup=8)
+        log(f"{name}: SFI {out[name]['sfi_steps_per_s_layer']:.0f} decode steps/s/layer, "
+            f"dense {out[name]['dense_steps_per_s_layer']:.0f}, speedup {out[name]['speedup_vs_dense']:.2f}")
+    return out
+
+
+def cpu_baseline(w, kv, q_steps, flags, slow_frac_window):
+    """The CPU oracle, as it stands, on layer 0 of the same workload: median
+    times of its three operations (the slow step's dense attention with the
+    mass, the Selector, the fast step) with the BLAS threads numpy uses by
+    default and with one thread, and the blended decode rate they give at the
+    workload's span-schedule slow fraction (and at the timed window's)."""
+    import statistics
+
     import numpy as np
-    import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
     T = int(kv.ctx[0])
     K = kv.k[0, :, :T].float().cpu().numpy().astype(np.float64)
     V = kv.v[0, :, :T].float().cpu().numpy().astype(np.float64)
-    qs = q_steps[:, 0].float().cpu().numpy().astype(np.float64)
+    q = q_steps[0, 0].float().cpu().numpy().astype(np.float64)
+    Hkv = K.shape[0]
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    done, sels, spent = 0, None, 0.0
-    while spent < budget and done < len(flags):
-        t0 = time.perf_counter()
-        if flags[done] or sels is None:
-            _, _, sels = O.slow_step(qs[done], K, V, T, w.n_sink, w.n_recent, w.top_k, w.lam)
-        else:
-            O.fast_step(qs[done], K, V, T, w.n_sink, w.n_recent, sels)
-        spent += time.perf_counter() - t0
-        done += 1
-    n_slow = sum(flags[:done])
-    return {"value": done / spent, "unit": "decode steps/s/layer", "cores": threads, "kind": "oracle",
-            "sample": f"first {done} decode steps ({n_slow} slow) of layer 0 of the same workload, "
-                      f"numpy float64, {spent:.1f}s"}
+
+    def ops(reps_slow, reps_fast):
+        ts = {"slow": [], "select": [], "fast": []}
+        sels = None
+        for _ in range(reps_slow):
+            t0 = time.perf_counter()
+            _, P = O.dense_attention(q, K, V)
+            f = O.group_mass(P, Hkv)
+            t1 = time.perf_counter()
+            sels = [O.select(f[g], T, w.n_sink, w.n_recent, w.top_k, w.lam)[0] for g in range(Hkv)]
+            t2 = time.perf_counter()
+            ts["slow"].append(t1 - t0)
+            ts["select"].append(t2 - t1)
+        for _ in range(reps_fast):
+            t0 = time.perf_counter()
+            O.fast_step(q, K, V, T, w.n_sink, w.n_recent, sels)
+            ts["fast"].append(time.perf_counter() - t0)
+        return {k: statistics.median(v) for k, v in ts.items()}
+
+    t_start = time.perf_counter()
+    many = ops(3, 5)
+    with threadpool_limits(1):
+        one = ops(1, 3)
+    spent = time.perf_counter() - t_start
+    f_sched = sum(flags[:w.n_steps]) / w.n_steps
+
+    def blended(m, f):
+        return 1.0 / (f * (m["slow"] + m["select"]) + (1.0 - f) * m["fast"])
+
+    return {"value": blended(many, f_sched), "unit": "decode steps/s/layer", "cores": threads,
+            "kind": "oracle", "os_cpu_count": os.cpu_count(),
+            "sample": f"layer 0 of the same workload (T={T}), numpy float64: medians of 3 slow steps (dense "
+                      f"attention + mass), 3 Selector runs and 5 fast steps with {threads} BLAS threads, and of 1/1/3 "
+                      f"with one thread ({spent:.1f}s in all); value = the blended rate at the schedule's slow "
+                      f"fraction {f_sched:.4f}",
+            "ms_all_threads": {k: 1e3 * v for k, v in many.items()},
+            "ms_one_thread": {k: 1e3 * v for k, v in one.items()},
+            "steps_per_s_layer_all_threads": {"slow": 1.0 / (many["slow"] + many["select"]), "fast": 1.0 / many["fast"],
+                                              "blended_schedule": blended(many, f_sched),
+                                              "blended_timed_window": blended(many, slow_frac_window)},
+            "steps_per_s_layer_one_thread": {"slow": 1.0 / (one["slow"] + one["select"]), "fast": 1.0 / one["fast"],
+                                             "blended_schedule": blended(one, f_sched)}}
 
 
 if __name__ == "__main__":

@@ -30,18 +30,23 @@ the design notes of the repository):
   over the G query heads that share a KV head (so it sums to 1);
 * the prior r is a parameter-free positional sink/recency bias over the
   candidate positions: r(a) = (1/a + 1/(n+1-a)) / (2 H_n);
-* the fused score is the printed arithmetic mixture, then a plain top-k with
-  the lowest position winning ties (Soft-NMS and cross-head exclusivity have
-  no formula on the pages and are not part of this path);
+* the fused score is the printed arithmetic mixture, then a top-k with the
+  lowest position winning ties;
+* optional, all off by default (``select_heads``): a key-norm correction of
+  the prior, one round of linear Soft-NMS within a head and a soft
+  exclusivity across heads, in readings stated at each function (the pages
+  name these steps but give no formula);
 * sinks, recent window and selected memory are disjoint; k counts only the
   selected memory;
 * the fast step renormalises the softmax over its support;
 * the span schedule is drawn from splitmix64 by Bernoulli trials.
 
-Parity pins for every function live in ``tests/test_oracle_*.py``.  The one
-choice not fixed by the pages or by mathematics is the exact shape of the
-prior r: it is pinned only by its own closed form ("parity unpinned" against
-the pages for that shape).
+Parity pins for every function live in ``tests/test_oracle_*.py``.  The
+choices not fixed by the pages or by mathematics are the exact shape of the
+prior r and the forms of the key-norm correction, the Soft-NMS round and
+the exclusivity: each is pinned by hand-worked examples and invariants of
+its own definition, not by the pages ("parity unpinned" against the pages
+for those forms).
 """
 
 from __future__ import annotations
@@ -156,6 +161,37 @@ def positional_prior(n):
     return (1.0 / a + 1.0 / (n + 1 - a)) / (2.0 * harmonic(n))
 
 
+def key_norms(K_rows):
+    """Euclidean norm of every key row, nu_j = ||k_j||_2 (float64)."""
+    K_rows = np.asarray(K_rows, np.float64)
+    return np.sqrt((K_rows * K_rows).sum(axis=-1))
+
+
+def keynorm_prior(n, nu, beta, c):
+    """Prior over n candidates with the key-norm correction.
+
+    [GIST] 2.B: the cache-based prior also corrects structural biases such as
+    tokens with extremely high key norms.  The pages give no formula; the
+    reading used here: z_j is candidate j's key norm nu_j in standard
+    deviations above the mean over the candidates (population statistics;
+    z = 0 when all norms are equal), the positional weight of the candidate
+    is multiplied by exp(-beta * max(0, z_j - c)), and the weights are
+    renormalised to a distribution.  beta >= 0 sets the strength, c the
+    number of standard deviations tolerated; beta = 0 is positional_prior(n)
+    itself.
+    """
+    if beta == 0 or n == 0:
+        return positional_prior(n)
+    nu = np.asarray(nu, np.float64)
+    mu = nu.mean()
+    sigma = math.sqrt(((nu - mu) ** 2).mean())
+    z = (nu - mu) / sigma if sigma > 0 else np.zeros(n)
+    penalty = np.exp(-beta * np.maximum(0.0, z - c))
+    a = np.arange(1, n + 1, dtype=np.float64)
+    w = (1.0 / a + 1.0 / (n + 1 - a)) * penalty
+    return w / w.sum()
+
+
 # ---------------------------------------------------------------------------
 # O5  fusion of evidence and prior
 # ---------------------------------------------------------------------------
@@ -163,6 +199,58 @@ def fused_score(f_cand, r, lam):
     """s_lambda = (1 - lambda) f + lambda r ([GIST] 2.B, the closed-form
     mixture that the reverse-KL fusion reduces to)."""
     return (1.0 - lam) * np.asarray(f_cand, np.float64) + lam * np.asarray(r, np.float64)
+
+
+# ---------------------------------------------------------------------------
+# O5b  discretisation: Soft-NMS within a head, exclusivity across heads
+# ---------------------------------------------------------------------------
+def soft_nms(score, radius, decay):
+    """Soft non-maximum suppression along the candidates of one head.
+
+    [GIST] 2.B, discretisation step 1: within a head, neighbouring tokens
+    with similar scores are suppressed to spread the selection over the
+    context.  The pages give no formula; the reading used here is one
+    parallel round of linear Soft-NMS (each score decayed once, by its
+    strongest suppressor, all decays computed from the undecayed scores)
+    with the overlap of two positions d apart, 0 < d <= radius, taken as
+    1 - d / (radius + 1).  A neighbour suppresses candidate j when it ranks
+    above j: a higher score, or the same score at a lower position (the
+    top-k order).  Candidate j keeps s_j * (1 - decay * overlap) for its
+    nearest suppressor, s_j when it has none.  radius = 0 or decay = 0
+    leaves the scores unchanged.  score: the fused scores of consecutive
+    candidate positions.
+    """
+    s = np.asarray(score, np.float64)
+    n = s.shape[0]
+    if radius <= 0 or decay == 0 or n == 0:
+        return s.copy()
+    fac = np.ones(n)
+    for d in range(1, radius + 1):
+        f_d = 1.0 - decay * (1.0 - d / (radius + 1))
+        # neighbour d below j ranks above j on a tie; neighbour d above j only when strictly higher
+        below = np.zeros(n, dtype=bool)
+        below[d:] = s[:-d] >= s[d:]
+        above = np.zeros(n, dtype=bool)
+        above[:-d] = s[d:] > s[:-d]
+        fac = np.where(below | above, np.minimum(fac, f_d), fac)
+    return s * fac
+
+
+def cross_head_exclusivity(S, eps):
+    """Soft competition between the KV heads of a sequence.
+
+    [GIST] 2.B, discretisation step 2: heads compete softly so that they do
+    not all select the same tokens.  Reading: head g's score of position j
+    is multiplied by its share of the heads' total score there, raised to
+    eps: S''[g, j] = S[g, j] * (S[g, j] / sum_h S[h, j]) ** eps.  eps = 0, a
+    single head, or a zero total leave the scores unchanged.  S: [Hkv, n].
+    """
+    S = np.asarray(S, np.float64)
+    if eps == 0 or S.shape[0] <= 1:
+        return S.copy()
+    tot = S.sum(axis=0)
+    share = np.divide(S, tot, out=np.ones_like(S), where=tot > 0)
+    return S * share ** eps
 
 
 # ---------------------------------------------------------------------------
@@ -195,6 +283,32 @@ def select(f_row, t, n_sink, n_recent, top_k, lam):
     r = positional_prior(n)
     s = fused_score(np.asarray(f_row, np.float64)[cand], r, lam) if n else np.zeros(0)
     return topk_select(s, cand, top_k), s, cand
+
+
+def select_heads(f, K, t, n_sink, n_recent, top_k, lam, knorm_beta=0.0, knorm_c=0.0, nms_radius=0,
+                 nms_decay=0.0, excl=0.0):
+    """Selector of one sequence over all of its KV heads, in [GIST] 2.B's
+    order: the prior (positional, with the key-norm correction), its mixture
+    with the evidence, Soft-NMS within each head, exclusivity across the
+    heads, then top-k.  With every option at zero it is ``select`` applied
+    to each head.
+
+    f: [Hkv, >= t] evidence; K: [Hkv, >= t, D] keys (read only when
+    knorm_beta != 0).  Returns (sels, final scores [Hkv, n], candidates).
+    """
+    cand = candidate_positions(t, n_sink, n_recent)
+    n = cand.shape[0]
+    Hkv = np.asarray(f).shape[0]
+    if n == 0:
+        return [np.zeros(0, dtype=np.int64) for _ in range(Hkv)], np.zeros((Hkv, 0)), cand
+    S = np.empty((Hkv, n))
+    for g in range(Hkv):
+        nu = key_norms(np.asarray(K[g])[cand]) if knorm_beta != 0 else None
+        r = keynorm_prior(n, nu, knorm_beta, knorm_c)
+        s = fused_score(np.asarray(f[g], np.float64)[cand], r, lam)
+        S[g] = soft_nms(s, nms_radius, nms_decay)
+    S = cross_head_exclusivity(S, excl)
+    return [topk_select(S[g], cand, top_k) for g in range(Hkv)], S, cand
 
 
 # ---------------------------------------------------------------------------

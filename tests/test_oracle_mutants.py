@@ -106,3 +106,73 @@ def test_span_length_off_by_one_caught(monkeypatch):
     orig = OS.SpanSchedule._draw_span
     monkeypatch.setattr(OS.SpanSchedule, "_draw_span", lambda self: orig(self) + 1)
     _expect_failure(TF.test_fixed_spans_slow_positions)
+
+
+# ------------------------------------------------------------------ optional Selector steps
+from tests import test_oracle_discretize as TX  # noqa: E402
+
+
+def test_nms_suppressed_by_lower_neighbours_caught(monkeypatch, golden):
+    def nms(score, radius, decay):
+        s = np.asarray(score, np.float64)
+        n = len(s)
+        if radius <= 0 or decay == 0 or n == 0:
+            return s.copy()
+        fac = np.ones(n)
+        for d in range(1, radius + 1):
+            f_d = 1.0 - decay * (1.0 - d / (radius + 1))
+            below = np.zeros(n, bool); below[d:] = s[:-d] <= s[d:]
+            above = np.zeros(n, bool); above[:-d] = s[d:] < s[:-d]
+            fac = np.where(below | above, np.minimum(fac, f_d), fac)
+        return s * fac
+    monkeypatch.setattr(O, "soft_nms", nms)
+    _expect_failure(TX.test_soft_nms_hand_examples, golden)
+
+
+def test_nms_tie_rule_reversed_caught(monkeypatch, golden):
+    def nms(score, radius, decay):
+        s = np.asarray(score, np.float64)
+        n = len(s)
+        fac = np.ones(n)
+        for d in range(1, radius + 1):
+            f_d = 1.0 - decay * (1.0 - d / (radius + 1))
+            below = np.zeros(n, bool); below[d:] = s[:-d] > s[d:]
+            above = np.zeros(n, bool); above[:-d] = s[d:] >= s[:-d]
+            fac = np.where(below | above, np.minimum(fac, f_d), fac)
+        return s * fac
+    monkeypatch.setattr(O, "soft_nms", nms)
+    _expect_failure(TX.test_soft_nms_hand_examples, golden)
+
+
+def test_exclusivity_share_of_the_maximum_caught(monkeypatch, golden):
+    def excl(S, eps):
+        S = np.asarray(S, np.float64)
+        if eps == 0 or S.shape[0] <= 1:
+            return S.copy()
+        return S * (S / S.max(axis=0)) ** eps
+    monkeypatch.setattr(O, "cross_head_exclusivity", excl)
+    _expect_failure(TX.test_exclusivity_hand_example, golden)
+
+
+def test_keynorm_on_raw_norms_caught(monkeypatch, golden):
+    def prior(n, nu, beta, c):
+        if beta == 0 or n == 0:
+            return O.positional_prior(n)
+        nu = np.asarray(nu, np.float64)
+        a = np.arange(1, n + 1, dtype=np.float64)
+        w = (1.0 / a + 1.0 / (n + 1 - a)) * np.exp(-beta * np.maximum(0.0, nu - nu.mean() - c))
+        return w / w.sum()
+    monkeypatch.setattr(O, "keynorm_prior", prior)
+    _expect_failure(TX.test_keynorm_prior_hand_example, golden)
+    _expect_failure(TX.test_keynorm_prior_invariants.hypothesis.inner_test, 10, 2.0, 0.5, 3)
+
+
+def test_keynorm_without_renormalising_caught(monkeypatch, golden):
+    def prior(n, nu, beta, c):
+        if beta == 0 or n == 0:
+            return O.positional_prior(n)
+        nu = np.asarray(nu, np.float64)
+        z = (nu - nu.mean()) / nu.std()
+        return O.positional_prior(n) * np.exp(-beta * np.maximum(0.0, z - c))
+    monkeypatch.setattr(O, "keynorm_prior", prior)
+    _expect_failure(TX.test_keynorm_prior_hand_example, golden)

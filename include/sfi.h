@@ -62,7 +62,7 @@ extern "C" {
 #endif
 
 #define SFI_VERSION_MAJOR 0
-#define SFI_VERSION_MINOR 4
+#define SFI_VERSION_MINOR 5
 
 typedef enum {
   SFI_OK = 0,
@@ -106,12 +106,40 @@ typedef struct {
 /* The sparse state kept for fast steps: n_sink sink tokens, a recent window
  * of n_recent tokens, and top_k selected tokens chosen by the Selector with
  * mixture weight lambda in [0, 1].  Sinks, window and selected memory are
- * disjoint; top_k counts only the selected memory. */
+ * disjoint; top_k counts only the selected memory.
+ *
+ * Optional Selector steps ("Slow-Fast Inference ...", gist.science
+ * technical summary, 2.B: the prior also corrects extreme key norms, and the
+ * scores are discretised by Soft-NMS within a head and a soft exclusivity
+ * between heads before the top-k).  The page gives no formulas; the readings
+ * implemented, all off at 0:
+ *  - knorm_beta, knorm_c: each candidate's positional prior weight is
+ *    multiplied by exp(-knorm_beta * max(0, z - knorm_c)), z its key norm in
+ *    standard deviations above the candidates' mean (population statistics
+ *    of the KV head), and the prior is renormalised.  Needs the slow step's
+ *    key norms: sfi_slow_step_select / _async only (sfi_select rejects it).
+ *  - nms_radius, nms_decay: one parallel round of linear Soft-NMS along the
+ *    candidates: a neighbour d <= nms_radius positions away that ranks above
+ *    candidate j (higher score, or equal score at a lower position) decays
+ *    it to s_j * (1 - nms_decay * (1 - d / (nms_radius + 1))), the nearest
+ *    such neighbour's factor applying.
+ *  - excl: each KV head's score at a position is multiplied by its share of
+ *    the sequence's heads' total score there, to the power excl.
+ * Ranges: knorm_beta >= 0, knorm_c finite, 0 <= nms_radius <= 32,
+ * 0 <= nms_decay <= 1, excl >= 0, and with any option on
+ * n_kv_heads * (64 + 2 * nms_radius) <= 16384.  With an option on the
+ * Selector scores the candidates in a pass of its own before the top-k, and
+ * sfi_workspace_bytes, given these parameters, includes its buffers. */
 typedef struct {
   int32_t n_sink;
   int32_t n_recent;
   int32_t top_k;
   float lambda;
+  float knorm_beta;
+  float knorm_c;
+  int32_t nms_radius;
+  float nms_decay;
+  float excl;
 } sfi_support_params;
 
 /* Bytes of workspace `op` needs for this cache shape (the maximum over all

@@ -41,7 +41,8 @@ class sfi_kv_desc(C.Structure):
 
 class sfi_support_params(C.Structure):
     _fields_ = [("n_sink", C.c_int32), ("n_recent", C.c_int32), ("top_k", C.c_int32),
-                ("lambda_", C.c_float)]
+                ("lambda_", C.c_float), ("knorm_beta", C.c_float), ("knorm_c", C.c_float),
+                ("nms_radius", C.c_int32), ("nms_decay", C.c_float), ("excl", C.c_float)]
 
 
 _lib = None
@@ -164,8 +165,12 @@ class KVDesc:
         return self.desc.kv_capacity
 
 
-def support_params(n_sink, n_recent, top_k, lam):
-    return sfi_support_params(int(n_sink), int(n_recent), int(top_k), float(lam))
+def support_params(n_sink, n_recent, top_k, lam, knorm_beta=0.0, knorm_c=0.0, nms_radius=0, nms_decay=0.0,
+                   excl=0.0):
+    """Support parameters; the optional Selector steps (key-norm prior,
+    Soft-NMS, exclusivity) are off at their zero defaults."""
+    return sfi_support_params(int(n_sink), int(n_recent), int(top_k), float(lam), float(knorm_beta),
+                              float(knorm_c), int(nms_radius), float(nms_decay), float(excl))
 
 
 def _need(t, dtype, shape, name):

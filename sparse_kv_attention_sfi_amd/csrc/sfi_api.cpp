@@ -157,7 +157,28 @@ int32_t check_params(const sfi_support_params* sp) {
     return fail(SFI_ERR_INVALID_ARG, "n_sink and n_recent must be <= 2^30");
   if (!(sp->lambda >= 0.f && sp->lambda <= 1.f))
     return fail(SFI_ERR_INVALID_ARG, "lambda must lie in [0, 1]");
+  if (!(std::isfinite(sp->knorm_beta) && sp->knorm_beta >= 0.f) || !std::isfinite(sp->knorm_c))
+    return fail(SFI_ERR_INVALID_ARG, "knorm_beta must be finite and >= 0, knorm_c finite");
+  if (sp->nms_radius < 0 || sp->nms_radius > 32) return fail(SFI_ERR_INVALID_ARG, "nms_radius must lie in [0, 32]");
+  if (!(sp->nms_decay >= 0.f && sp->nms_decay <= 1.f)) return fail(SFI_ERR_INVALID_ARG, "nms_decay must lie in [0, 1]");
+  if (!(std::isfinite(sp->excl) && sp->excl >= 0.f)) return fail(SFI_ERR_INVALID_ARG, "excl must be finite and >= 0");
   return SFI_OK;
+}
+
+// Whether the optional Selector steps (key-norm prior, Soft-NMS, exclusivity)
+// are on: the Selector then scores the candidates in a pass of its own.
+bool sel_options(const sfi_support_params* sp) {
+  return sp->knorm_beta > 0.f || (sp->nms_radius > 0 && sp->nms_decay > 0.f) || sp->excl > 0.f;
+}
+
+// Candidate positions one score workgroup handles for all KV heads: its
+// mixture window (chunk + 2 radius), Soft-NMS results (chunk) and column
+// totals (chunk) fit kScoreLds floats; a multiple of 32, at most 1024;
+// 0 when even 32 do not fit.
+int score_chunk(const sfi_kv_desc* d, const sfi_support_params* sp) {
+  const int64_t room = kScoreLds - 2LL * sp->nms_radius * d->n_kv_heads;
+  const int64_t c = room / (2LL * d->n_kv_heads + 1) / 32 * 32;
+  return static_cast<int>(std::min<int64_t>(1024, std::max<int64_t>(0, c)));
 }
 
 float logit_scale(const sfi_kv_desc* d) {
@@ -200,6 +221,29 @@ SelectLayout select_layout(const sfi_kv_desc* d) {
   L.head_info = L.chunk_above + align_up(bh * kSelMaxChunks * sizeof(int32_t));
   L.end = L.head_info + align_up(bh * 2 * sizeof(int32_t));
   return L;
+}
+
+// Buffers of the optional Selector steps, placed after every other scratch
+// so that the slow step's kernels may write the key norms while its logits
+// and partials are in use: final scores and key norms [B][Hkv][T_cap], per
+// split norm sums, per head norm statistics, per mass block normaliser sums.
+struct ExtLayout {
+  size_t score, knorm, knorm_part, knorm_stat, zpart, end;
+  int zpart_stride;
+};
+int slow_part_stride(const sfi_kv_desc* d);
+ExtLayout ext_layout(const sfi_kv_desc* d, size_t start) {
+  const size_t bh = static_cast<size_t>(d->batch) * d->n_kv_heads;
+  const size_t rows = bh * static_cast<size_t>(d->kv_capacity);
+  ExtLayout E;
+  E.zpart_stride = static_cast<int>(ceil_div(d->kv_capacity, kMassChunk));
+  E.score = align_up(start);
+  E.knorm = E.score + align_up(rows * sizeof(float));
+  E.knorm_part = E.knorm + align_up(rows * sizeof(float));
+  E.knorm_stat = E.knorm_part + align_up(bh * slow_part_stride(d) * 2 * sizeof(double));
+  E.zpart = E.knorm_stat + align_up(bh * 2 * sizeof(double));
+  E.end = E.zpart + align_up(bh * E.zpart_stride * sizeof(double));
+  return E;
 }
 
 int slow_unit_rows(const sfi_kv_desc* d) {
@@ -497,6 +541,60 @@ int32_t run_select(const SelectArgs& a, int32_t cnt, hipStream_t s) {
   return e == hipSuccess ? SFI_OK : hip_fail(e, "select launch");
 }
 
+// The optional Selector steps: the final scores of every listed row's
+// candidates into the extension's score buffer (key-norm correction when
+// knorm is given, with the combine's statistics), then the radix top-k over
+// those scores.  Timed with the Selector.
+int32_t run_scored_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* ids, int32_t cnt,
+                          const float* mass, const ExtLayout& E, char* w, bool knorm, SelectArgs& sa,
+                          hipStream_t s) {
+  ScoreArgs a{};
+  a.mass = mass;
+  a.knorm = knorm ? reinterpret_cast<const float*>(w + E.knorm) : nullptr;
+  a.knorm_stat = reinterpret_cast<const double*>(w + E.knorm_stat);
+  a.zpart = reinterpret_cast<const double*>(w + E.zpart);
+  a.score = reinterpret_cast<float*>(w + E.score);
+  a.t_cap = desc->kv_capacity;
+  a.n_kv_heads = desc->n_kv_heads;
+  a.n_sink = sp->n_sink;
+  a.n_recent = sp->n_recent;
+  a.zpart_stride = E.zpart_stride;
+  a.chunk = score_chunk(desc, sp);
+  a.lambda = sp->lambda;
+  a.knorm_beta = sp->knorm_beta;
+  a.knorm_c = sp->knorm_c;
+  a.nms_radius = sp->nms_radius;
+  a.nms_decay = sp->nms_decay;
+  a.excl = sp->excl;
+  a.tab.n = cnt;
+  a.tab.ctx_dev = desc->ctx_len;
+  a.tab.wg_begin[0] = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const int64_t n = std::max<int64_t>(0, desc->ctx_len_host[ids[i]] - static_cast<int64_t>(sp->n_sink) - sp->n_recent);
+    a.tab.ent[i].seq = ids[i];
+    a.tab.ent[i].ctx = desc->ctx_len_host[ids[i]];
+    a.tab.ent[i].nsplit = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(n, a.chunk)));
+    a.tab.wg_begin[i + 1] = a.tab.wg_begin[i] + a.tab.ent[i].nsplit;
+  }
+  sa.mass = a.score;
+  sa.pre_scores = true;
+  sa.hist_ready = false;
+  const int grid = a.tab.wg_begin[cnt];
+  const hipError_t e = timed(SFI_K_SELECT, s, [&] {
+    hipError_t x = launch_score(a, grid, s);
+    return x == hipSuccess ? launch_select(sa, sa.tab.wg_begin[cnt], s) : x;
+  });
+  return e == hipSuccess ? SFI_OK : hip_fail(e, "select launch");
+}
+
+// The optional steps' constraints a call checks before it enqueues anything.
+int32_t check_options(const sfi_kv_desc* desc, const sfi_support_params* sp) {
+  if (sel_options(sp) && score_chunk(desc, sp) < 32)
+    return fail(SFI_ERR_UNSUPPORTED, "n_kv_heads %d with nms_radius %d exceeds the score pass's LDS (n_kv_heads * "
+                "(64 + 2 * nms_radius) + 32 <= 16384)", desc->n_kv_heads, sp->nms_radius);
+  return SFI_OK;
+}
+
 }  // namespace
 
 LaunchTiming* launch_timing() { return g_timing; }
@@ -529,13 +627,15 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* desc, const sfi_support_params* sp
     case SFI_OP_SLOW: return slow_layout(desc).end;
     case SFI_OP_SELECT:
       if (check_params(sp) != SFI_OK) return 0;
-      return select_layout(desc).end;
+      return sel_options(sp) ? ext_layout(desc, select_layout(desc).end).end : select_layout(desc).end;
     case SFI_OP_FAST:
       if (check_params(sp) != SFI_OK) return 0;
       return fast_layout(desc, sp).end;
-    case SFI_OP_SLOW_SELECT:
+    case SFI_OP_SLOW_SELECT: {
       if (check_params(sp) != SFI_OK) return 0;
-      return std::max(slow_layout(desc).end, select_layout(desc).end);
+      const size_t base = std::max(slow_layout(desc).end, select_layout(desc).end);
+      return sel_options(sp) ? ext_layout(desc, base).end : base;
+    }
     default: fail(SFI_ERR_INVALID_ARG, "unknown op %d", op); return 0;
   }
 }
@@ -614,13 +714,18 @@ int32_t sfi_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const 
     return fail(SFI_ERR_INVALID_ARG, "mass / sel_idx / sel_cnt is NULL");
   if ((st = check_aligned({{mass, "mass"}}, kVecAlign)) != SFI_OK) return st;
   if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}}, kIntAlign)) != SFI_OK) return st;
-  if ((st = check_ws(ws, ws_bytes, select_layout(desc).end)) != SFI_OK) return st;
+  if (sp->knorm_beta > 0.f)
+    return fail(SFI_ERR_UNSUPPORTED, "the key-norm prior needs the slow step's key norms: use sfi_slow_step_select");
+  if ((st = check_options(desc, sp)) != SFI_OK) return st;
+  const bool ext = sel_options(sp);
+  const ExtLayout E = ext_layout(desc, select_layout(desc).end);
+  if ((st = check_ws(ws, ws_bytes, ext ? E.end : select_layout(desc).end)) != SFI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
     SelectArgs a{};
     plan_select(desc, sp, ids, cnt, mass, sel_idx, sel_cnt, w, a);
-    return run_select(a, cnt, s);
+    return ext ? run_scored_select(desc, sp, ids, cnt, mass, E, w, false, a, s) : run_select(a, cnt, s);
   });
 }
 
@@ -648,7 +753,11 @@ static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_
                           kVecAlign)) != SFI_OK)
     return st;
   if ((st = check_aligned({{sel_idx, "sel_idx"}, {sel_cnt, "sel_cnt"}}, kIntAlign)) != SFI_OK) return st;
-  if ((st = check_ws(ws, ws_bytes, std::max(slow_layout(desc).end, select_layout(desc).end))) != SFI_OK) return st;
+  if ((st = check_options(desc, sp)) != SFI_OK) return st;
+  const bool ext = sel_options(sp), knorm = sp->knorm_beta > 0.f;
+  const ExtLayout E = ext_layout(desc, std::max(slow_layout(desc).end, select_layout(desc).end));
+  if ((st = check_ws(ws, ws_bytes, ext ? E.end : std::max(slow_layout(desc).end, select_layout(desc).end))) != SFI_OK)
+    return st;
   const bool split = sel_s != s;
   hipEvent_t ev_slow = nullptr, ev_sel = nullptr;
   if (split && (!stream_event(0, &ev_slow) || !stream_event(1, &ev_sel)))
@@ -666,13 +775,29 @@ static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_
     SlowArgs a{};
     CombineArgs c{};
     plan_slow(desc, ids, cnt, q, out, mass, mass != nullptr, w, a, c);
-    a.clear_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
-    a.clear_list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
-    c.sel_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
     c.n_sink = sp->n_sink;
     c.n_recent = sp->n_recent;
     c.top_k = sp->top_k;
     c.lambda = sp->lambda;
+    if (!ext) {
+      // the combine builds the Selector's first histogram next to the mass
+      a.clear_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
+      a.clear_list_n = reinterpret_cast<int32_t*>(w + H.sel_list_n);
+      c.sel_hist = reinterpret_cast<uint32_t*>(w + H.sel_hist);
+    } else if (knorm) {
+      // the slow step emits key norms; the combine their statistics
+      a.knorm = reinterpret_cast<float*>(w + E.knorm);
+      a.knorm_part = reinterpret_cast<double*>(w + E.knorm_part);
+      a.n_sink = sp->n_sink;
+      a.n_recent = sp->n_recent;
+      c.knorm = a.knorm;
+      c.knorm_part = a.knorm_part;
+      c.knorm_stat = reinterpret_cast<double*>(w + E.knorm_stat);
+      c.zpart = reinterpret_cast<double*>(w + E.zpart);
+      c.zpart_stride = E.zpart_stride;
+      c.knorm_beta = sp->knorm_beta;
+      c.knorm_c = sp->knorm_c;
+    }
     int32_t r = run_slow(desc, a, c, cnt, s);
     if (r != SFI_OK) return r;
     if (split) {
@@ -689,7 +814,7 @@ static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_
       sa.packed_v = packed_v;
       sa.row_bytes = desc->head_dim * elem_bytes(desc->kv_dtype);
     }
-    r = run_select(sa, cnt, sel_s);
+    r = ext ? run_scored_select(desc, sp, ids, cnt, mass, E, w, knorm, sa, sel_s) : run_select(sa, cnt, sel_s);
     if (r != SFI_OK) return r;
     if (split && (e = hipEventRecord(ev_sel, sel_s)) != hipSuccess) return hip_fail(e, "event record");
     return SFI_OK;

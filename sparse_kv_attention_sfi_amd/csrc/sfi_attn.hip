@@ -523,7 +523,13 @@ __device__ __forceinline__ void load_q(const void* q, int64_t q_row0, int lane,
 // ---------------------------------------------------------------------------
 // slow step, kernel 1: split-K partials
 // ---------------------------------------------------------------------------
-template <typename E, int D, int G>
+// NORMS: also the Euclidean norm of every key row streamed (the key-norm
+// prior's input) and, per split, the sums of the candidates' norms and
+// squared norms in double precision.  A row's 16-byte pieces sit in lanes
+// l, l + 16, l + 32 and l + 48 of the MFMA layout; each lane sums its pieces'
+// squares (pairwise in float, then in double) and two lane exchanges complete
+// the row.
+template <typename E, int D, int G, bool NORMS>
 __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
@@ -537,6 +543,7 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   __shared__ float s_m[NW * G], s_l[NW * G];
   // the split's logits, [head][row], written out in one pass at the end
   __shared__ __attribute__((aligned(16))) float s_lg[G * kLogitBufRows];
+  __shared__ double s_nrm[NORMS ? 2 * NW : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -576,6 +583,7 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
   // stored block by block, or left dirty in L2, they interleave with the K/V
   // read stream and cost HBM time far above their share of bytes.
   const bool buffered = a.logits != nullptr && a.split_rows <= kLogitBufRows;
+  double nrm_sum = 0.0, nrm_sq = 0.0;  // NORMS: this lane's candidate rows
 
   for (int r0 = r_begin + wave * ROWS; r0 < r_end; r0 += NW * ROWS) {
     uint4 kb[TILES][A::kNL];
@@ -593,6 +601,35 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
     for (int i = 0; i < NV; ++i) {
       const int row = min(r0 + vr + A::kRPL * i, r_end - 1);
       vb[i] = ld16_stream(Vb + static_cast<int64_t>(row) * RB + 16 * vp);
+    }
+    if constexpr (NORMS) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        double p2 = 0.0;
+#pragma unroll
+        for (int kk = 0; kk < A::kNL; ++kk) {
+          float x[A::kEpp];
+          widen(E(), kb[t][kk], x);
+#pragma unroll
+          for (int e = 0; e < A::kEpp; ++e) x[e] = x[e] * x[e];
+#pragma unroll
+          for (int w2 = A::kEpp / 2; w2 >= 1; w2 /= 2)
+#pragma unroll
+            for (int e = 0; e < w2; ++e) x[e] += x[e + w2];
+          p2 += static_cast<double>(x[0]);
+        }
+        p2 += __shfl_xor(p2, 16, 64);
+        p2 += __shfl_xor(p2, 32, 64);
+        const int row = r0 + 16 * t + kr;
+        if (kg == 0 && row < r_end) {
+          const double nu = sqrt(p2);
+          a.knorm[(static_cast<int64_t>(b) * a.n_kv_heads + g) * a.t_cap + row] = static_cast<float>(nu);
+          if (row >= a.n_sink && row < T - a.n_recent) {
+            nrm_sum += nu;
+            nrm_sq += p2;
+          }
+        }
+      }
     }
     float* lbase = a.logits == nullptr ? nullptr
                    : buffered          ? s_lg + (r0 - r_begin)
@@ -620,8 +657,32 @@ __global__ __launch_bounds__(kSlowThreads) void slow_partial_kernel(SlowArgs a) 
       }
     }
   }
+  if constexpr (NORMS) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      nrm_sum += __shfl_xor(nrm_sum, m, 64);
+      nrm_sq += __shfl_xor(nrm_sq, m, 64);
+    }
+    if (lane == 0) {
+      s_nrm[2 * wave] = nrm_sum;
+      s_nrm[2 * wave + 1] = nrm_sq;
+    }
+  }
   st.finish_wave(s_m, s_l, s_o, wave, lane);
   __syncthreads();
+  if constexpr (NORMS) {
+    if (threadIdx.x == 0) {
+      double sn = 0.0, sq = 0.0;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        sn += s_nrm[2 * w2];
+        sq += s_nrm[2 * w2 + 1];
+      }
+      double* kp = a.knorm_part + ((static_cast<int64_t>(b) * a.n_kv_heads + g) * a.part_stride + split) * 2;
+      kp[0] = sn;
+      kp[1] = sq;
+    }
+  }
   const int64_t slot = qh0 * a.part_stride + split;
   merge_waves_to_global<D, G, NW>(s_m, s_l, s_o, a.part_ml + slot * 2,
                                   static_cast<int64_t>(a.part_stride) * 2, a.part_o + slot * D,
@@ -791,6 +852,67 @@ __device__ __forceinline__ void merge_partials(const float* ml, int64_t ml_hstri
   }
 }
 
+// The key-norm prior's statistics of KV head row (b, g): mean and standard
+// deviation of the candidates' key norms, from the slow partial's per-split
+// sums (the same fixed-order reduction in every workgroup, so all agree bit
+// for bit; mass block 0 stores them), and this mass block's share of the
+// prior's normaliser: the sum over its candidates of the positional weight
+// 1/a + 1/(n + 1 - a) times exp(-beta * max(0, z - c)), z the candidate's
+// norm in standard deviations above the mean, in double precision.
+__device__ void knorm_prior_block(const CombineArgs& a, int b, int g, int r, int T, int nsplit, int j0, int j1) {
+  constexpr int NW = kCombineThreads / 64;
+  __shared__ double s_stat[2];
+  __shared__ double s_red[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t bg = static_cast<int64_t>(b) * a.n_kv_heads + g;
+  const int n = max(0, T - a.n_sink - a.n_recent);
+  if (wave == 0) {
+    const double* kp = a.knorm_part + bg * a.part_stride * 2;
+    double sn = 0.0, sq = 0.0;
+    for (int i = lane; i < nsplit; i += 64) {
+      sn += kp[2 * i];
+      sq += kp[2 * i + 1];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      sn += __shfl_xor(sn, m, 64);
+      sq += __shfl_xor(sq, m, 64);
+    }
+    if (lane == 0) {
+      const double mu = n > 0 ? sn / n : 0.0;
+      const double sd = n > 0 ? sqrt(fmax(0.0, sq / n - mu * mu)) : 0.0;
+      s_stat[0] = mu;
+      s_stat[1] = sd;
+      if (r == 0) {
+        a.knorm_stat[2 * bg] = mu;
+        a.knorm_stat[2 * bg + 1] = sd;
+      }
+    }
+  }
+  __syncthreads();
+  const double mu = s_stat[0], sd = s_stat[1];
+  const double beta = a.knorm_beta, c = a.knorm_c;
+  const float* nrow = a.knorm + bg * a.t_cap;
+  double z = 0.0;
+  const int lo = max(j0, a.n_sink), hi = min(j1, T - a.n_recent);
+  for (int j = lo + tid; j < hi; j += kCombineThreads) {
+    const int i = j - a.n_sink;
+    const double w = 1.0 / (i + 1) + 1.0 / (n - i);
+    const double zz = sd > 0.0 ? (static_cast<double>(nrow[j]) - mu) / sd : 0.0;
+    z += w * exp(-beta * fmax(0.0, zz - c));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
+  if (lane == 0) s_red[wave] = z;
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += s_red[w];
+    a.zpart[bg * a.zpart_stride + r] = tot;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // slow step, kernel 2: merge partials; per-position softmax mass
 // ---------------------------------------------------------------------------
@@ -849,6 +971,7 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
     const float invG = 1.f / static_cast<float>(G);
     ScoreParams sp;
     sp.f = nullptr;
+    sp.pre = false;
     sp.n = n_cand;
     sp.lo = a.n_sink;
     sp.lambda = a.lambda;
@@ -884,6 +1007,7 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
       for (int i = tid; i < kSelBins; i += kCombineThreads)
         if (s_hist[i] != 0u) atomicAdd(gh + i, s_hist[i]);
     }
+    if (a.knorm_part != nullptr) knorm_prior_block(a, b, g, r, T, nsplit, j0, j1);
   } else {
     const int h = r - mblocks;
     merge_partials<D, 1, kCombineThreads>(ml + h * ml_hstride, ml_hstride,
@@ -1405,16 +1529,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t word
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename E, int D>
-static hipError_t slow_partial_g(const SlowArgs& a, int group, int grid, hipStream_t s) {
+template <typename E, int D, bool NORMS>
+static hipError_t slow_partial_gn(const SlowArgs& a, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: launch(slow_partial_kernel<E, D, 1>, grid, kSlowThreads, s, a); break;
-    case 2: launch(slow_partial_kernel<E, D, 2>, grid, kSlowThreads, s, a); break;
-    case 4: launch(slow_partial_kernel<E, D, 4>, grid, kSlowThreads, s, a); break;
-    case 8: launch(slow_partial_kernel<E, D, 8>, grid, kSlowThreads, s, a); break;
+    case 1: launch(slow_partial_kernel<E, D, 1, NORMS>, grid, kSlowThreads, s, a); break;
+    case 2: launch(slow_partial_kernel<E, D, 2, NORMS>, grid, kSlowThreads, s, a); break;
+    case 4: launch(slow_partial_kernel<E, D, 4, NORMS>, grid, kSlowThreads, s, a); break;
+    case 8: launch(slow_partial_kernel<E, D, 8, NORMS>, grid, kSlowThreads, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t slow_partial_g(const SlowArgs& a, int group, int grid, hipStream_t s) {
+  return a.knorm != nullptr ? slow_partial_gn<E, D, true>(a, group, grid, s)
+                            : slow_partial_gn<E, D, false>(a, group, grid, s);
 }
 
 hipError_t launch_slow_partial(const SlowArgs& a, int dtype, int head_dim, int group, int grid,

@@ -73,6 +73,12 @@ struct SlowArgs {
   // optional: Selector bookkeeping the first split of each head clears
   uint32_t* clear_hist;    // [B * Hkv][4096] or nullptr
   int32_t* clear_list_n;   // [B * Hkv]
+  // optional: key norms of every row, and per split the sums of the
+  // candidates' norms and squared norms (the key-norm prior's statistics)
+  float* knorm;            // [B][Hkv][T_cap] or nullptr
+  double* knorm_part;      // [B * Hkv][part_stride][2]
+  int32_t n_sink;          // candidates are [n_sink, T - n_recent)
+  int32_t n_recent;
   SeqTable tab;
 };
 
@@ -93,6 +99,14 @@ struct CombineArgs {
   int32_t n_recent;
   int32_t top_k;
   float lambda;
+  // optional: the key-norm prior's statistics and normaliser partial sums
+  const double* knorm_part;  // [B * Hkv][part_stride][2] or nullptr
+  const float* knorm;        // [B][Hkv][T_cap]
+  double* knorm_stat;        // [B * Hkv][2]: mean and standard deviation of the candidates' norms
+  double* zpart;             // [B * Hkv][zpart_stride]: per mass block, sum of the penalised positional weights
+  int32_t zpart_stride;
+  float knorm_beta;
+  float knorm_c;
   SeqTable tab;  // nsplit = split-K splits; wg_begin counts combine workgroups
   int32_t mass_blocks[kMaxSeqPerLaunch];  // per entry: mass workgroups per KV head
 };
@@ -117,6 +131,7 @@ struct SelectArgs {
   int32_t chunk;         // candidates per workgroup
   float lambda;
   bool hist_ready;       // the top-digit histogram was built with the mass
+  bool pre_scores;       // `mass` holds the candidates' final scores (select_score_kernel)
   // optional: copy the kept rows into packed buffers while emitting them
   const void* k;
   const void* v;
@@ -153,6 +168,33 @@ struct FastArgs {
   float scale_log2;
   SeqTable tab;         // nsplit = chunks per KV head
 };
+
+// Final candidate scores with the optional Selector steps: the prior (with
+// the key-norm correction), its mixture with the evidence, Soft-NMS within a
+// head and exclusivity across heads.  One workgroup scores `chunk` candidate
+// positions of one row for all its KV heads.
+struct ScoreArgs {
+  const float* mass;         // [B][Hkv][T_cap]
+  const float* knorm;        // [B][Hkv][T_cap] or nullptr (no key-norm correction)
+  const double* knorm_stat;  // [B * Hkv][2]
+  const double* zpart;       // [B * Hkv][zpart_stride]
+  float* score;              // [B][Hkv][T_cap]: entries [n_sink, T - n_recent) written
+  int64_t t_cap;
+  int32_t n_kv_heads;
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t zpart_stride;
+  int32_t chunk;
+  float lambda;
+  float knorm_beta;
+  float knorm_c;
+  int32_t nms_radius;
+  float nms_decay;
+  float excl;
+  SeqTable tab;              // nsplit = chunks per row
+};
+constexpr int kScoreThreads = 512;
+constexpr int kScoreLds = 16384;  // floats of LDS for a workgroup's scores
 
 struct SupportArgs {
   const int32_t* sel_idx;
@@ -209,10 +251,11 @@ int32_t fail(int32_t status, const char* fmt, ...);
 // Launchers (defined next to their kernels).  They only enqueue; arguments
 // were validated by the caller.  Return the launch's hipError_t.
 hipError_t launch_slow_partial(const SlowArgs& a, int dtype, int head_dim, int group,
-                               int grid, hipStream_t s);
+                               int grid, hipStream_t s);  // a.knorm set: the variant that also emits key norms
 hipError_t launch_slow_combine(const CombineArgs& a, int head_dim, int group, int grid,
                                hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int grid, hipStream_t s);
 hipError_t launch_fast_partial(const FastArgs& a, int dtype, int head_dim, int group, int grid,
                                hipStream_t s);
 hipError_t launch_fast_merge(const FastArgs& a, int head_dim, int group, hipStream_t s);

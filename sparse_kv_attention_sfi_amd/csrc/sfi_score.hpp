@@ -12,7 +12,8 @@
 namespace sfi {
 
 struct ScoreParams {
-  const float* f;   // mass row, shifted so that f[i] is candidate i
+  const float* f;   // mass row (or final-score row when pre), shifted so that f[i] is candidate i
+  bool pre;         // f already holds the final scores (the optional Selector steps ran)
   int n;
   int lo;           // first candidate position
   float one_minus_lambda;
@@ -24,10 +25,13 @@ struct ScoreParams {
 // in every pass.
 __device__ __forceinline__ uint64_t key_of(const ScoreParams& p, int i, float f) {
 #pragma clang fp contract(off)
-  const float a = static_cast<float>(i + 1);
-  const float b = static_cast<float>(p.n - i);
-  const float r = (__builtin_amdgcn_rcpf(a) + __builtin_amdgcn_rcpf(b)) * p.inv_2h;
-  const float s = __builtin_fmaf(p.lambda, r, p.one_minus_lambda * f);
+  float s = f;
+  if (!p.pre) {
+    const float a = static_cast<float>(i + 1);
+    const float b = static_cast<float>(p.n - i);
+    const float r = (__builtin_amdgcn_rcpf(a) + __builtin_amdgcn_rcpf(b)) * p.inv_2h;
+    s = __builtin_fmaf(p.lambda, r, p.one_minus_lambda * f);
+  }
   uint32_t u = __float_as_uint(s);
   u ^= (u & 0x80000000u) ? 0xffffffffu : 0x80000000u;  // order-preserving
   const uint32_t pos = static_cast<uint32_t>(p.lo + i);

@@ -87,6 +87,7 @@ __device__ __forceinline__ HeadCtx head_ctx(const SelectArgs& a) {
 __device__ __forceinline__ ScoreParams score_params(const SelectArgs& a, const HeadCtx& h, float inv2h) {
   ScoreParams sp;
   sp.f = a.mass + h.bg * a.t_cap + a.n_sink;
+  sp.pre = a.pre_scores;
   sp.n = h.n;
   sp.lo = a.n_sink;
   sp.lambda = a.lambda;
@@ -488,6 +489,126 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     }
     base += total;
   }
+}
+
+// ---------------------------------------------------------------------------
+// optional Selector steps: the candidates' final scores
+// ---------------------------------------------------------------------------
+// One workgroup scores candidate positions [c0, c0 + chunk) of one row for all
+// of its KV heads, in the order of the gist.science technical summary, 2.B:
+//  1. prior r: the positional weight 1/a + 1/(n + 1 - a), times the key-norm
+//     factor exp(-beta * max(0, z - c)) when that correction is on, over its
+//     normaliser (2 H_n, or the sum of the combine's per-block partials), in
+//     double precision;
+//  2. mixture s = (1 - lambda) f + lambda r in float, as the plain Selector
+//     forms it;
+//  3. Soft-NMS: the nearest neighbour within the radius that ranks above the
+//     candidate (higher s, or equal s at a lower position) decays it by
+//     1 - decay * (1 - d / (radius + 1));
+//  4. exclusivity: times its share of the row's heads' total, to the power
+//     excl.
+// Steps 1-2 also cover `radius` positions on either side, so that step 3
+// sees every neighbour.  The final scores go to a.score, where the radix
+// top-k reads them.
+__global__ __launch_bounds__(kScoreThreads) void select_score_kernel(ScoreArgs a) {
+#pragma clang fp contract(off)
+  __shared__ float s_lds[kScoreLds];
+  __shared__ double s_inv[kMaxKvHeads];
+  __shared__ double s_mu[kMaxKvHeads], s_sd[kMaxKvHeads];
+  const int tid = threadIdx.x;
+  const int e = find_entry(a.tab, blockIdx.x);
+  const int cidx = blockIdx.x - a.tab.wg_begin[e];
+  const int b = a.tab.ent[e].seq;
+  const int T = row_ctx(a.tab, e);
+  const int Hkv = a.n_kv_heads;
+  const int n = max(0, T - a.n_sink - a.n_recent);
+  const int c0 = cidx * a.chunk;
+  if (c0 >= n) return;  // past the candidates (grid planned for a longer context)
+  const int R = a.nms_radius;
+  const int W = a.chunk + 2 * R;  // window scored in steps 1-2
+  const int64_t row0 = static_cast<int64_t>(b) * Hkv;
+  const bool knorm = a.knorm != nullptr;
+  // per head: 1 / normaliser of the prior, and the norms' mean and deviation
+  if (tid < Hkv) {
+    const int64_t bg = row0 + tid;
+    if (knorm) {
+      const int nblk = (a.tab.ent[e].ctx + kMassChunk - 1) / kMassChunk;
+      double z = 0.0;
+      for (int k = 0; k < nblk; ++k) z += a.zpart[bg * a.zpart_stride + k];
+      s_inv[tid] = z > 0.0 ? 1.0 / z : 0.0;
+      s_mu[tid] = a.knorm_stat[2 * bg];
+      s_sd[tid] = a.knorm_stat[2 * bg + 1];
+    } else {
+      s_inv[tid] = 1.0 / (2.0 * harmonic_number(n));
+    }
+  }
+  __syncthreads();
+  const float lam = a.lambda, oml = 1.0f - a.lambda;
+  const double beta = a.knorm_beta, kc = a.knorm_c;
+  float* s_mix = s_lds;                     // [Hkv][W]
+  float* s_nms = s_lds + Hkv * W;           // [Hkv][chunk]
+  float* s_tot = s_nms + Hkv * a.chunk;     // [chunk]
+  for (int idx = tid; idx < Hkv * W; idx += kScoreThreads) {
+    const int g = idx / W, q = idx - g * W;
+    const int p = c0 - R + q;
+    float v = -1.0f;
+    if (p >= 0 && p < n) {
+      const int64_t off = (row0 + g) * a.t_cap + a.n_sink + p;
+      double w = 1.0 / (p + 1) + 1.0 / (n - p);
+      if (knorm) {
+        const double sd = s_sd[g];
+        const double z = sd > 0.0 ? (static_cast<double>(a.knorm[off]) - s_mu[g]) / sd : 0.0;
+        w *= exp(-beta * fmax(0.0, z - kc));
+      }
+      const float r = static_cast<float>(w * s_inv[g]);
+      v = __builtin_fmaf(lam, r, oml * a.mass[off]);
+    }
+    s_mix[idx] = v;
+  }
+  __syncthreads();
+  const bool nms = R > 0 && a.nms_decay > 0.f;
+  const int cend = min(a.chunk, n - c0);
+  for (int idx = tid; idx < Hkv * a.chunk; idx += kScoreThreads) {
+    const int g = idx / a.chunk, q = idx - g * a.chunk;
+    if (q >= cend) continue;
+    const int p = c0 + q;
+    const float* m = s_mix + g * W + q + R;  // m[0] is candidate p
+    const float v = m[0];
+    float fac = 1.0f;
+    if (nms) {
+      for (int d = 1; d <= R; ++d) {
+        const bool below = p - d >= 0 && m[-d] >= v;
+        const bool above = p + d < n && m[d] > v;
+        if (below || above) {
+          fac = 1.0f - a.nms_decay * (1.0f - static_cast<float>(d) / static_cast<float>(R + 1));
+          break;
+        }
+      }
+    }
+    s_nms[idx] = v * fac;
+  }
+  __syncthreads();
+  const bool excl = a.excl > 0.f && Hkv > 1;
+  if (excl) {
+    for (int q = tid; q < cend; q += kScoreThreads) {
+      float t = 0.f;
+      for (int g = 0; g < Hkv; ++g) t += s_nms[g * a.chunk + q];
+      s_tot[q] = t;
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < Hkv * a.chunk; idx += kScoreThreads) {
+    const int g = idx / a.chunk, q = idx - g * a.chunk;
+    if (q >= cend) continue;
+    float v = s_nms[idx];
+    if (excl && s_tot[q] > 0.f) v = v * powf(v / s_tot[q], a.excl);
+    a.score[(row0 + g) * a.t_cap + a.n_sink + c0 + q] = v;
+  }
+}
+
+hipError_t launch_score(const ScoreArgs& a, int grid, hipStream_t s) {
+  launch(select_score_kernel, grid, kScoreThreads, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs& a, int grid, hipStream_t s) {

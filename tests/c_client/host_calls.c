@@ -42,9 +42,17 @@ int main(void) {
   EXPECT(sfi_slow_step(&d, ids, 2, (void*)0x30000, (float*)0x40000, NULL, (void*)0x50000, (size_t)1 << 40,
                        NULL) == SFI_ERR_UNSUPPORTED);
   d.head_dim = 64;
-  sfi_support_params sp = {4, 16, 32, 0.1f};
+  sfi_support_params sp = {.n_sink = 4, .n_recent = 16, .top_k = 32, .lambda = 0.1f};
   size_t need = sfi_workspace_bytes(&d, &sp, SFI_OP_SLOW_SELECT);
   EXPECT(need > 0);
+  /* the optional Selector steps: their scores need more workspace; an out-of-range radius fails */
+  sfi_support_params opt = sp;
+  opt.nms_radius = 2;
+  opt.nms_decay = 0.5f;
+  opt.excl = 1.0f;
+  EXPECT(sfi_workspace_bytes(&d, &opt, SFI_OP_SLOW_SELECT) > need);
+  opt.nms_radius = 40;
+  EXPECT(sfi_workspace_bytes(&d, &opt, SFI_OP_SLOW_SELECT) == 0 && strstr(sfi_last_error(), "nms_radius") != NULL);
   EXPECT(sfi_slow_step_select(&d, &sp, ids, 2, (void*)0x30000, (float*)0x40000, (float*)0x60000,
                               (int32_t*)0x70000, (int32_t*)0x80000, NULL, NULL, (void*)0x50000, need - 1,
                               NULL) == SFI_ERR_WORKSPACE);

@@ -84,3 +84,30 @@ def check_support(gpu_sel, f_row, T, ns, W, k, lam, where=""):
     for j in set(ora) - set(gpu):
         assert sc[j] <= sk * (1 + GAP_REL), (where, j, sc[j], sk)
     return "tolerant"
+
+
+def check_support_scores(gpu_sel, ora_sel, score, cand, k, where=""):
+    """Support parity against the oracle's final candidate scores (the
+    optional Selector steps): the GPU set equals the oracle's when the
+    oracle's k-th and (k+1)-th scores are separated by more than GAP_REL
+    relative, else every GPU-only index scores within GAP_REL of the k-th
+    score and every oracle-only index does not exceed it by more."""
+    gpu = sorted(int(x) for x in gpu_sel)
+    ora = [int(x) for x in ora_sel]
+    assert len(gpu) == len(ora), (where, len(gpu), len(ora))
+    assert len(set(gpu)) == len(gpu), where
+    n = len(cand)
+    if n <= k:
+        assert gpu == ora, where
+        return "all"
+    order = np.sort(score)[::-1]
+    sk, sk1 = order[k - 1], order[k]
+    if sk > 0 and (sk - sk1) / sk > GAP_REL:
+        assert gpu == ora, (where, sk, sk1)
+        return "exact"
+    sc = dict(zip(cand.tolist(), score.tolist()))
+    for j in set(gpu) - set(ora):
+        assert sc[j] >= sk * (1 - GAP_REL), (where, j, sc[j], sk)
+    for j in set(ora) - set(gpu):
+        assert sc[j] <= sk * (1 + GAP_REL), (where, j, sc[j], sk)
+    return "tolerant"

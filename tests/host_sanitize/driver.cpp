@@ -68,7 +68,8 @@ static void noalloc_limits() {
   void* fake = reinterpret_cast<void*>(0x3000);
   float* ffake = reinterpret_cast<float*>(0x3000);
   int32_t* ifake = reinterpret_cast<int32_t*>(0x3000);
-  const sfi_support_params sp = {4, 16, 8, 0.1f}, big = {16, 256, 65000, 0.1f};
+  const sfi_support_params sp = {4, 16, 8, 0.1f, 0.f, 0.f, 0, 0.f, 0.f},
+                           big = {16, 256, 65000, 0.1f, 0.f, 0.f, 0, 0.f, 0.f};
   const sfi_kv_desc d65 = desc(65, 8, 2, 64, SFI_F32, 100, ctx.data());
   CHECK(sfi_fast_step_packed_noalloc(&d65, &sp, ids.data(), 65, fake, fake, fake, ifake, ffake, nullptr) ==
         SFI_ERR_UNSUPPORTED);
@@ -95,7 +96,9 @@ static void validation() {
   void* fake = reinterpret_cast<void*>(0x3000);
   float* ffake = reinterpret_cast<float*>(0x3000);
   int32_t* ifake = reinterpret_cast<int32_t*>(0x3000);
-  const sfi_support_params sp = {4, 16, 8, 0.1f}, sp_bad = {4, 16, 8, 1.5f}, sp_empty = {0, 0, 0, 0.1f};
+  const sfi_support_params sp = {4, 16, 8, 0.1f, 0.f, 0.f, 0, 0.f, 0.f},
+                           sp_bad = {4, 16, 8, 1.5f, 0.f, 0.f, 0, 0.f, 0.f},
+                           sp_empty = {0, 0, 0, 0.1f, 0.f, 0.f, 0, 0.f, 0.f};
   const sfi_kv_desc bad[] = {desc(1, 6, 4, 64, SFI_F32, 100, ctx1), desc(1, 24, 2, 64, SFI_F32, 100, ctx1),
                              desc(1, 8, 2, 96, SFI_F32, 100, ctx1), desc(1, 8, 2, 64, 7, 100, ctx1),
                              desc(1, 8, 2, 64, SFI_F32, 0, ctx1)};
@@ -130,7 +133,7 @@ static void validation() {
   CHECK(sfi_debug_support(&d, &sp, id0, 1, ifake, ifake, nullptr, ifake, 8, nullptr) < 0);
   CHECK(sfi_slow_step(&d, id0, 0, fake, ffake, nullptr, fake, 0, nullptr) == SFI_OK);  // nothing to do
   for (int op : {SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_OP_SLOW_SELECT}) {
-    const sfi_support_params big = {16, 256, 2048, 0.1f};
+    const sfi_support_params big = {16, 256, 2048, 0.1f, 0.f, 0.f, 0, 0.f, 0.f};
     const sfi_kv_desc small = desc(1, 32, 8, 128, SFI_BF16, 1000, ctx1);
     const sfi_kv_desc large = desc(1, 32, 8, 128, SFI_BF16, 131072, ctx1);
     const size_t a = sfi_workspace_bytes(&small, &big, op), b = sfi_workspace_bytes(&large, &big, op);

@@ -7,6 +7,7 @@ namespace sfi {
 hipError_t launch_slow_partial(const SlowArgs&, int, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_slow_combine(const CombineArgs&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_select(const SelectArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_score(const ScoreArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_fast_partial(const FastArgs&, int, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_fast_merge(const FastArgs&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_support(const SupportArgs&, int, hipStream_t) { return hipErrorInvalidValue; }

@@ -303,3 +303,30 @@ def test_noalloc_fast_step_rejects_what_its_fixed_scratch_cannot_hold():
     assert call(C.byref(desc), C.byref(sp), dup.ctypes.data_as(C.POINTER(C.c_int32)), 2, a, a, a, a, a,
                 None) == B.SFI_ERR_INVALID_ARG
     assert b"twice" in lib.sfi_last_error()
+
+
+def test_selector_option_ranges_and_the_key_norm_restriction():
+    """The optional Selector steps' parameters are range-checked before any
+    launch; the key-norm correction needs the fused refresh (sfi_select
+    rejects it); too many KV heads for the score pass's LDS are unsupported;
+    and turning an option on enlarges the Selector's workspace."""
+    lib = S.lib()
+    a = C.c_void_p(0x3000)
+    ids = np.zeros(1, dtype=np.int32)
+    pid = ids.ctypes.data_as(C.POINTER(C.c_int32))
+    desc, keep = _desc(batch=1, hq=32, hkv=8, d=128, dtype=B.SFI_BF16, cap=4000, ctx=(4000,))
+    base = B.sfi_support_params(16, 256, 512, 0.1)
+    for kw in (dict(knorm_beta=-1.0), dict(knorm_c=float("nan")), dict(nms_radius=33), dict(nms_radius=-1),
+               dict(nms_decay=1.5), dict(excl=-0.5), dict(excl=float("inf"))):
+        sp = S.support_params(16, 256, 512, 0.1, **kw)
+        assert lib.sfi_select(C.byref(desc), C.byref(sp), pid, 1, a, a, a, a, 1 << 40, None) == B.SFI_ERR_INVALID_ARG, kw
+    sp = S.support_params(16, 256, 512, 0.1, knorm_beta=1.0)
+    assert lib.sfi_select(C.byref(desc), C.byref(sp), pid, 1, a, a, a, a, 1 << 40, None) == B.SFI_ERR_UNSUPPORTED
+    assert b"key norms" in lib.sfi_last_error()
+    wide, kw2 = _desc(batch=1, hq=256, hkv=256, d=64, dtype=B.SFI_BF16, cap=4000, ctx=(4000,))
+    sp = S.support_params(16, 256, 512, 0.1, nms_radius=8, nms_decay=0.5)
+    assert lib.sfi_select(C.byref(wide), C.byref(sp), pid, 1, a, a, a, a, 1 << 40, None) == B.SFI_ERR_UNSUPPORTED
+    for op in (B.SFI_OP_SELECT, B.SFI_OP_SLOW_SELECT):
+        plain = lib.sfi_workspace_bytes(C.byref(desc), C.byref(base), op)
+        opt = lib.sfi_workspace_bytes(C.byref(desc), C.byref(S.support_params(16, 256, 512, 0.1, excl=1.0)), op)
+        assert 0 < plain < opt

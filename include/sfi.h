@@ -49,7 +49,16 @@
  *  - Supported shapes: head_dim 64 or 128; Hq / Hkv in {1, 2, 4, 8};
  *    kv_dtype SFI_F32 or SFI_BF16; 1 <= ctx_len[b] <= kv_capacity <= 2^30;
  *    batch <= 65536; n_kv_heads <= 256.  Support parameters: n_sink and
- *    n_recent <= 2^30, top_k <= 2^24.
+ *    n_recent <= 2^30, top_k <= 2^24; the fast steps take supports of at
+ *    most n_sink + n_recent + top_k <= 512 * R rows, R = 128 rows per
+ *    workgroup by default (65536 rows), and fail with SFI_ERR_UNSUPPORTED
+ *    beyond.
+ *  - Tuning knobs, read from the environment once per process (at the first
+ *    call that needs them): SFI_FAST_TILES = 1, 2 or 4 (default 2) sets the
+ *    fast steps' rows per wave to 16 times that value (R = 64, 128, 256);
+ *    SFI_SLOW_TARGET_WGS (default 1024, at least 64) is the number of
+ *    split-K workgroups the slow step aims at.  Results stay within the same
+ *    tolerances for every setting; the defaults measured fastest on MI355X.
  */
 #ifndef SFI_H_
 #define SFI_H_
@@ -70,7 +79,8 @@ typedef enum {
   SFI_ERR_UNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
   SFI_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   SFI_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
-  SFI_ERR_INJECTED = -5     /* failure forced by SFI_FAULT_INJECT (testing) */
+  SFI_ERR_INJECTED = -5,    /* failure forced by SFI_FAULT_INJECT (testing) */
+  SFI_ERR_NO_MEMORY = -6    /* a host allocation (the scheduler's state) failed */
 } sfi_status;
 
 typedef enum { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;

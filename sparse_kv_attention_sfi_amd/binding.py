@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsfi.so")
 
 SFI_OK, SFI_ERR_INVALID_ARG, SFI_ERR_UNSUPPORTED, SFI_ERR_WORKSPACE, SFI_ERR_HIP, SFI_ERR_INJECTED = 0, -1, -2, -3, -4, -5
+SFI_ERR_NO_MEMORY = -6
 SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_OP_SLOW_SELECT = 0, 1, 2, 3
 SFI_SPAN_FIXED, SFI_SPAN_GEOMETRIC = 0, 1

@@ -615,6 +615,7 @@ const char* sfi_status_str(int32_t st) {
     case SFI_ERR_WORKSPACE: return "SFI_ERR_WORKSPACE";
     case SFI_ERR_HIP: return "SFI_ERR_HIP";
     case SFI_ERR_INJECTED: return "SFI_ERR_INJECTED";
+    case SFI_ERR_NO_MEMORY: return "SFI_ERR_NO_MEMORY";
     default: return "SFI_ERR_UNKNOWN";
   }
 }

@@ -18,6 +18,11 @@
 
 #include "../../include/sfi.h"
 
+namespace sfi {
+// Records the message for sfi_last_error() and returns the status (host runtime).
+int32_t fail(int32_t status, const char* fmt, ...);
+}  // namespace sfi
+
 namespace {
 
 struct SeqState {
@@ -73,30 +78,35 @@ extern "C" {
 
 int32_t sfi_sched_create(int32_t batch, uint64_t seed, int32_t mode, double span_param, int32_t t_max,
                          sfi_sched** out) {
-  if (out == nullptr || batch < 1 || t_max < 0) return SFI_ERR_INVALID_ARG;
+  using sfi::fail;
+  if (out == nullptr) return fail(SFI_ERR_INVALID_ARG, "sfi_sched_create: out is NULL");
   *out = nullptr;
+  if (batch < 1) return fail(SFI_ERR_INVALID_ARG, "sfi_sched_create: batch must be >= 1 (got %d)", batch);
+  if (t_max < 0) return fail(SFI_ERR_INVALID_ARG, "sfi_sched_create: t_max must be >= 0 (got %d)", t_max);
+  int64_t fixed_len = 0;
+  unsigned __int128 threshold = 0;
+  if (mode == SFI_SPAN_FIXED) {
+    if (!(span_param >= 1.0) || span_param != std::floor(span_param) || span_param > 1e15)
+      return fail(SFI_ERR_INVALID_ARG, "sfi_sched_create: a fixed span length must be an integer in [1, 1e15]");
+    fixed_len = static_cast<int64_t>(span_param);
+  } else if (mode == SFI_SPAN_GEOMETRIC) {
+    if (!geometric_threshold(span_param, &threshold))
+      return fail(SFI_ERR_INVALID_ARG, "sfi_sched_create: the geometric mean span must lie in [1, 2^52)");
+  } else {
+    return fail(SFI_ERR_INVALID_ARG, "sfi_sched_create: unknown span mode %d", mode);
+  }
   sfi_sched* s = new (std::nothrow) sfi_sched();
-  if (s == nullptr) return SFI_ERR_INVALID_ARG;
+  if (s == nullptr) return fail(SFI_ERR_NO_MEMORY, "sfi_sched_create: out of host memory");
   s->mode = mode;
   s->t_max = t_max;
-  s->fixed_len = 0;
-  s->threshold = 0;
-  if (mode == SFI_SPAN_FIXED) {
-    if (!(span_param >= 1.0) || span_param != std::floor(span_param) || span_param > 1e15) {
-      delete s;
-      return SFI_ERR_INVALID_ARG;
-    }
-    s->fixed_len = static_cast<int64_t>(span_param);
-  } else if (mode == SFI_SPAN_GEOMETRIC) {
-    if (!geometric_threshold(span_param, &s->threshold)) {
-      delete s;
-      return SFI_ERR_INVALID_ARG;
-    }
-  } else {
+  s->fixed_len = fixed_len;
+  s->threshold = threshold;
+  try {
+    s->seqs.resize(static_cast<size_t>(batch));
+  } catch (const std::bad_alloc&) {
     delete s;
-    return SFI_ERR_INVALID_ARG;
+    return fail(SFI_ERR_NO_MEMORY, "sfi_sched_create: out of host memory for %d sequences", batch);
   }
-  s->seqs.resize(static_cast<size_t>(batch));
   for (int32_t b = 0; b < batch; ++b) {
     s->seqs[b].rng = seed + static_cast<uint64_t>(b);
     s->seqs[b].remaining = 0;
@@ -109,7 +119,7 @@ int32_t sfi_sched_create(int32_t batch, uint64_t seed, int32_t mode, double span
 
 int32_t sfi_sched_step(sfi_sched* s, int32_t* slow_ids, int32_t* n_slow, int32_t* fast_ids, int32_t* n_fast) {
   if (s == nullptr || slow_ids == nullptr || n_slow == nullptr || fast_ids == nullptr || n_fast == nullptr)
-    return SFI_ERR_INVALID_ARG;
+    return sfi::fail(SFI_ERR_INVALID_ARG, "sfi_sched_step: NULL argument");
   int32_t ns = 0, nf = 0;
   for (size_t b = 0; b < s->seqs.size(); ++b) {
     SeqState& q = s->seqs[b];
@@ -131,7 +141,10 @@ int32_t sfi_sched_step(sfi_sched* s, int32_t* slow_ids, int32_t* n_slow, int32_t
 }
 
 int32_t sfi_sched_force_slow(sfi_sched* s, int32_t seq) {
-  if (s == nullptr || seq < 0 || static_cast<size_t>(seq) >= s->seqs.size()) return SFI_ERR_INVALID_ARG;
+  if (s == nullptr) return sfi::fail(SFI_ERR_INVALID_ARG, "sfi_sched_force_slow: scheduler is NULL");
+  if (seq < 0 || static_cast<size_t>(seq) >= s->seqs.size())
+    return sfi::fail(SFI_ERR_INVALID_ARG, "sfi_sched_force_slow: sequence %d out of range [0, %zu)", seq,
+                     s->seqs.size());
   s->seqs[seq].forced = true;
   return SFI_OK;
 }

@@ -330,3 +330,26 @@ def test_selector_option_ranges_and_the_key_norm_restriction():
         plain = lib.sfi_workspace_bytes(C.byref(desc), C.byref(base), op)
         opt = lib.sfi_workspace_bytes(C.byref(desc), C.byref(S.support_params(16, 256, 512, 0.1, excl=1.0)), op)
         assert 0 < plain < opt
+
+
+def test_scheduler_errors_leave_a_message():
+    """Every failing scheduler call sets sfi_last_error() with its own message
+    (not a stale one from an earlier call); the out-of-memory status has its
+    own name."""
+    lib = S.lib()
+    h = C.c_void_p()
+    cases = [((1, 0, B.SFI_SPAN_GEOMETRIC, 0.5, 0), b"geometric mean"),
+             ((1, 0, B.SFI_SPAN_FIXED, 2.5, 0), b"fixed span"),
+             ((0, 0, B.SFI_SPAN_FIXED, 4.0, 0), b"batch"),
+             ((1, 0, 99, 4.0, 0), b"span mode"),
+             ((1, 0, B.SFI_SPAN_FIXED, 4.0, -1), b"t_max")]
+    for args, msg in cases:
+        lib.sfi_status_str(0)
+        st = lib.sfi_sched_create(*args, C.byref(h))
+        assert st == B.SFI_ERR_INVALID_ARG and msg in lib.sfi_last_error(), (args, lib.sfi_last_error())
+    s = S.Scheduler(2, 1, "fixed", 4)
+    with pytest.raises(S.SFIError, match="out of range"):
+        s.force_slow(5)
+    assert lib.sfi_sched_step(None, None, None, None, None) == B.SFI_ERR_INVALID_ARG
+    assert b"sfi_sched_step" in lib.sfi_last_error()
+    assert S.sfi_status_str(B.SFI_ERR_NO_MEMORY) == "SFI_ERR_NO_MEMORY"

@@ -12,7 +12,7 @@ import oracle as O
 import sparse_kv_attention_sfi_amd as S
 import synth
 from synth import gen
-from tests.gpu_helpers import MASS_SUM_TOL, OUT_TOL, check_mass, check_support, np64
+from tests.gpu_helpers import MASS_SUM_TOL, OUT_TOL, TRIPWIRE, check_mass, check_support, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,7 @@ def _check_slow(r, b, q_b, K64, V64, T):
     o_ref, P = O.dense_attention(q_b, K64[:, :T], V64[:, :T])
     f_ref = O.group_mass(P, w.n_kv_heads)
     assert np.max(np.abs(np64(r.out[b]) - o_ref)) < OUT_TOL
+    assert np.max(np.abs(np64(r.out[b]) - o_ref)) < TRIPWIRE
     check_mass(np64(r.mass[b, :, :T]), f_ref, b)
     kinds = [check_support(s, f_ref[g], T, w.n_sink, w.n_recent, w.top_k, w.lam, f"b{b} g{g}")
              for g, s in enumerate(r.gpu_sel(b))]
@@ -176,6 +177,7 @@ def test_8b_layer_sampled_steps(wname, n_fast):
             assert torch.equal(r.out, packed_out)
             ref = O.fast_step(np64(q[t, 0]), K64, V64, T, w.n_sink, w.n_recent, r.gpu_sel(0))
             assert np.max(np.abs(gpu - ref)) < OUT_TOL
+            assert np.max(np.abs(gpu - ref)) < TRIPWIRE
             # with the oracle's own support (differs only at near-ties)
             ref2 = O.fast_step(np64(q[t, 0]), K64, V64, T, w.n_sink, w.n_recent, ora_sels)
             assert np.max(np.abs(gpu - ref2)) < OUT_TOL

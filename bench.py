@@ -128,6 +128,8 @@ def parse():
     p.add_argument("--batch-check", type=int, default=16, metavar="B",
                    help="also time the fast step for B sequences in one launch (0: skip)")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-full-schedule", action="store_true",
+                   help="skip the replay of the whole span schedule (its blended rate is then null)")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the per-workload block (32K layer, batch 16, 32-layer growing history)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -340,17 +342,19 @@ def main():
     # The whole span schedule of the workload (its w.n_steps steps), replayed
     # the same way: the blended rate at the schedule's own slow fraction,
     # whatever share of slow steps the --steps window above happened to hold.
-    full_flags = flags[:w.n_steps]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for t in range(w.n_steps):
-        q_buf.copy_(q_steps[t])
-        run["slow" if full_flags[t] else "fast"]()
-    torch.cuda.synchronize()
-    t_full = time.perf_counter() - t_start
-    full_schedule = {"steps": w.n_steps, "slow_steps": sum(full_flags),
-                     "slow_fraction": sum(full_flags) / w.n_steps,
-                     "blended_steps_per_s_layer": w.n_steps * L / t_full}
+    full_schedule = None
+    if not args.no_full_schedule:
+        full_flags = flags[:w.n_steps]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for t in range(w.n_steps):
+            q_buf.copy_(q_steps[t])
+            run["slow" if full_flags[t] else "fast"]()
+        torch.cuda.synchronize()
+        t_full = time.perf_counter() - t_start
+        full_schedule = {"steps": w.n_steps, "slow_steps": sum(full_flags),
+                         "slow_fraction": sum(full_flags) / w.n_steps,
+                         "blended_steps_per_s_layer": w.n_steps * L / t_full}
 
     # dense-every-step baseline (same queries)
     kd = min(args.dense_steps, n_steps)

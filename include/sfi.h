@@ -234,14 +234,22 @@ int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp,
  * sfi_pack_support copies, for each listed (b, g), the rows
  * K[b][g][sel_idx[b][g][i]] and V[...] for i < sel_cnt[b][g] into
  * packed_k[b][g][i] and packed_v[b][g][i] (device [B][Hkv][top_k][D],
- * kv_dtype).  Indices outside [0, ctx_len[b]) are skipped. */
+ * kv_dtype).  Indices outside [0, ctx_len[b]) are skipped: their slots keep
+ * whatever they held.  The Selector never emits such an index; a caller that
+ * passes its own sel_idx must keep every index below sel_cnt inside the
+ * context, because sfi_fast_step_packed attends to every slot below sel_cnt
+ * (a skipped slot's stale row included) while sfi_fast_step ignores an
+ * out-of-range index. */
 int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
                          const int32_t* seq_ids_host, int32_t n_seq, const int32_t* sel_idx,
                          const int32_t* sel_cnt, void* packed_k, void* packed_v, void* stream);
 
 /* Fast step over a packed support: the same result as sfi_fast_step with the
- * sel_idx that filled packed_k / packed_v; the selected rows are read
- * contiguously from the packed buffers (no index lookups). */
+ * sel_idx that filled packed_k / packed_v, provided every index below sel_cnt
+ * lay inside the context when it was packed (always so for the Selector's
+ * output); the selected rows are read contiguously from the packed buffers
+ * (no index lookups).  Slots at or past min(sel_cnt, the current candidate
+ * count) are never attended, whatever they hold. */
 int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* sp,
                              const int32_t* seq_ids_host, int32_t n_seq, const void* q,
                              const void* packed_k, const void* packed_v, const int32_t* sel_cnt,

@@ -211,7 +211,7 @@ Header header_layout(const sfi_kv_desc* d) {
 size_t header_bytes(const sfi_kv_desc* d) { return header_layout(d).end; }
 
 struct SelectLayout {
-  size_t list, chunk_above, head_info, end;
+  size_t list, chunk_above, head_info, above_pos, end;
 };
 SelectLayout select_layout(const sfi_kv_desc* d) {
   const size_t bh = static_cast<size_t>(d->batch) * d->n_kv_heads;
@@ -219,7 +219,8 @@ SelectLayout select_layout(const sfi_kv_desc* d) {
   L.list = header_bytes(d);
   L.chunk_above = L.list + align_up(bh * kSelListCap * sizeof(uint64_t));
   L.head_info = L.chunk_above + align_up(bh * kSelMaxChunks * sizeof(int32_t));
-  L.end = L.head_info + align_up(bh * 2 * sizeof(int32_t));
+  L.above_pos = L.head_info + align_up(bh * 2 * sizeof(int32_t));
+  L.end = L.above_pos + align_up(bh * static_cast<size_t>(d->kv_capacity) * sizeof(int32_t));
   return L;
 }
 
@@ -504,6 +505,7 @@ void plan_select(const sfi_kv_desc* desc, const sfi_support_params* sp, const in
   a.list = reinterpret_cast<uint64_t*>(w + L.list);
   a.chunk_above = reinterpret_cast<int32_t*>(w + L.chunk_above);
   a.head_info = reinterpret_cast<int32_t*>(w + L.head_info);
+  a.above_pos = reinterpret_cast<int32_t*>(w + L.above_pos);
   a.t_cap = desc->kv_capacity;
   a.n_kv_heads = desc->n_kv_heads;
   a.n_sink = sp->n_sink;

@@ -1326,7 +1326,8 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   __shared__ float s_m[NW * G], s_l[NW * G];
   __shared__ FastTailSmem s_tail;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar, so every test on a wave's rows is a scalar branch
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x;
   const int e = ONE ? 0 : find_entry(a.tab, wg);
   const int local = ONE ? wg : wg - a.tab.wg_begin[e];
@@ -1346,19 +1347,6 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   const char* Kp = static_cast<const char*>(a.packed_k) + bg * a.top_k * RB;
   const char* Vp = static_cast<const char*>(a.packed_v) + bg * a.top_k * RB;
   const int64_t qh0 = static_cast<int64_t>(b) * a.n_q_heads + g * G;
-  // byte offset of support row p from the cache or packed base
-  auto row_off = [&](int p, bool& packed) -> int64_t {
-    packed = false;
-    if (p < ns_eff) return static_cast<int64_t>(p) * RB;
-    if (p < fixed) return static_cast<int64_t>(w_lo + p - ns_eff) * RB;
-    const int qrow = p - fixed;
-    if (qrow < kmax) {
-      packed = true;
-      return static_cast<int64_t>(qrow) * RB;
-    }
-    return 0;
-  };
-
   uint4 qa[A::kNL];
   load_q<E, D, G>(a.q, qh0, lane, qa);
   A st;
@@ -1368,20 +1356,47 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   const int vr = lane / A::kPPR, vp = lane % A::kPPR;
   uint4 kb[TILES][A::kNL];
   uint4 vb[NV];
+  // Row addresses, by wave-uniform tests: in waves whose rows are all packed
+  // slots (most of them) a row is its buffer's base plus a 32-bit offset,
+  // slots past kmax re-reading the last one (masked below); waves that reach
+  // into the sinks or the window pick each row's source with selects; waves
+  // past the largest possible support read cache row 0 (and compute
+  // nothing).  Every wave then issues the same straight run of loads, so the
+  // MFMAs wait for them one by one.
+  const char* krow[TILES];
+  const char* vrow[NV];
+  if (w0 >= fixed + kmax) {
 #pragma unroll
-  for (int tt = 0; tt < TILES; ++tt) {
-    bool pk;
-    const int64_t off = row_off(w0 + 16 * tt + kr, pk);
-    const char* src = (pk ? Kp : Kc) + off + 16 * kg;
+    for (int tt = 0; tt < TILES; ++tt) krow[tt] = Kc + 16 * kg;
 #pragma unroll
-    for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16_stream(src + 64 * kk);
+    for (int i = 0; i < NV; ++i) vrow[i] = Vc + 16 * vp;
+  } else if (w0 >= fixed) {
+    const int q0 = w0 - fixed, qlast = kmax - 1;
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt)
+      krow[tt] = Kp + (static_cast<uint32_t>(min(q0 + 16 * tt + kr, qlast)) * RB + 16 * kg);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      vrow[i] = Vp + (static_cast<uint32_t>(min(q0 + vr + A::kRPL * i, qlast)) * RB + 16 * vp);
+  } else {
+    // support element p: a sink or window row of the cache, a packed slot,
+    // or (past kmax) cache row 0
+    auto src = [&](int p, const char* cache, const char* packed) -> const char* {
+      const bool pk = p >= fixed && p - fixed < kmax;
+      const int crow = p < ns_eff ? p : (p < fixed ? w_lo + p - ns_eff : 0);
+      return pk ? packed + static_cast<int64_t>(p - fixed) * RB : cache + static_cast<int64_t>(crow) * RB;
+    };
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) krow[tt] = src(w0 + 16 * tt + kr, Kc, Kp) + 16 * kg;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vrow[i] = src(w0 + vr + A::kRPL * i, Vc, Vp) + 16 * vp;
   }
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    bool pk;
-    const int64_t off = row_off(w0 + vr + A::kRPL * i, pk);
-    vb[i] = ld16_stream((pk ? Vp : Vc) + off + 16 * vp);
-  }
+  for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+    for (int kk = 0; kk < A::kNL; ++kk) kb[tt][kk] = ld16_stream(krow[tt] + 64 * kk);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) vb[i] = ld16_stream(vrow[i]);
   const int cnt = min(max(a.sel_cnt[bg], 0), kmax);
   const int size = fixed + cnt;
   bool kvalid[TILES];
@@ -1389,10 +1404,13 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   for (int tt = 0; tt < TILES; ++tt) kvalid[tt] = (w0 + 16 * tt + kr) < size;
   // Rows past the support (packed slots cnt .. kmax - 1 were not written by
   // this span's selection) get zero V: their probability is zero, but 0 * V
-  // would still turn a non-finite stale value into NaN.
+  // would still turn a non-finite stale value into NaN.  Only the wave that
+  // straddles the end of the support takes this branch.
+  if (w0 < size && w0 + ROWS > size) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (w0 + vr + A::kRPL * i >= size) vb[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NV; ++i)
+      if (w0 + vr + A::kRPL * i >= size) vb[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (w0 < size) {
     if constexpr (kMfma) {
       st.template consume_pv_mfma<TILES>(qa, kb, vb, kvalid, s_p + wave * ROWS * G, s_v + wave * ROWS * RB,

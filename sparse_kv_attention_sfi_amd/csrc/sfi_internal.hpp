@@ -122,6 +122,8 @@ struct SelectArgs {
   // per-call scratch
   uint64_t* list;        // [B * Hkv][kSelListCap] keys of the threshold bin
   int32_t* chunk_above;  // [B * Hkv][kSelMaxChunks] keys above the bin per chunk
+  int32_t* above_pos;    // [B * Hkv][t_cap]: from each chunk's first candidate on, the
+                         // candidate indices of its keys above the bin, ascending
   int32_t* head_info;    // [B * Hkv][2] threshold bin, keys above it
   int64_t t_cap;
   int32_t n_kv_heads;

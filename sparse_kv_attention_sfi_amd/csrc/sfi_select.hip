@@ -281,6 +281,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
   }
   const ScoreParams sp = score_params(a, h, s_inv2h);
   uint64_t* glist = a.list + h.bg * kSelListCap;
+  int32_t* gabove = a.above_pos + h.bg * a.t_cap + i0;
   int gt_all = 0;
   for (int t0 = i0; t0 < i1; t0 += kGatherStep) {
     if (t0 != i0) {
@@ -304,6 +305,16 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
     // one scan of both counts: (gt << 16) | eq, totals below 2^16 per pass
     int tot;
     const int pre = block_excl_scan((gt << 16) | eq, s_wave, &tot);
+    // this thread's keys above the bin, in candidate order after those of
+    // the threads and passes before it
+    if (gt > 0) {
+      int slot = gt_all + (pre >> 16);
+#pragma unroll
+      for (int u = 0; u < kRun; ++u) {
+        const int i = t0 + tid * kRun + u;
+        if (i < i1 && top_digit(key[u]) > d1) gabove[slot++] = i;
+      }
+    }
     gt_all += tot >> 16;
     const int eq_tot = tot & 0xffff;
     if (eq_tot > 0) {
@@ -367,16 +378,29 @@ __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const
 // Writes the kept positions of the workgroup's chunk in ascending order at the
 // chunk's output offset.  With PACK it also copies their K and V rows into the
 // packed buffers at the same slots, so the fast step reads them contiguously.
-// The chunk's evidence, the head's bookkeeping and the head of the threshold
-// bin's list are all requested in the first round trip.
+//
+// Usual case (the threshold bin's list fits in LDS and a chunk is at most
+// kStep candidates): the chunk's kept keys are its keys above the bin, listed
+// by select_gather, and its list keys at or above K*, so the evidence is not
+// read again.  The rows above the bin are certain to be kept: their loads are
+// issued before K* is resolved and land in registers while it is, and go to
+// their slots once the ranks are known.  A bitmap of the chunk's kept
+// candidates gives every kept row its rank.  Otherwise the chunk's keys are
+// recomputed from the evidence and compared with K*.
 template <bool PACK>
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
   constexpr int kStep = kGatherStep;  // candidates per emission pass (kRun per thread)
+  constexpr int kWords = kStep / 32;
+  constexpr int kPreU = 8;            // prefetched 16-byte pieces of K (and of V) per thread
   __shared__ __attribute__((aligned(16))) uint64_t s_list[kSelListCap];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSelBins];
-  __shared__ int s_pos[PACK ? kStep : 1];
+  __shared__ int s_pos[kStep];
+  __shared__ int s_late[PACK ? kStep : 1];
+  __shared__ uint32_t s_bits[kWords];
+  __shared__ int s_wpre[kWords];
   __shared__ int s_wave[kSelWaves];
   __shared__ int s_res[2];
+  __shared__ int s_nlate;
   __shared__ uint64_t s_kstar;
   const HeadCtx h = head_ctx(a);
   const int tid = threadIdx.x;
@@ -400,6 +424,144 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   }
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
   if (h.c > 0 && i0 >= h.n) return;  // past the candidates (grid planned for a longer context)
+  const int lo = a.n_sink + i0;      // first position of this chunk
+  // first round trip: the head's bookkeeping, the head of the threshold bin's
+  // list, this chunk's count and first entries of keys above the bin
+  const int d1 = a.head_info[2 * h.bg];
+  const int above = a.head_info[2 * h.bg + 1];
+  const int cnt_d1 = a.list_n[h.bg];
+  const int n_ab = a.chunk_above[h.bg * kSelMaxChunks + h.c];
+  const uint64_t* glist = a.list + h.bg * kSelListCap;
+  const int32_t* gabove = a.above_pos + h.bg * a.t_cap + i0;
+  const uint64_t first = glist[tid];  // always inside the list; used if tid < cnt_d1
+  const int ab_first = i0 + tid < i1 ? gabove[tid] : 0;
+  // keys above the threshold bin in the chunks before this one (this
+  // thread's share)
+  int above_before = 0;
+  for (int c = tid; c < h.c; c += kSelThreads) above_before += a.chunk_above[h.bg * kSelMaxChunks + c];
+  const int need = K - above;  // rank of K* inside bin d1 (1-based)
+  const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
+  const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
+  if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = K;
+
+  if (a.chunk <= kStep && cnt_d1 <= kSelListCap) {
+    const int len = i1 - i0, nw = (len + 31) >> 5;
+    s_list[tid] = first;
+    for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
+    if (tid < n_ab) s_pos[tid] = ab_first;
+    for (int r = kSelThreads + tid; r < n_ab; r += kSelThreads) s_pos[r] = gabove[r];
+    if (tid < kWords) s_bits[tid] = 0u;
+    if (tid == 0) s_nlate = 0;
+    __syncthreads();
+    // rows above the bin: loads issued now, stored once their slots are known
+    const int np = a.row_bytes >> 4;
+    const int n_pre = PACK ? min(n_ab, kPreU * kSelThreads / np) : 0;
+    const char* Kc = static_cast<const char*>(a.k) + h.bg * a.t_cap * a.row_bytes;
+    const char* Vc = static_cast<const char*>(a.v) + h.bg * a.t_cap * a.row_bytes;
+    uint4 pk[PACK ? kPreU : 1], pv[PACK ? kPreU : 1];
+    if (PACK) {
+#pragma unroll
+      for (int u = 0; u < kPreU; ++u) {
+        const int it = tid + kSelThreads * u;
+        const int r = it / np, pc = it - r * np;
+        if (r < n_pre) {
+          const int64_t off = static_cast<int64_t>(a.n_sink + s_pos[r]) * a.row_bytes + 16 * pc;
+          pk[u] = ld16_stream(Kc + off);
+          pv[u] = ld16_stream(Vc + off);
+        }
+      }
+    }
+    const uint64_t kstar =
+        cnt_d1 <= kSelThreads
+            ? rank_select(s_list, cnt_d1, need, reinterpret_cast<int*>(s_hist), &s_kstar)
+            : radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
+                            s_hist, s_wave, s_res, &s_kstar);
+    // mark the chunk's kept candidates; count the kept list keys before it
+    int before = above_before;
+    for (int i = tid; i < cnt_d1; i += kSelThreads) {
+      const uint64_t key = s_list[i];
+      if (key < kstar) continue;
+      const int p = key_position(key) - lo;
+      if (p < 0) {
+        ++before;
+      } else if (p < len) {
+        atomicOr(&s_bits[p >> 5], 1u << (p & 31));
+        if (PACK) s_late[atomicAdd(&s_nlate, 1)] = p;
+      }
+    }
+    for (int r = tid; r < n_ab; r += kSelThreads) {
+      const int p = s_pos[r] - i0;
+      atomicOr(&s_bits[p >> 5], 1u << (p & 31));
+      if (PACK && r >= n_pre) s_late[atomicAdd(&s_nlate, 1)] = p;
+    }
+    int base;
+    (void)block_excl_scan(before, s_wave, &base);  // its barriers also complete the marking
+    const uint32_t wbits = tid < nw ? s_bits[tid] : 0u;
+    int wtot;
+    const int wpre = block_excl_scan(__popc(wbits), s_wave, &wtot);
+    if (tid < nw) s_wpre[tid] = wpre;
+    __syncthreads();
+    if (tid < nw) {
+      int k = base + wpre;
+      for (uint32_t bits = wbits; bits != 0u; bits &= bits - 1u, ++k)
+        if (k < K) out[k] = lo + 32 * tid + (__ffs(bits) - 1);
+    }
+    if (PACK) {
+      // slot of kept candidate p of the chunk
+      auto slot_of = [&](int p) {
+        return base + s_wpre[p >> 5] + __popc(s_bits[p >> 5] & ((1u << (p & 31)) - 1u));
+      };
+      char* PK = static_cast<char*>(a.packed_k) + h.bg * K * a.row_bytes;
+      char* PV = static_cast<char*>(a.packed_v) + h.bg * K * a.row_bytes;
+#pragma unroll
+      for (int u = 0; u < kPreU; ++u) {
+        const int it = tid + kSelThreads * u;
+        const int r = it / np, pc = it - r * np;
+        if (r < n_pre) {
+          const int slot = slot_of(s_pos[r] - i0);
+          if (slot < K) {
+            const int64_t off = static_cast<int64_t>(slot) * a.row_bytes + 16 * pc;
+            *reinterpret_cast<uint4*>(PK + off) = pk[u];
+            *reinterpret_cast<uint4*>(PV + off) = pv[u];
+          }
+        }
+      }
+      // the kept rows of the threshold bin and the rows above it past the
+      // prefetch: copied now
+      const int items = s_nlate * np;
+      constexpr int kU = 4;
+      for (int j0 = tid; j0 < items; j0 += kU * kSelThreads) {
+        uint4 kv[kU], vv[kU];
+        int slot[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int it = j0 + u * kSelThreads;
+          slot[u] = K;
+          if (it < items) {
+            const int r = it / np, pc = it - r * np;
+            const int p = s_late[r];
+            slot[u] = slot_of(p);
+            const int64_t off = static_cast<int64_t>(lo + p) * a.row_bytes + 16 * pc;
+            kv[u] = ld16_stream(Kc + off);
+            vv[u] = ld16_stream(Vc + off);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int it = j0 + u * kSelThreads;
+          if (it < items && slot[u] < K) {
+            const int pc = it - (it / np) * np;
+            const int64_t off = static_cast<int64_t>(slot[u]) * a.row_bytes + 16 * pc;
+            *reinterpret_cast<uint4*>(PK + off) = kv[u];
+            *reinterpret_cast<uint4*>(PV + off) = vv[u];
+          }
+        }
+      }
+    }
+    return;
+  }
+
+  // general case: keys recomputed from the evidence
   const float* frow = a.mass + h.bg * a.t_cap + a.n_sink;
   float fv[kRun];
 #pragma unroll
@@ -407,25 +569,12 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     const int i = i0 + tid * kRun + u;
     fv[u] = i < i1 ? frow[i] : 0.f;
   }
-  const int d1 = a.head_info[2 * h.bg];
-  const int above = a.head_info[2 * h.bg + 1];
-  const int cnt_d1 = a.list_n[h.bg];
-  const uint64_t* glist = a.list + h.bg * kSelListCap;
-  const uint64_t first = glist[tid];  // always inside the list; used if tid < cnt_d1
-  // keys above the threshold bin in the chunks before this one (this
-  // thread's share), requested with the first round trip
-  int above_before = 0;
-  for (int c = tid; c < h.c; c += kSelThreads) above_before += a.chunk_above[h.bg * kSelMaxChunks + c];
   const float inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
   const ScoreParams sp = score_params(a, h, inv2h);
-  // keys of the first pass, computed while the list is still on its way
   uint64_t key[kRun];
 #pragma unroll
   for (int u = 0; u < kRun; ++u) key[u] = key_of(sp, i0 + tid * kRun + u, fv[u]);
   s_list[tid] = first;
-  const int need = K - above;  // rank of K* inside bin d1 (1-based)
-  const uint64_t pfx = static_cast<uint64_t>(d1) << (64 - kSelDigitBits);
-  const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
   uint64_t kstar;
   int before;  // kept keys of the chunks before this one (this thread's share)
   if (cnt_d1 <= kSelListCap) {
@@ -436,7 +585,6 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
                 ? rank_select(s_list, cnt_d1, need, reinterpret_cast<int*>(s_hist), &s_kstar)
                 : radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, cnt_d1, pfx, pmask, 64 - kSelDigitBits,
                                 need, s_hist, s_wave, s_res, &s_kstar);
-    const int lo = a.n_sink + i0;  // first position of this chunk
     for (int i = tid; i < cnt_d1; i += kSelThreads) {
       const uint64_t key = s_list[i];
       before += key >= kstar && key_position(key) < lo;
@@ -452,7 +600,6 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   }
   int base;
   (void)block_excl_scan(before, s_wave, &base);
-  if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = K;
   for (int t0 = i0; t0 < i1; t0 += kStep) {
     if (t0 != i0) {
 #pragma unroll

@@ -126,6 +126,142 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int 
   __syncthreads();
 }
 
+// find_digit over the 4096-bin top-digit histogram read straight from global
+// memory into registers: thread t holds bins 8 (kSelThreads - 1 - t) ... + 7
+// (thread 0 the highest), loaded as two 16-byte pieces.
+static_assert(kSelBins == 8 * kSelThreads, "eight top-digit bins per thread");
+__device__ __forceinline__ void load_top_bins(const uint32_t* ghist, uint32_t (&hv)[8]) {
+  const int b0 = (kSelThreads - 1 - threadIdx.x) * 8;
+  const uint4 lo = reinterpret_cast<const uint4*>(ghist + b0)[0];
+  const uint4 hi = reinterpret_cast<const uint4*>(ghist + b0)[1];
+  hv[0] = lo.x; hv[1] = lo.y; hv[2] = lo.z; hv[3] = lo.w;
+  hv[4] = hi.x; hv[5] = hi.y; hv[6] = hi.z; hv[7] = hi.w;
+}
+__device__ __forceinline__ void find_top_digit(const uint32_t (&hv)[8], int need, int* s_wave, int* s_res) {
+  const int tid = threadIdx.x;
+  const int b0 = (kSelThreads - 1 - tid) * 8;
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) local += static_cast<int>(hv[u]);
+  int tot;
+  const int above_me = block_excl_scan(local, s_wave, &tot);
+  if (above_me < need && need <= above_me + local) {
+    int run = above_me;
+#pragma unroll
+    for (int u = 7; u >= 0; --u) {
+      const int c = static_cast<int>(hv[u]);
+      if (run + c >= need) {
+        s_res[0] = b0 + u;
+        s_res[1] = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+}
+
+// K* among the m threshold-bin keys in LDS (m <= kSelListCap): the key with
+// exactly need - 1 larger keys.  The bits below the top digit are resolved
+// 8 at a time: the keys that match the resolved prefix are histogrammed into
+// 256 LDS bins and one wave scans them; once at most 64 keys match the
+// prefix, they are gathered and one wave ranks them.  s_h: 256 words,
+// s_small: 64 keys, s_res: 4 ints.
+__device__ uint64_t list_resolve(const uint64_t* keys, int m, int need, uint64_t prefix, uint64_t pmask, int shift,
+                                 uint32_t* s_h, uint64_t* s_small, int* s_res, uint64_t* s_key) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int match = m;
+  while (match > 64 && shift > 0) {
+    const int width = shift >= 8 ? 8 : shift;
+    shift -= width;
+    const uint32_t dmask = (1u << width) - 1u;
+    if (tid < 256) s_h[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < m; i += kSelThreads) {
+      const uint64_t key = keys[i];
+      if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l: bins 255 - 4 l (first) down to 252 - 4 l
+      const uint4 h4 = reinterpret_cast<const uint4*>(s_h)[63 - lane];
+      const int hb[4] = {static_cast<int>(h4.w), static_cast<int>(h4.z), static_cast<int>(h4.y),
+                         static_cast<int>(h4.x)};
+      const int c = hb[0] + hb[1] + hb[2] + hb[3];
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+      }
+      int run = incl - c;
+      if (run < need && need <= incl) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (run + hb[u] >= need) {
+            s_res[0] = 255 - 4 * lane - u;
+            s_res[1] = run;
+            s_res[2] = hb[u];
+            break;
+          }
+          run += hb[u];
+        }
+      }
+    }
+    __syncthreads();
+    const int digit = s_res[0];
+    need -= s_res[1];
+    match = s_res[2];
+    prefix |= static_cast<uint64_t>(digit) << shift;
+    pmask |= static_cast<uint64_t>(dmask) << shift;
+    __syncthreads();
+  }
+  if (tid == 0) s_res[3] = 0;
+  __syncthreads();
+  for (int i = tid; i < m; i += kSelThreads) {
+    const uint64_t key = keys[i];
+    if ((key & pmask) == prefix) {
+      const int slot = atomicAdd(&s_res[3], 1);
+      if (slot < 64) s_small[slot] = key;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int cnt = min(s_res[3], 64);
+    const uint64_t mine = lane < cnt ? s_small[lane] : 0ull;
+    int rank = 0;
+    for (int j = 0; j < cnt; ++j) rank += s_small[j] > mine;
+    if (lane < cnt && rank == need - 1) *s_key = mine;
+  }
+  __syncthreads();
+  return *s_key;
+}
+
+// Exclusive prefix sum over the workgroup of two counters at once (64-bit
+// lanes: a in the high word, b in the low word); *total gets both sums.
+__device__ __forceinline__ uint64_t block_excl_scan2(uint32_t a, uint32_t b, uint64_t* s_wave2, uint64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t v = (static_cast<uint64_t>(a) << 32) | b;
+  uint64_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wave2[wave] = incl;
+  __syncthreads();
+  uint64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint64_t x = s_wave2[w];
+    before += (w < wave) ? x : 0ull;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
 // Among m <= kSelThreads distinct keys in LDS (16-byte aligned), the one with
 // exactly need - 1 larger keys.  The list is cut into P = kSelThreads / m
 // parts; thread t counts the keys of part t / m that exceed key t % m (eight
@@ -247,7 +383,6 @@ constexpr int kRun = 8;                         // candidates per thread and pas
 constexpr int kGatherStep = kRun * kSelThreads;  // candidates per pass
 
 __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSelBins];
   __shared__ int s_wave[kSelWaves];
   __shared__ int s_res[2];
   __shared__ int s_base;
@@ -258,9 +393,12 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
   if (h.keep_all || (h.c > 0 && h.c * a.chunk >= h.n)) return;
   const int tid = threadIdx.x;
   const int i0 = h.c * a.chunk, i1 = min(h.n, i0 + a.chunk);
-  // each thread owns a contiguous run of kRun candidates per pass, so its
-  // keys in d1 are written without per-key atomics; the first pass's evidence
-  // is loaded before the histogram so both share a round trip
+  // the histogram is requested first, then the first pass's evidence, so
+  // the threshold bin is found while the evidence is still on its way; each
+  // thread owns a contiguous run of kRun candidates per pass, so its keys in
+  // d1 are written without per-key atomics
+  uint32_t hv[8];
+  load_top_bins(a.hist + h.bg * kSelBins, hv);
   const float* frow = a.mass + h.bg * a.t_cap + a.n_sink;
   float fv[kRun];
 #pragma unroll
@@ -269,11 +407,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
     fv[u] = i < i1 ? frow[i] : 0.f;
   }
   if (tid == 0) s_inv2h = static_cast<float>(1.0 / (2.0 * harmonic_number(h.n)));
-  const uint32_t* gh = a.hist + h.bg * kSelBins;
-  for (int i = tid; i < kSelBins / 4; i += kSelThreads)
-    reinterpret_cast<uint4*>(s_hist)[i] = reinterpret_cast<const uint4*>(gh)[i];
-  __syncthreads();
-  find_digit(s_hist, kSelBins, a.top_k, s_wave, s_res);
+  find_top_digit(hv, a.top_k, s_wave, s_res);
   const uint32_t d1 = static_cast<uint32_t>(s_res[0]);
   if (h.c == 0 && tid == 0) {
     a.head_info[2 * h.bg] = s_res[0];
@@ -343,7 +477,8 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(SelectArgs a
 // Copies rows pos[r] of the cache into slots base + r of the packed buffers
 // for r < count; workgroup-wide cooperative 16-byte copies.
 __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const int* s_pos, int base, int count) {
-  const int np = a.row_bytes >> 4;  // 16-byte pieces per row
+  const int np = a.row_bytes >> 4;  // 16-byte pieces per row (8, 16 or 32)
+  const int lg = __builtin_ctz(np);
   const int items = count * np;
   const char* K = static_cast<const char*>(a.k) + bg * a.t_cap * a.row_bytes;
   const char* V = static_cast<const char*>(a.v) + bg * a.t_cap * a.row_bytes;
@@ -356,7 +491,7 @@ __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const
     for (int u = 0; u < kU; ++u) {
       const int it = i0 + u * kSelThreads;
       if (it < items) {
-        const int r = it / np, pc = it - r * np;
+        const int r = it >> lg, pc = it & (np - 1);
         const int64_t off = static_cast<int64_t>(s_pos[r]) * a.row_bytes + 16 * pc;
         kv[u] = ld16_stream(K + off);
         vv[u] = ld16_stream(V + off);
@@ -366,7 +501,7 @@ __device__ __forceinline__ void copy_rows(const SelectArgs& a, int64_t bg, const
     for (int u = 0; u < kU; ++u) {
       const int it = i0 + u * kSelThreads;
       if (it < items) {
-        const int r = it / np, pc = it - r * np;
+        const int r = it >> lg, pc = it & (np - 1);
         const int64_t off = static_cast<int64_t>(r) * a.row_bytes + 16 * pc;
         *reinterpret_cast<uint4*>(PK + off) = kv[u];
         *reinterpret_cast<uint4*>(PV + off) = vv[u];
@@ -399,7 +534,9 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   __shared__ uint32_t s_bits[kWords];
   __shared__ int s_wpre[kWords];
   __shared__ int s_wave[kSelWaves];
-  __shared__ int s_res[2];
+  __shared__ uint64_t s_wave2[kSelWaves];
+  __shared__ uint64_t s_small[64];
+  __shared__ int s_res[4];
   __shared__ int s_nlate;
   __shared__ uint64_t s_kstar;
   const HeadCtx h = head_ctx(a);
@@ -454,8 +591,9 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     if (tid == 0) s_nlate = 0;
     __syncthreads();
     // rows above the bin: loads issued now, stored once their slots are known
-    const int np = a.row_bytes >> 4;
-    const int n_pre = PACK ? min(n_ab, kPreU * kSelThreads / np) : 0;
+    const int np = a.row_bytes >> 4;  // 8, 16 or 32 pieces per row
+    const int lg = __builtin_ctz(np);
+    const int n_pre = PACK ? min(n_ab, (kPreU * kSelThreads) >> lg) : 0;
     const char* Kc = static_cast<const char*>(a.k) + h.bg * a.t_cap * a.row_bytes;
     const char* Vc = static_cast<const char*>(a.v) + h.bg * a.t_cap * a.row_bytes;
     uint4 pk[PACK ? kPreU : 1], pv[PACK ? kPreU : 1];
@@ -463,7 +601,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
 #pragma unroll
       for (int u = 0; u < kPreU; ++u) {
         const int it = tid + kSelThreads * u;
-        const int r = it / np, pc = it - r * np;
+        const int r = it >> lg, pc = it & (np - 1);
         if (r < n_pre) {
           const int64_t off = static_cast<int64_t>(a.n_sink + s_pos[r]) * a.row_bytes + 16 * pc;
           pk[u] = ld16_stream(Kc + off);
@@ -472,10 +610,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
       }
     }
     const uint64_t kstar =
-        cnt_d1 <= kSelThreads
-            ? rank_select(s_list, cnt_d1, need, reinterpret_cast<int*>(s_hist), &s_kstar)
-            : radix_resolve([&](int i) { return s_list[i]; }, cnt_d1, cnt_d1, pfx, pmask, 64 - kSelDigitBits, need,
-                            s_hist, s_wave, s_res, &s_kstar);
+        list_resolve(s_list, cnt_d1, need, pfx, pmask, 64 - kSelDigitBits, s_hist, s_small, s_res, &s_kstar);
     // mark the chunk's kept candidates; count the kept list keys before it
     int before = above_before;
     for (int i = tid; i < cnt_d1; i += kSelThreads) {
@@ -494,11 +629,12 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
       atomicOr(&s_bits[p >> 5], 1u << (p & 31));
       if (PACK && r >= n_pre) s_late[atomicAdd(&s_nlate, 1)] = p;
     }
-    int base;
-    (void)block_excl_scan(before, s_wave, &base);  // its barriers also complete the marking
+    __syncthreads();  // the marking is complete
     const uint32_t wbits = tid < nw ? s_bits[tid] : 0u;
-    int wtot;
-    const int wpre = block_excl_scan(__popc(wbits), s_wave, &wtot);
+    uint64_t tot2;
+    const uint64_t pre2 = block_excl_scan2(static_cast<uint32_t>(before), __popc(wbits), s_wave2, &tot2);
+    const int base = static_cast<int>(tot2 >> 32);              // kept keys before the chunk
+    const int wpre = static_cast<int>(pre2 & 0xffffffffull);   // kept candidates before word tid
     if (tid < nw) s_wpre[tid] = wpre;
     __syncthreads();
     if (tid < nw) {
@@ -516,7 +652,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
 #pragma unroll
       for (int u = 0; u < kPreU; ++u) {
         const int it = tid + kSelThreads * u;
-        const int r = it / np, pc = it - r * np;
+        const int r = it >> lg, pc = it & (np - 1);
         if (r < n_pre) {
           const int slot = slot_of(s_pos[r] - i0);
           if (slot < K) {
@@ -538,7 +674,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
           const int it = j0 + u * kSelThreads;
           slot[u] = K;
           if (it < items) {
-            const int r = it / np, pc = it - r * np;
+            const int r = it >> lg, pc = it & (np - 1);
             const int p = s_late[r];
             slot[u] = slot_of(p);
             const int64_t off = static_cast<int64_t>(lo + p) * a.row_bytes + 16 * pc;
@@ -550,7 +686,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
         for (int u = 0; u < kU; ++u) {
           const int it = j0 + u * kSelThreads;
           if (it < items && slot[u] < K) {
-            const int pc = it - (it / np) * np;
+            const int pc = it & (np - 1);
             const int64_t off = static_cast<int64_t>(slot[u]) * a.row_bytes + 16 * pc;
             *reinterpret_cast<uint4*>(PK + off) = kv[u];
             *reinterpret_cast<uint4*>(PV + off) = vv[u];

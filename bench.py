@@ -463,6 +463,15 @@ def main():
     def us(name):
         return kern.get(name, {}).get("avg_us", 0.0)
 
+    # what one launch of each kernel group does on this workload
+    scope = {"slow_partial": "split-K dense attention over the whole context, writing the logits for the mass",
+             "slow_combine": "merge of the split partials, the mass and the Selector's first histogram",
+             "select": "Selector: threshold-bin gather and emission of the kept positions with their packed rows",
+             "fast_partial": ("the whole fast step: sparse attention over the support in chunks, and, when the "
+                              "launch fits the CUs, the merge of the chunk states in the same kernel"
+                              if "fast_merge" not in kern else "sparse attention over the support in chunks"),
+             "fast_merge": "merge of the fast step's chunk states (separate kernel)"}
+
     slow_us = us("slow_partial") + us("slow_combine") + us("select") + us("pack")
     fast_us = us("fast_partial") + us("fast_merge")
     value = K * L / t_blend
@@ -500,7 +509,8 @@ def main():
         "kernels": kern,
         "kernel_time_share": {n: t / sum(total_time.values()) for n, t in total_time.items()},
         "cold_cache_check": cold,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d.get("GBps"), "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": dominant, "scope": scope.get(dominant), "achieved": d.get("GBps"),
+                     "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": d.get("frac"), "traffic": measured_traffic(dominant, w.name),
                      "alg_bytes_per_launch": d.get("alg_bytes"), "avg_launch_us": d["avg_us"],
                      **traffic_rate(measured_traffic(dominant, w.name), d["avg_us"])},
@@ -845,10 +855,13 @@ def cpu_baseline(w, kv, q_steps, flags, slow_frac_window):
             ts["fast"].append(time.perf_counter() - t0)
         return {k: statistics.median(v) for k, v in ts.items()}
 
+    # about ten seconds of CPU work in all (the slow step and the Selector take
+    # about 0.1 s each with all threads)
+    reps = {"many": (30, 100), "one": (8, 30)}
     t_start = time.perf_counter()
-    many = ops(3, 5)
+    many = ops(*reps["many"])
     with threadpool_limits(1):
-        one = ops(1, 3)
+        one = ops(*reps["one"])
     spent = time.perf_counter() - t_start
     f_sched = sum(flags[:w.n_steps]) / w.n_steps
 
@@ -857,10 +870,11 @@ def cpu_baseline(w, kv, q_steps, flags, slow_frac_window):
 
     return {"value": blended(many, f_sched), "unit": "decode steps/s/layer", "cores": threads,
             "kind": "oracle", "os_cpu_count": os.cpu_count(),
-            "sample": f"layer 0 of the same workload (T={T}), numpy float64: medians of 3 slow steps (dense "
-                      f"attention + mass), 3 Selector runs and 5 fast steps with {threads} BLAS threads, and of 1/1/3 "
-                      f"with one thread ({spent:.1f}s in all); value = the blended rate at the schedule's slow "
-                      f"fraction {f_sched:.4f}",
+            "sample": f"layer 0 of the same workload (T={T}), numpy float64: medians of {reps['many'][0]} slow steps "
+                      f"(dense attention + mass), {reps['many'][0]} Selector runs and {reps['many'][1]} fast steps with "
+                      f"{threads} BLAS threads, and of {reps['one'][0]}/{reps['one'][0]}/{reps['one'][1]} with one "
+                      f"thread ({spent:.1f}s in all); value = the blended rate at the schedule's slow fraction "
+                      f"{f_sched:.4f}",
             "ms_all_threads": {k: 1e3 * v for k, v in many.items()},
             "ms_one_thread": {k: 1e3 * v for k, v in one.items()},
             "steps_per_s_layer_all_threads": {"slow": 1.0 / (many["slow"] + many["select"]), "fast": 1.0 / many["fast"],

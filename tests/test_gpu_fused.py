@@ -304,3 +304,37 @@ def test_refresh_and_fast_rows_on_two_streams():
     for t, (a, b) in enumerate(zip(serial, forked)):
         for key in a:
             assert torch.equal(a[key], b[key]), (t, key)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("bf16", 64)])
+def test_chunks_with_more_kept_rows_than_the_emit_prefetch(dtype, D):
+    """top_k close to the candidate count: every 4096-candidate chunk keeps
+    far more rows above the threshold bin than the emit pass prefetches
+    (128 to 512 rows by row size), so the rest are copied after K*, beside
+    the kept threshold-bin rows.  Equal to the separate calls bit for bit
+    (positions and packed rows) and to the oracle."""
+    ctx = [20000, 13000]
+    kv, q = random_cache(2, 4 * 2, 2, 20000, D, DT[dtype], ctx, seed=611 + D, q_scale=3.0)
+    sp = S.support_params(16, 256, 9000, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    a = _separate(kv, sp, [0, 1], q, ws)
+    b = _fused(kv, sp, [0, 1], q, ws)
+    _assert_same(a, b)
+    _check_oracle(kv, sp, q, b, [0, 1])
+
+
+def test_chunks_longer_than_one_emission_pass():
+    """Over 4.19M candidates per head, so each Selector chunk spans more than
+    one 4096-candidate pass and the emit pass recomputes the chunk's keys from
+    the evidence (the path that also serves threshold bins larger than LDS).
+    The fused refresh equals the separate calls bit for bit and the oracle's
+    selection; the packed rows are the cache rows at the selected
+    positions."""
+    T = 4_300_000
+    kv, q = random_cache(1, 4, 1, T, 64, torch.bfloat16, [T], seed=613, q_scale=3.0)
+    sp = S.support_params(16, 256, 3000, 0.1)
+    ws = S.alloc_workspace(kv, sp)
+    a = _separate(kv, sp, [0], q, ws)
+    b = _fused(kv, sp, [0], q, ws)
+    _assert_same(a, b)
+    _check_oracle(kv, sp, q, b, [0])

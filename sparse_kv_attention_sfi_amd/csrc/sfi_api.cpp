@@ -816,6 +816,8 @@ static int32_t slow_step_select_impl(const sfi_kv_desc* desc, const sfi_support_
       sa.packed_k = packed_k;
       sa.packed_v = packed_v;
       sa.row_bytes = desc->head_dim * elem_bytes(desc->kv_dtype);
+      sa.rows32 = static_cast<uint64_t>(desc->kv_capacity) * sa.row_bytes <= kOutOfRange - 15 &&
+                  static_cast<uint64_t>(sp->top_k) * sa.row_bytes <= kOutOfRange - 15;
     }
     r = ext ? run_scored_select(desc, sp, ids, cnt, mass, E, w, knorm, sa, sel_s) : run_select(sa, cnt, sel_s);
     if (r != SFI_OK) return r;

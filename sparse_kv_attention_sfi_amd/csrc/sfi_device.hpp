@@ -91,6 +91,29 @@ __device__ __forceinline__ float2 ld8_dev(const float* base, int32_t bytes, int3
   const i2 d = __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(base, bytes), off, 0, kCpolDevice);
   return make_float2(__int_as_float(d.x), __int_as_float(d.y));
 }
+// Range-checked 16-byte accesses through a wave-uniform buffer descriptor: a
+// load at an offset past the buffer returns zeros without touching memory and
+// a store there is dropped, so work lists that fill a wave only partly need no
+// branches (and the compiler keeps exact counts of the accesses in flight).
+// `bytes` is the buffer's size, below the out-of-range offset (0xFFFFFFFF)
+// by at least 16.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_u(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int32_t>(bytes), 0x00020000);
+}
+// streaming (non-temporal, cache policy nt) load
+__device__ __forceinline__ uint4 buf_ld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4 d = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int32_t>(off), 0, 2);
+  return make_uint4(static_cast<uint32_t>(d.x), static_cast<uint32_t>(d.y), static_cast<uint32_t>(d.z),
+                    static_cast<uint32_t>(d.w));
+}
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  typedef int i4 __attribute__((ext_vector_type(4)));
+  const i4 d = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, static_cast<int32_t>(off), 0, 0);
+}
+
 // s_waitcnt vmcnt(0): this wave's earlier vector memory accesses, stores
 // included, have completed (expcnt and lgkmcnt fields left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -32,6 +32,7 @@ constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a mer
 constexpr int kSlowTargetWgs = 1024;  // slow partial workgroups aimed at per launch
 constexpr int kLogitBufRows = 1024;   // slow partial: a split's logits are buffered in LDS up to this size
 constexpr int kTicketStride = 32;     // fast-step chunk counters, one per 128-byte line
+constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;  // a buffer offset past every buffer: loads give 0, stores drop
 
 // One launch's rows.  A row's fields sit together in one 16-byte record, so
 // a workgroup fetches them with one scalar load.
@@ -140,6 +141,7 @@ struct SelectArgs {
   void* packed_k;        // [B][Hkv][top_k][D] or nullptr
   void* packed_v;
   int32_t row_bytes;
+  bool rows32;           // a KV head's cache rows and packed slots fit 32-bit byte offsets
   SeqTable tab;          // nsplit = chunks per KV head
 };
 

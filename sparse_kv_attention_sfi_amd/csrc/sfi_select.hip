@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   const uint64_t pmask = static_cast<uint64_t>(kSelBins - 1) << (64 - kSelDigitBits);
   if (h.c == 0 && tid == 0) a.sel_cnt[h.bg] = K;
 
-  if (a.chunk <= kStep && cnt_d1 <= kSelListCap) {
+  if (a.chunk <= kStep && cnt_d1 <= kSelListCap && (!PACK || a.rows32)) {
     const int len = i1 - i0, nw = (len + 31) >> 5;
     s_list[tid] = first;
     for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
@@ -590,23 +590,29 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     if (tid < kWords) s_bits[tid] = 0u;
     if (tid == 0) s_nlate = 0;
     __syncthreads();
-    // rows above the bin: loads issued now, stored once their slots are known
-    const int np = a.row_bytes >> 4;  // 8, 16 or 32 pieces per row
+    // rows above the bin: loads issued now, stored once their slots are known.
+    // Row accesses go through range-checked buffer descriptors of the head's
+    // cache rows and packed slots: an item past the list gets an offset past
+    // the buffer, so the loops have no branches.
+    const int np = PACK ? a.row_bytes >> 4 : 1;  // 8, 16 or 32 pieces per row
     const int lg = __builtin_ctz(np);
+    const uint32_t rb = static_cast<uint32_t>(a.row_bytes);
     const int n_pre = PACK ? min(n_ab, (kPreU * kSelThreads) >> lg) : 0;
-    const char* Kc = static_cast<const char*>(a.k) + h.bg * a.t_cap * a.row_bytes;
-    const char* Vc = static_cast<const char*>(a.v) + h.bg * a.t_cap * a.row_bytes;
+    const uint32_t cache_bytes = static_cast<uint32_t>(a.t_cap) * rb;
+    const __amdgpu_buffer_rsrc_t rk =
+        buf_rsrc_u(static_cast<const char*>(a.k) + h.bg * a.t_cap * a.row_bytes, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        buf_rsrc_u(static_cast<const char*>(a.v) + h.bg * a.t_cap * a.row_bytes, cache_bytes);
     uint4 pk[PACK ? kPreU : 1], pv[PACK ? kPreU : 1];
     if (PACK) {
 #pragma unroll
       for (int u = 0; u < kPreU; ++u) {
         const int it = tid + kSelThreads * u;
         const int r = it >> lg, pc = it & (np - 1);
-        if (r < n_pre) {
-          const int64_t off = static_cast<int64_t>(a.n_sink + s_pos[r]) * a.row_bytes + 16 * pc;
-          pk[u] = ld16_stream(Kc + off);
-          pv[u] = ld16_stream(Vc + off);
-        }
+        const uint32_t off =
+            r < n_pre ? static_cast<uint32_t>(a.n_sink + s_pos[min(r, kStep - 1)]) * rb + 16 * pc : kOutOfRange;
+        pk[u] = buf_ld16_stream(rk, off);
+        pv[u] = buf_ld16_stream(rv, off);
       }
     }
     const uint64_t kstar =
@@ -643,54 +649,51 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
         if (k < K) out[k] = lo + 32 * tid + (__ffs(bits) - 1);
     }
     if (PACK) {
-      // slot of kept candidate p of the chunk
+      // slot of kept candidate p of the chunk (p is clamped into the chunk, so
+      // the lookups of items past a list stay inside the bitmap)
       auto slot_of = [&](int p) {
+        p = min(max(p, 0), len - 1);
         return base + s_wpre[p >> 5] + __popc(s_bits[p >> 5] & ((1u << (p & 31)) - 1u));
       };
-      char* PK = static_cast<char*>(a.packed_k) + h.bg * K * a.row_bytes;
-      char* PV = static_cast<char*>(a.packed_v) + h.bg * K * a.row_bytes;
+      const uint32_t packed_bytes = static_cast<uint32_t>(K) * rb;
+      const __amdgpu_buffer_rsrc_t rpk =
+          buf_rsrc_u(static_cast<char*>(a.packed_k) + h.bg * K * a.row_bytes, packed_bytes);
+      const __amdgpu_buffer_rsrc_t rpv =
+          buf_rsrc_u(static_cast<char*>(a.packed_v) + h.bg * K * a.row_bytes, packed_bytes);
+      // slot -> byte offset in the packed buffers (out of range past K)
+      auto slot_off = [&](int slot, int pc) -> uint32_t {
+        return slot < K ? static_cast<uint32_t>(slot) * rb + 16 * pc : kOutOfRange;
+      };
 #pragma unroll
       for (int u = 0; u < kPreU; ++u) {
         const int it = tid + kSelThreads * u;
         const int r = it >> lg, pc = it & (np - 1);
-        if (r < n_pre) {
-          const int slot = slot_of(s_pos[r] - i0);
-          if (slot < K) {
-            const int64_t off = static_cast<int64_t>(slot) * a.row_bytes + 16 * pc;
-            *reinterpret_cast<uint4*>(PK + off) = pk[u];
-            *reinterpret_cast<uint4*>(PV + off) = pv[u];
-          }
-        }
+        const uint32_t off = r < n_pre ? slot_off(slot_of(s_pos[min(r, kStep - 1)] - i0), pc) : kOutOfRange;
+        buf_st16(rpk, off, pk[u]);
+        buf_st16(rpv, off, pv[u]);
       }
       // the kept rows of the threshold bin and the rows above it past the
       // prefetch: copied now
       const int items = s_nlate * np;
       constexpr int kU = 4;
-      for (int j0 = tid; j0 < items; j0 += kU * kSelThreads) {
+      for (int j0 = 0; j0 < items; j0 += kU * kSelThreads) {
         uint4 kv[kU], vv[kU];
-        int slot[kU];
+        uint32_t dst[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-          const int it = j0 + u * kSelThreads;
-          slot[u] = K;
-          if (it < items) {
-            const int r = it >> lg, pc = it & (np - 1);
-            const int p = s_late[r];
-            slot[u] = slot_of(p);
-            const int64_t off = static_cast<int64_t>(lo + p) * a.row_bytes + 16 * pc;
-            kv[u] = ld16_stream(Kc + off);
-            vv[u] = ld16_stream(Vc + off);
-          }
+          const int it = j0 + tid + u * kSelThreads;
+          const int r = min(it >> lg, kStep - 1), pc = it & (np - 1);
+          const int p = s_late[r];
+          const bool in = it < items;
+          dst[u] = in ? slot_off(slot_of(p), pc) : kOutOfRange;
+          const uint32_t src = in ? static_cast<uint32_t>(lo + p) * rb + 16 * pc : kOutOfRange;
+          kv[u] = buf_ld16_stream(rk, src);
+          vv[u] = buf_ld16_stream(rv, src);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-          const int it = j0 + u * kSelThreads;
-          if (it < items && slot[u] < K) {
-            const int pc = it & (np - 1);
-            const int64_t off = static_cast<int64_t>(slot[u]) * a.row_bytes + 16 * pc;
-            *reinterpret_cast<uint4*>(PK + off) = kv[u];
-            *reinterpret_cast<uint4*>(PV + off) = vv[u];
-          }
+          buf_st16(rpk, dst[u], kv[u]);
+          buf_st16(rpv, dst[u], vv[u]);
         }
       }
     }

@@ -74,8 +74,12 @@ __device__ __forceinline__ HeadCtx head_ctx(const SelectArgs& a) {
   h.e = find_entry(a.tab, wg);
   const int local = wg - a.tab.wg_begin[h.e];
   h.M = a.tab.ent[h.e].nsplit;
-  h.g = local / h.M;
-  h.c = local - h.g * h.M;
+  // consecutive workgroups take the same chunk of consecutive KV heads: with
+  // workgroups dealt round-robin to the XCDs, all chunks of one head then
+  // share an XCD (when the head count divides by the XCD count), so its
+  // histogram, lists and counts are fetched into one L2 only
+  h.g = local % a.n_kv_heads;
+  h.c = local / a.n_kv_heads;
   h.b = a.tab.ent[h.e].seq;
   h.T = row_ctx(a.tab, h.e);
   h.bg = static_cast<int64_t>(h.b) * a.n_kv_heads + h.g;

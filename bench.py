@@ -11,15 +11,16 @@ last-level cache at its next step; a timed cold-cache check (each call after
 a 1 GiB read) confirms the kernel times.
 
 A "step" is one decode step over all layers: for every layer either the slow
-path (dense split-K attention + mass + Selector + packing of the selected
-rows) or the fast path (sparse attention over the packed support), as the
-scheduler says (``--slow async`` runs each layer's Selector on a second
-stream under the next layer's slow attention, the pages' asynchronous layer
-pipeline; on this attention-only loop it is slower than one stream).
-``value`` = K * layers / wall time of K steps (decode steps per
-second per layer), with inputs resident in HBM.  Each step's queries are
-staged into fixed buffers and the step is replayed as a HIP graph (one for
-slow steps, one for fast steps).
+path (dense split-K attention + mass + Selector) or the fast path (sparse
+attention over the support), as the scheduler says; the first fast step of a
+span gathers the selected rows by index and packs them, the later ones read
+the packed rows (``--pack refresh`` packs in the refresh instead;
+``--slow async`` runs each layer's Selector on a second stream under the next
+layer's slow attention, the pages' asynchronous layer pipeline, slower than
+one stream on this attention-only loop).  ``value`` = K * layers / wall time
+of K steps (decode steps per second per layer), with inputs resident in HBM.
+Each step's queries are staged into fixed buffers and the step is replayed as
+a HIP graph (one each for slow steps, first fast steps and other fast steps).
 
 Also reported: the blended rate over the workload's whole span schedule
 (``full_schedule``, at the schedule's own slow fraction, beside
@@ -69,6 +70,8 @@ def csrc_digest():
 
 def kernel_group(name):
     """Bench kernel name of a device kernel (the Selector's kernels form one group)."""
+    if "fast_partial_kernel<" in name and name.split(">")[0].endswith("true"):
+        return "fast_pack"  # the gather step's packing variant (last template argument)
     for key, group in (("slow_partial", "slow_partial"), ("slow_combine", "slow_combine"), ("select_", "select"),
                        ("pack_kernel", "pack"), ("fast_packed", "fast_partial"), ("fast_partial", "fast_partial"),
                        ("fast_merge", "fast_merge")):
@@ -116,6 +119,9 @@ def parse():
     p.add_argument("--mode", choices=["graph", "eager"], default="graph")
     p.add_argument("--fast", choices=["packed", "gather"], default="packed",
                    help="fast step over the packed support (default) or gathering rows by index")
+    p.add_argument("--pack", choices=["deferred", "refresh"], default="deferred",
+                   help="where the selected rows are packed: by the first fast step of each span "
+                        "(sfi_fast_step_pack, default), which reads them anyway, or in the refresh's emission pass")
     p.add_argument("--slow", choices=["fused", "async", "separate"], default="fused",
                    help="slow step + Selector (+ pack): fused on one stream (default), fused with the Selector on a "
                         "second stream under the next layer's slow step, or as separate calls")
@@ -127,6 +133,8 @@ def parse():
                    help="independent layer caches cycled per step for single-layer batched workloads (C4)")
     p.add_argument("--batch-check", type=int, default=16, metavar="B",
                    help="also time the fast step for B sequences in one launch (0: skip)")
+    p.add_argument("--graph-reps", type=int, default=16,
+                   help="replays of each step kind's graph timed alone (per-layer cost of each kind; 0: skip)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-full-schedule", action="store_true",
                    help="skip the replay of the whole span schedule (its blended rate is then null)")
@@ -252,6 +260,10 @@ def main():
     sel = torch.empty(L, 1, w.n_kv_heads, w.top_k, dtype=torch.int32, device=dev)
     cnt = torch.empty(L, 1, w.n_kv_heads, dtype=torch.int32, device=dev)
     packed = args.fast == "packed"
+    # deferred packing: the refresh only selects; the first fast step of the
+    # span gathers the selected rows and packs them for the packed steps after it
+    deferred = packed and args.pack == "deferred"
+    refresh_pk = packed and not deferred
     if packed:
         pk = torch.empty(L, 1, w.n_kv_heads, w.top_k, w.head_dim, dtype=q_steps.dtype, device=dev)
         pv = torch.empty_like(pk)
@@ -268,7 +280,7 @@ def main():
 
     def slow_layer(l):
         S.sfi_slow_step_select(kvs[l], sp, [0], q_buf[l], out_buf[l], mass, sel[l], cnt[l],
-                               pk[l] if packed else None, pv[l] if packed else None, ws)
+                               pk[l] if refresh_pk else None, pv[l] if refresh_pk else None, ws)
 
     def fast_layer(l):
         if packed:
@@ -283,7 +295,8 @@ def main():
                 if l >= depth:
                     main.wait_event(sel_done[l - depth])
                 S.sfi_slow_step_select_async(kvs[l], sp, [0], q_buf[l], out_buf[l], massd[l % depth], sel[l], cnt[l],
-                                             pk[l] if packed else None, pv[l] if packed else None, wsd[l % depth],
+                                             pk[l] if refresh_pk else None, pv[l] if refresh_pk else None,
+                                             wsd[l % depth],
                                              main, side)
                 sel_done[l].record(side)
             main.wait_stream(side)
@@ -294,12 +307,26 @@ def main():
                 continue
             S.sfi_slow_step(kvs[l], [0], q_buf[l], out_buf[l], mass, ws)
             S.sfi_select(kvs[l], sp, [0], mass, sel[l], cnt[l], ws)
-            if packed:
+            if refresh_pk:
                 S.sfi_pack_support(kvs[l], sp, [0], sel[l], cnt[l], pk[l], pv[l])
 
     def fast_layers():
         for l in range(L):
             fast_layer(l)
+
+    def first_layer(l):
+        S.sfi_fast_step_pack(kvs[l], sp, [0], q_buf[l], sel[l], cnt[l], out_buf[l], pk[l], pv[l], ws)
+
+    def first_layers():
+        for l in range(L):
+            first_layer(l)
+
+    def kind_of(t):
+        """slow (refresh), first (the span's first fast step: packs when
+        deferred) or fast."""
+        if flags[t]:
+            return "slow"
+        return "first" if deferred and (t == 0 or flags[t - 1]) else "fast"
 
     def dense_layers():
         for l in range(L):
@@ -308,6 +335,8 @@ def main():
     # eager warm-up (also primes the selection used by the first fast step)
     q_buf.copy_(q_steps[0])
     slow_layers()
+    if deferred:
+        first_layers()
     fast_layers()
     dense_layers()
     torch.cuda.synchronize()
@@ -315,18 +344,21 @@ def main():
     graphs = None
     if args.mode == "graph":
         graphs = {}
-        for name, fn in (("slow", slow_layers), ("fast", fast_layers), ("dense", dense_layers)):
+        for name, fn in (("slow", slow_layers), ("first", first_layers), ("fast", fast_layers),
+                         ("dense", dense_layers)):
+            if name == "first" and not deferred:
+                continue
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fn()
             graphs[name] = g
-        run = {"slow": graphs["slow"].replay, "fast": graphs["fast"].replay, "dense": graphs["dense"].replay}
+        run = {name: g.replay for name, g in graphs.items()}
     else:
-        run = {"slow": slow_layers, "fast": fast_layers, "dense": dense_layers}
+        run = {"slow": slow_layers, "first": first_layers, "fast": fast_layers, "dense": dense_layers}
 
     def step(t, kind=None):
         q_buf.copy_(q_steps[t])
-        run[kind or ("slow" if flags[t] else "fast")]()
+        run[kind or kind_of(t)]()
 
     for t in range(W):
         step(t)
@@ -337,6 +369,7 @@ def main():
     torch.cuda.synchronize()
     t_blend = time.perf_counter() - t_start
     n_slow_timed = sum(flags[W:W + K])
+    n_first_timed = sum(kind_of(t) == "first" for t in range(W, W + K))
     log(f"blended: {K} steps ({n_slow_timed} slow) x {L} layers in {t_blend * 1e3:.1f} ms")
 
     # The whole span schedule of the workload (its w.n_steps steps), replayed
@@ -349,12 +382,30 @@ def main():
         t_start = time.perf_counter()
         for t in range(w.n_steps):
             q_buf.copy_(q_steps[t])
-            run["slow" if full_flags[t] else "fast"]()
+            run[kind_of(t)]()
         torch.cuda.synchronize()
         t_full = time.perf_counter() - t_start
         full_schedule = {"steps": w.n_steps, "slow_steps": sum(full_flags),
                          "slow_fraction": sum(full_flags) / w.n_steps,
                          "blended_steps_per_s_layer": w.n_steps * L / t_full}
+
+    # Each kind of step alone, as the decode loop runs it (its graph replayed
+    # back to back, one query): the per-layer cost of a refresh, of the span's
+    # first fast step and of the other fast steps, kernel gaps included.
+    graph_us = None
+    if graphs is not None and args.graph_reps:
+        graph_us = {}
+        q_buf.copy_(q_steps[0])
+        for name in ("slow", "first", "fast", "dense"):
+            if name not in graphs:
+                continue
+            graphs[name].replay()
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for _ in range(args.graph_reps):
+                graphs[name].replay()
+            torch.cuda.synchronize()
+            graph_us[name] = (time.perf_counter() - t_start) * 1e6 / (args.graph_reps * L)
 
     # dense-every-step baseline (same queries)
     kd = min(args.dense_steps, n_steps)
@@ -373,7 +424,7 @@ def main():
     ke = min(args.eager_steps, n_steps)
     for t in range(ke):
         q_buf.copy_(q_steps[t])
-        (slow_layers if flags[t] else fast_layers)()
+        {"slow": slow_layers, "first": first_layers, "fast": fast_layers}[kind_of(t)]()
     torch.cuda.synchronize()
     S.sfi_profile_enable(False)
     kern = {}
@@ -410,7 +461,7 @@ def main():
         S.sfi_profile_reset()
         for i in range(args.cold_checks):
             l = i % L
-            for fn in (lambda: slow_layer(l), lambda: fast_layer(l)):
+            for fn in (lambda: slow_layer(l), lambda: fast_layer(l)) + ((lambda: first_layer(l),) if deferred else ()):
                 # the timed call follows the flush in stream order, with the GPU busy
                 # in between (after an idle wait a short kernel also pays to wake up)
                 torch.sum(flush, dim=0, out=sink)
@@ -442,9 +493,12 @@ def main():
         "slow_combine": 4 * w.n_q_heads * T + 4 * w.n_q_heads * nsplit * (w.head_dim + 2)
                         + 4 * w.n_kv_heads * T + 4 * w.n_q_heads * w.head_dim,
         "select": 4 * w.n_kv_heads * n_cand + 4 * w.n_kv_heads * w.top_k
-                  + (2 * 2 * w.n_kv_heads * kk * kv_row if fused and packed else 0),
+                  + (2 * 2 * w.n_kv_heads * kk * kv_row if fused and refresh_pk else 0),
         "pack": 2 * 2 * w.n_kv_heads * kk * kv_row + 4 * w.n_kv_heads * w.top_k,
         "fast_partial": 2 * w.n_kv_heads * supp * kv_row + q_bytes + (0 if packed else 4 * w.n_kv_heads * w.top_k),
+        # the gather step reads the indices and the rows, and writes the selected rows again
+        "fast_pack": 2 * w.n_kv_heads * supp * kv_row + q_bytes + 4 * w.n_kv_heads * w.top_k
+                     + 2 * w.n_kv_heads * kk * kv_row,
         # the merge reads every chunk's (max, sum) and output partial
         "fast_merge": 4 * w.n_q_heads * nchunk * (w.head_dim + 2) + 4 * w.n_q_heads * w.head_dim,
     }
@@ -456,7 +510,8 @@ def main():
     # GPU time of each kernel over the timed steps = launches there x average
     n_fast_timed = K - n_slow_timed
     per_step = {"slow_partial": n_slow_timed, "slow_combine": n_slow_timed, "select": n_slow_timed,
-                "pack": n_slow_timed if packed else 0, "fast_partial": n_fast_timed, "fast_merge": n_fast_timed}
+                "pack": n_slow_timed if refresh_pk else 0, "fast_partial": n_fast_timed - n_first_timed,
+                "fast_pack": n_first_timed, "fast_merge": n_fast_timed}
     total_time = {n: kern[n]["avg_us"] * per_step[n] * L for n in kern if n in per_step}
     dominant = max(total_time, key=total_time.get)
 
@@ -466,7 +521,9 @@ def main():
     # what one launch of each kernel group does on this workload
     scope = {"slow_partial": "split-K dense attention over the whole context, writing the logits for the mass",
              "slow_combine": "merge of the split partials, the mass and the Selector's first histogram",
-             "select": "Selector: threshold-bin gather and emission of the kept positions with their packed rows",
+             "select": ("Selector: threshold-bin gather and emission of the kept positions"
+                        + (" with their packed rows" if refresh_pk and fused else "")),
+             "fast_pack": "the span's first fast step over the gathered support, packing the selected rows it reads",
              "fast_partial": ("the whole fast step: sparse attention over the support in chunks, and, when the "
                               "launch fits the CUs, the merge of the chunk states in the same kernel"
                               if "fast_merge" not in kern else "sparse attention over the support in chunks"),
@@ -474,6 +531,7 @@ def main():
 
     slow_us = us("slow_partial") + us("slow_combine") + us("select") + us("pack")
     fast_us = us("fast_partial") + us("fast_merge")
+    first_us = us("fast_pack") + us("fast_merge") if deferred else None
     value = K * L / t_blend
     dense_rate = kd * L / t_dense if kd else None
     d = kern[dominant]
@@ -495,17 +553,19 @@ def main():
                                f"top-k {w.top_k}, lambda {w.lam}, geometric spans mean {w.span_param}; "
                                f"{L} independent layer caches per decode step",
                    "layers": L, "ctx": w.ctx, "batch": 1, "mode": args.mode, "fast_path": args.fast,
-                   "slow_path": args.slow,
+                   "slow_path": args.slow, "packing": args.pack if packed else None,
                    "slow_steps_timed": n_slow_timed},
         "slow_fraction_timed": n_slow_timed / K,
         "full_schedule": full_schedule,
         "slow_step_us": slow_us or None,
         "fast_step_us": fast_us or None,
+        "first_fast_step_us": first_us or None,
         "slow_steps_per_s_layer": 1e6 / slow_us if slow_us else None,
         "fast_steps_per_s_layer": 1e6 / fast_us if fast_us else None,
         "blended_steps_per_s_layer": value,
         "dense_steps_per_s_layer": dense_rate,
         "speedup_vs_dense": value / dense_rate if dense_rate else None,
+        "graph_step_us": graph_us,
         "kernels": kern,
         "kernel_time_share": {n: t / sum(total_time.values()) for n, t in total_time.items()},
         "cold_cache_check": cold,
@@ -541,7 +601,7 @@ def main():
         del kvs, q_steps, graphs, run
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        result["configs"] = config_block(dev, result)
+        result["configs"] = config_block(dev, result, args.pack)
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -552,16 +612,20 @@ def main():
     print(json.dumps(result))
 
 
-def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=None):
+def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=None, pack="deferred"):
     """Decode-loop throughput of workload ``w`` over ``layers`` layer caches
     (the workload's own layers, or independent caches cycled so that no
     layer's data is still cached at its next step), over the whole span
     schedule (``n_steps`` steps, the workload's count by default).
 
     Each decode step runs, for every layer: the KV append (growing-history
-    workloads), the fused refresh for the rows that open a span, and the
-    packed fast step for the others.  Every distinct slow/fast row pattern
-    of the schedule is captured once as a HIP graph and replayed; with
+    workloads), the fused refresh for the rows that open a span, and one fast
+    launch for the others.  With ``pack="deferred"`` the refresh only
+    selects, and in the fast launch (sfi_fast_step_pack with per-row flags)
+    the rows on their span's first fast step gather and pack their support
+    while the others read their packed rows; with ``pack="refresh"`` the
+    refresh packs and the fast launch reads packed rows only.  Every distinct
+    row pattern of the schedule is captured once as a HIP graph and replayed; with
     appends the context lengths live in device memory (advanced by the
     append kernel), so a captured step stays valid as the history grows.
     The dense baseline replays a graph of the same loop with every row
@@ -580,6 +644,14 @@ def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=N
     plan = [tuple(tuple(x) for x in sched.step()) for _ in range(n_steps)]
     sched.close()
     flags = [[b in slow for slow, _ in plan] for b in range(B)]
+    deferred = pack == "deferred"
+    if deferred:
+        # (slow rows, rows on their span's first fast step, other fast rows)
+        plan = [(slow, tuple(b for b in fast if t > 0 and b in plan[t - 1][0]),
+                 tuple(b for b in fast if not (t > 0 and b in plan[t - 1][0])))
+                for t, (slow, fast) in enumerate(plan)]
+    else:
+        plan = [(slow, (), fast) for slow, fast in plan]
     span_ids = [gen.span_ids_from_flags(f) for f in flags]
     t0 = time.time()
     kvs, ctx_devs = [], []
@@ -619,7 +691,7 @@ def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=N
         kn_buf, vn_buf = torch.empty_like(kn_all[0]), torch.empty_like(vn_all[0])
     all_rows = list(range(B))
 
-    def step_calls(slow, fast, dense=False):
+    def step_calls(slow, first, fast, dense=False):
         for l in range(L):
             if w.append:
                 S.sfi_kv_append(kvs[l], all_rows, kn_buf[l], vn_buf[l])
@@ -627,9 +699,15 @@ def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=N
                 S.sfi_slow_step(kvs[l], all_rows, q_buf[l], out[l], None, ws)
                 continue
             if slow:
-                S.sfi_slow_step_select(kvs[l], sp, list(slow), q_buf[l], out[l], mass, sel[l], cnt[l], pk[l], pv[l],
-                                       ws)
-            if fast:
+                S.sfi_slow_step_select(kvs[l], sp, list(slow), q_buf[l], out[l], mass, sel[l], cnt[l],
+                                       None if deferred else pk[l], None if deferred else pv[l], ws)
+            if first:
+                # one launch for every fast row: the rows on their span's first
+                # fast step gather and pack, the others read their packed rows
+                rows = sorted(first + fast)
+                S.sfi_fast_step_pack(kvs[l], sp, rows, q_buf[l], sel[l], cnt[l], out[l], pk[l], pv[l], ws,
+                                     pack_flags=[int(b in first) for b in rows])
+            elif fast:
                 S.sfi_fast_step_packed(kvs[l], sp, list(fast), q_buf[l], pk[l], pv[l], cnt[l], out[l], ws)
 
     def stage(t):
@@ -647,7 +725,7 @@ def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=N
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             if key == ("dense",):
-                step_calls((), (), dense=True)
+                step_calls((), (), (), dense=True)
             else:
                 step_calls(*key)
         graphs[key] = g
@@ -686,6 +764,7 @@ def measure_loop(w, dev, layers, dense_steps, warmup=8, n_steps=None, log_name=N
            "sfi_steps_per_s_layer": value, "sfi_tokens_per_s_layer": value * B,
            "dense_steps_per_s_layer": dense_rate, "dense_steps_timed": kd,
            "speedup_vs_dense": value / dense_rate, "slow_row_fraction": slow_rows / (n_steps * B),
+           "packing": pack,
            "graphs": len(graphs), "mode": "graph replay per slow/fast row pattern"
                                           + (", device context lengths" if w.append else "")}
     del kvs, q_all, graphs
@@ -701,7 +780,7 @@ def run_batched(args, w, dev):
     whole span schedule (or --steps steps) replayed from captured graphs."""
     L = w.n_layers if w.n_layers > 1 else max(1, args.batched_caches)
     r = measure_loop(w, dev, L, args.dense_steps or 64, warmup=args.warmup,
-                     n_steps=args.steps if args.steps < w.n_steps else w.n_steps)
+                     n_steps=args.steps if args.steps < w.n_steps else w.n_steps, pack=args.pack)
     result = {
         "metric": METRIC, "value": r["sfi_steps_per_s_layer"], "unit": "decode steps/s/layer", "n_gpus": 1,
         "steps": r["steps"], "warmup": args.warmup, "ms_per_step": 1e3 * r["layers"] / r["sfi_steps_per_s_layer"],
@@ -797,7 +876,7 @@ def fast_batch_check(w, sp, batch, dev, ctx=32768, calls=20):
     return res
 
 
-def config_block(dev, headline):
+def config_block(dev, headline, pack="deferred"):
     """SFI against dense decode on every workload beside the headline: the
     32K layer (128 independent layer caches), the batch of 16 mixed contexts
     (8 cycled caches) and the 32-layer growing-history loop, each over its
@@ -812,7 +891,7 @@ def config_block(dev, headline):
                      "speedup_vs_dense": hs["blended_steps_per_s_layer"] / headline["dense_steps_per_s_layer"],
                      "slow_row_fraction": hs["slow_fraction"]}
     for name, w, layers in (("C2", synth.C2, 128), ("C4", synth.C4, 8), ("C5", synth.C5, synth.C5.n_layers)):
-        out[name] = measure_loop(w, dev, layers, dense_steps=64, warmup=8)
+        out[name] = measure_loop(w, dev, layers, dense_steps=64, warmup=8, pack=pack)
         log(f"{name}: SFI {out[name]['sfi_steps_per_s_layer']:.0f} decode steps/s/layer, "
             f"dense {out[name]['dense_steps_per_s_layer']:.0f}, speedup {out[name]['speedup_vs_dense']:.2f}")
     return out

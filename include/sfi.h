@@ -244,6 +244,30 @@ int32_t sfi_pack_support(const sfi_kv_desc* desc, const sfi_support_params* sp,
                          const int32_t* seq_ids_host, int32_t n_seq, const int32_t* sel_idx,
                          const int32_t* sel_cnt, void* packed_k, void* packed_v, void* stream);
 
+/* sfi_fast_step that also packs: besides the output it writes the selected
+ * rows it reads, K[b][g][sel_idx[b][g][i]] and V[...] for i below the count
+ * the fast step uses (min(sel_cnt, the current candidate count)), into
+ * packed_k[b][g][i] and packed_v[b][g][i] (device [B][Hkv][top_k][D],
+ * kv_dtype; indices outside the context are skipped, as sfi_pack_support skips
+ * them).  The output is sfi_fast_step's, bit for bit, and the packed rows are
+ * sfi_pack_support's: the first fast step of a span can pack the support for
+ * the sfi_fast_step_packed calls that follow, instead of the refresh packing
+ * it (the memory-coalesced layout of "Slow-Fast Inference ...", gist.science
+ * technical summary, 3 "Systemdesign und Kernel-Optimierung", made on the
+ * first read of the selected rows).
+ *   pack_flags : host, n_seq entries, or NULL (every row packs).  Row
+ *                seq_ids[i] packs when pack_flags[i] != 0; a row whose flag is
+ *                0 is computed as by sfi_fast_step_packed from the packed rows
+ *                an earlier call wrote (its buffers are only read), so one
+ *                launch serves a batch whose rows are at different points of
+ *                their spans.
+ * Other arguments and the workspace as for sfi_fast_step; packed_k /
+ * packed_v may be NULL only when top_k = 0. */
+int32_t sfi_fast_step_pack(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids_host,
+                           int32_t n_seq, const int32_t* pack_flags, const void* q, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, float* out, void* packed_k, void* packed_v, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* Fast step over a packed support: the same result as sfi_fast_step with the
  * sel_idx that filled packed_k / packed_v, provided every index below sel_cnt
  * lay inside the context when it was packed (always so for the Selector's
@@ -376,7 +400,8 @@ typedef enum {
   SFI_K_PACK = 5,         /* packing of the selected rows */
   SFI_K_FAST_MERGE = 6,   /* merge of the fast step's chunk states, for launches with more
                              workgroups than the GPU has compute units */
-  SFI_K_COUNT = 7
+  SFI_K_FAST_PACK = 7,    /* a fast-step launch of sfi_fast_step_pack in which some row packs */
+  SFI_K_COUNT = 8
 } sfi_kernel_id;
 int32_t sfi_profile_enable(int32_t on);
 int32_t sfi_profile_reset(void);

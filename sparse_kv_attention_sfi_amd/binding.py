@@ -21,10 +21,11 @@ SFI_ERR_NO_MEMORY = -6
 SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_SLOW, SFI_OP_SELECT, SFI_OP_FAST, SFI_OP_SLOW_SELECT = 0, 1, 2, 3
 SFI_SPAN_FIXED, SFI_SPAN_GEOMETRIC = 0, 1
-SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK, SFI_K_FAST_MERGE = range(7)
+(SFI_K_SLOW_PARTIAL, SFI_K_SLOW_COMBINE, SFI_K_SELECT, SFI_K_FAST, SFI_K_APPEND, SFI_K_PACK, SFI_K_FAST_MERGE,
+ SFI_K_FAST_PACK) = range(8)
 KERNEL_NAMES = {SFI_K_SLOW_PARTIAL: "slow_partial", SFI_K_SLOW_COMBINE: "slow_combine",
                 SFI_K_SELECT: "select", SFI_K_FAST: "fast_partial", SFI_K_APPEND: "append",
-                SFI_K_PACK: "pack", SFI_K_FAST_MERGE: "fast_merge"}
+                SFI_K_PACK: "pack", SFI_K_FAST_MERGE: "fast_merge", SFI_K_FAST_PACK: "fast_pack"}
 
 
 class SFIError(RuntimeError):
@@ -68,6 +69,7 @@ def lib():
             "sfi_slow_step": (I32, [D, P(I32), I32, VP, VP, VP, VP, SZ, VP]),
             "sfi_select": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, SZ, VP]),
             "sfi_fast_step": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, SZ, VP]),
+            "sfi_fast_step_pack": (I32, [D, S, P(I32), I32, P(I32), VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "sfi_kv_append": (I32, [D, P(I32), I32, VP, VP, VP]),
             "sfi_pack_support": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP]),
             "sfi_fast_step_packed": (I32, [D, S, P(I32), I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
@@ -308,6 +310,32 @@ def sfi_fast_step(kv: KVDesc, sp, seq_ids, q, sel_idx, sel_cnt, out, ws, stream=
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sfi_fast_step(C.byref(kv.desc), C.byref(sp), ids, n, _ptr(q), _ptr(sel_idx), _ptr(sel_cnt),
                                _ptr(out), _ptr(ws), nbytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_fast_step_pack(kv: KVDesc, sp, seq_ids, q, sel_idx, sel_cnt, out, packed_k, packed_v, ws, stream=None,
+                       pack_flags=None):
+    """pack_flags: one flag per listed row (None: every row packs); a row
+    whose flag is 0 reads the packed rows an earlier call wrote."""
+    import torch
+    B, Hq, Hkv, D = kv.batch, kv.n_q_heads, kv.n_kv_heads, kv.head_dim
+    _need(q, kv.dtype, (B, Hq, D), "q")
+    _need(out, torch.float32, (B, Hq, D), "out")
+    _need(sel_idx, torch.int32, (B, Hkv, sp.top_k), "sel_idx")
+    _need(sel_cnt, torch.int32, (B, Hkv), "sel_cnt")
+    _need(packed_k, kv.dtype, (B, Hkv, sp.top_k, D), "packed_k")
+    _need(packed_v, kv.dtype, (B, Hkv, sp.top_k, D), "packed_v")
+    _, ids, n = _ids(seq_ids)
+    flags = None
+    if pack_flags is not None:
+        flags = np.ascontiguousarray(np.asarray(pack_flags, dtype=np.int32))
+        if flags.shape != (n,):
+            raise ValueError(f"pack_flags must hold one flag per listed row ({n}), got shape {flags.shape}")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sfi_fast_step_pack(C.byref(kv.desc), C.byref(sp), ids, n,
+                                    None if flags is None else flags.ctypes.data_as(C.POINTER(C.c_int32)), _ptr(q),
+                                    _ptr(sel_idx), _ptr(sel_cnt), _ptr(out), _ptr(packed_k), _ptr(packed_v), _ptr(ws),
+                                    nbytes, _stream(stream)),
+           "sfi_fast_step_pack")
 
 
 def sfi_pack_support(kv: KVDesc, sp, seq_ids, sel_idx, sel_cnt, packed_k, packed_v, stream=None):

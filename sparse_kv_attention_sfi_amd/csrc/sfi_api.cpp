@@ -881,7 +881,8 @@ static int32_t check_fast(const sfi_kv_desc* desc, const sfi_support_params* sp,
 static int32_t launch_fast_group(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* ids,
                                  int32_t cnt, const void* q, const int32_t* sel_idx, const void* packed_k,
                                  const void* packed_v, const int32_t* sel_cnt, float* out, float* part_ml,
-                                 float* part_o, int32_t* ticket, hipStream_t s, bool timing) {
+                                 float* part_o, int32_t* ticket, hipStream_t s, bool timing,
+                                 void* pack_out_k = nullptr, void* pack_out_v = nullptr, uint64_t pack_mask = ~0ull) {
   const int G = desc->n_q_heads / desc->n_kv_heads;
   const int crow = fast_chunk_rows();
   FastArgs a{};
@@ -892,6 +893,23 @@ static int32_t launch_fast_group(const sfi_kv_desc* desc, const sfi_support_para
   a.q = q;
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
+  a.pack_out_k = pack_out_k;
+  a.pack_out_v = pack_out_v;
+  if (pack_out_k != nullptr) {
+    // rows that pack gather through sel_idx; the others read the packed
+    // buffers (written by an earlier call); both kinds: one mixed launch
+    const uint64_t all = cnt >= 64 ? ~0ull : (1ull << cnt) - 1;
+    pack_mask &= all;
+    if (pack_mask == 0) {
+      a.packed_k = pack_out_k;
+      a.packed_v = pack_out_v;
+      a.pack_out_k = a.pack_out_v = nullptr;
+    } else if (pack_mask != all) {
+      a.packed_k = pack_out_k;
+      a.packed_v = pack_out_v;
+      a.pack_mask = pack_mask;
+    }
+  }
   a.part_ml = part_ml;
   a.part_o = part_o;
   a.out = out;
@@ -923,7 +941,7 @@ static int32_t launch_fast_group(const sfi_kv_desc* desc, const sfi_support_para
   a.ticket = fused ? ticket : nullptr;
   auto partial = [&] { return launch_fast_partial(a, desc->kv_dtype, desc->head_dim, G, grid, s); };
   auto merge = [&] { return launch_fast_merge(a, desc->head_dim, G, s); };
-  hipError_t e = timing ? timed(SFI_K_FAST, s, partial) : partial();
+  hipError_t e = timing ? timed(a.pack_out_k != nullptr ? SFI_K_FAST_PACK : SFI_K_FAST, s, partial) : partial();
   if (e == hipSuccess && !fused) e = timing ? timed(SFI_K_FAST_MERGE, s, merge) : merge();
   return e == hipSuccess ? SFI_OK : hip_fail(e, "fast launch");
 }
@@ -931,7 +949,8 @@ static int32_t launch_fast_group(const sfi_kv_desc* desc, const sfi_support_para
 static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
                               int32_t n_seq, const void* q, const int32_t* sel_idx, const void* packed_k,
                               const void* packed_v, const int32_t* sel_cnt, float* out, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              void* stream, void* pack_out_k = nullptr, void* pack_out_v = nullptr,
+                              const int32_t* pack_flags = nullptr) {
   int32_t st = check_fast(desc, sp, seq_ids, n_seq, q, sel_idx, packed_k, packed_v, sel_cnt, out, false);
   if (st != SFI_OK || n_seq == 0) return st;
   const FastLayout L = fast_layout(desc, sp);
@@ -939,9 +958,17 @@ static int32_t fast_step_impl(const sfi_kv_desc* desc, const sfi_support_params*
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   return for_each_group(seq_ids, n_seq, [&](const int32_t* ids, int32_t cnt) -> int32_t {
+    static_assert(kMaxSeqPerLaunch <= 64, "one pack_mask bit per table entry");
+    uint64_t mask = ~0ull;
+    if (pack_flags != nullptr) {
+      mask = 0;
+      for (int32_t i = 0; i < cnt; ++i)
+        if (pack_flags[(ids - seq_ids) + i] != 0) mask |= 1ull << i;
+    }
     return launch_fast_group(desc, sp, ids, cnt, q, sel_idx, packed_k, packed_v, sel_cnt, out,
                              reinterpret_cast<float*>(w + L.part_ml), reinterpret_cast<float*>(w + L.part_o),
-                             reinterpret_cast<int32_t*>(w + header_layout(desc).fast_ticket), s, true);
+                             reinterpret_cast<int32_t*>(w + header_layout(desc).fast_ticket), s, true, pack_out_k,
+                             pack_out_v, mask);
   });
 }
 
@@ -950,6 +977,21 @@ int32_t sfi_fast_step(const sfi_kv_desc* desc, const sfi_support_params* sp, con
                       size_t ws_bytes, void* stream) {
   if (sel_idx == nullptr && sp != nullptr && sp->top_k > 0) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
   return fast_step_impl(desc, sp, seq_ids, n_seq, q, sel_idx, nullptr, nullptr, sel_cnt, out, ws, ws_bytes, stream);
+}
+
+int32_t sfi_fast_step_pack(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,
+                           int32_t n_seq, const int32_t* pack_flags, const void* q, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, float* out, void* packed_k, void* packed_v, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (sp != nullptr && sp->top_k > 0) {
+    if (sel_idx == nullptr) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
+    if (packed_k == nullptr || packed_v == nullptr) return fail(SFI_ERR_INVALID_ARG, "packed_k / packed_v is NULL");
+    int32_t st;
+    if ((st = check_aligned({{packed_k, "packed_k"}, {packed_v, "packed_v"}}, kVecAlign)) != SFI_OK) return st;
+  }
+  const bool pack = sp != nullptr && sp->top_k > 0;
+  return fast_step_impl(desc, sp, seq_ids, n_seq, q, sel_idx, nullptr, nullptr, sel_cnt, out, ws, ws_bytes, stream,
+                        pack ? packed_k : nullptr, pack ? packed_v : nullptr, pack_flags);
 }
 
 int32_t sfi_fast_step_packed(const sfi_kv_desc* desc, const sfi_support_params* sp, const int32_t* seq_ids,

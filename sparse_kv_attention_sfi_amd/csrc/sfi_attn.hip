@@ -1068,6 +1068,35 @@ struct FastTailSmem {
   int last;
 };
 
+// Shared memory of a fast-step workgroup (gather and packed paths alike): the
+// probabilities of each wave's rows, the per-wave output slots (VALU P.V) or
+// the V staging rows (MFMA P.V), the per-wave running max and sum, the support
+// positions of the chunk (gather path), and the tail's merge buffers.  Each
+// is its own LDS variable (one set per instantiation), so the compiler knows
+// they do not overlap.
+template <typename E, int D, int G, int TILES>
+struct FastSmem {
+  float* p;
+  float* o;
+  char* v;
+  float* m;
+  float* l;
+  int* pos;
+  FastTailSmem* tail;
+};
+template <typename E, int D, int G, int TILES>
+__device__ __forceinline__ FastSmem<E, D, G, TILES> fast_smem() {
+  constexpr int kRows = TILES * 16, kWaves = kFastThreads / 64;
+  constexpr bool kMfma = fast_pv_mfma<E, TILES>();
+  __shared__ __attribute__((aligned(16))) float p[kWaves * kRows * G];
+  __shared__ __attribute__((aligned(16))) float o[kMfma ? 4 : kWaves * Attn<E, D, G>::kRowGroups * G * D];
+  __shared__ __attribute__((aligned(16))) char v[kMfma ? kWaves * kRows * Attn<E, D, G>::kRowBytes : 16];
+  __shared__ float m[kWaves * G], l[kWaves * G];
+  __shared__ int pos[kWaves * kRows];
+  __shared__ FastTailSmem tail;
+  return {p, o, v, m, l, pos, &tail};
+}
+
 // Merge of the nchunk chunk states of the G query heads of one (sequence, KV
 // head) into the output, renormalised over the whole support.  Thread
 // (sub, h, c4) merges slots sub, sub + NSUB, ... of head h's column quad c4
@@ -1169,10 +1198,14 @@ __device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t eg, 
 //    the next workgroup could already use.
 // On the MFMA path a wave's output slot reuses its own V staging rows (its
 // reads of them are complete).
-template <typename A, int D, int G, int NW, int ROWS, bool MFMA>
+// `late` issues stores that nothing in the kernel waits for (the packing of
+// sfi_fast_step_pack): after the ticket, so that the wait for the chunk-state
+// stores does not also wait for them, and in the last workgroup after the
+// merge, whose loads would otherwise wait behind them.
+template <typename A, int D, int G, int NW, int ROWS, bool MFMA, typename Late>
 __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v, FastTailSmem& sh,
                                             int wave, int lane, int tid, const FastArgs& a, int64_t eg, int64_t qh0,
-                                            int chunk, int nchunk) {
+                                            int chunk, int nchunk, Late&& late) {
   constexpr int kWaveBytes = ROWS * A::kRowBytes;
   if constexpr (MFMA) {
     wave_sync();
@@ -1191,6 +1224,7 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
                                       *reinterpret_cast<float4*>(a.out + (qh0 + h) * D + d) =
                                           make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
                                     });
+    late();
     return;
   }
   // one buffer descriptor per workgroup (its G heads' rows)
@@ -1204,6 +1238,7 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
                                         *reinterpret_cast<float2*>(mlg + (h * a.part_stride + chunk) * 2) =
                                             make_float2(M, L);
                                     });
+    late();
     return;
   }
   const int ml_bytes = G * a.part_stride * 8, o_bytes = G * a.part_stride * D * 4;
@@ -1217,13 +1252,20 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
   int32_t* ticket = a.ticket + eg * kTicketStride;
   if (tid == 0) sh.last = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nchunk - 1;
   __syncthreads();
-  if (!sh.last) return;
+  if (!sh.last) {
+    late();
+    return;
+  }
   fast_merge_slots<D, G, true>(a, eg, qh0, nchunk, sh, tid);
   if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  late();
 }
 
-template <typename E, int D, int G, int TILES, bool ONE>
-__global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
+// Fast step over the support gathered through sel_idx: each workgroup first
+// resolves its chunk's support positions into LDS, then loads the rows.
+// PACK: also write the selected rows it loads to the packed buffers.
+template <typename E, int D, int G, int TILES, bool ONE, bool PACK>
+__device__ __forceinline__ void fast_gather_body(const FastArgs& a, const FastSmem<E, D, G, TILES>& sm, int e) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
   constexpr int ROWS = TILES * 16;  // rows per wave
@@ -1232,18 +1274,16 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
   constexpr int NV = ROWS / A::kRPL;
 
   constexpr bool kMfma = fast_pv_mfma<E, TILES>();
-  __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
-  __shared__ __attribute__((aligned(16))) float s_o[kMfma ? 4 : NW * A::kRowGroups * G * D];
-  __shared__ __attribute__((aligned(16))) char s_v[kMfma ? NW * ROWS * A::kRowBytes : 16];
-  __shared__ float s_m[NW * G], s_l[NW * G];
-  __shared__ int s_pos[CH];
-  __shared__ FastTailSmem s_tail;
+  float* s_p = sm.p;
+  float* s_o = sm.o;
+  char* s_v = sm.v;
+  float* s_m = sm.m;
+  float* s_l = sm.l;
+  int* s_pos = sm.pos;
+  FastTailSmem& s_tail = *sm.tail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
-  // ONE: a one-row launch, whose entry sits at fixed kernel-argument offsets
-  // that load with the other arguments (no table search)
-  const int e = ONE ? 0 : find_entry(a.tab, wg);
   const int local = ONE ? wg : wg - a.tab.wg_begin[e];
   const int nchunk = a.tab.ent[e].nsplit;
   const int g = local / nchunk;
@@ -1299,9 +1339,39 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
                                          lane);
       }
     }
+    // Deferred packing: the selected rows this wave loaded also go to the
+    // packed buffers at their selection slots (support element p is slot
+    // p - fixed), through range-checked buffer stores: rows that are not
+    // selected, or whose index is not a position of the context, get an
+    // offset past the buffer and are dropped, as the packing pass skips them.
+    auto pack_rows = [&] {
+      if constexpr (!PACK) return;
+      const int fixed = sg.ns_eff + sg.w_eff;
+      const uint32_t pbytes = static_cast<uint32_t>(a.top_k) * RB;
+      const __amdgpu_buffer_rsrc_t rpk =
+          buf_rsrc_u(static_cast<char*>(a.pack_out_k) + bg * a.top_k * RB, pbytes);
+      const __amdgpu_buffer_rsrc_t rpv =
+          buf_rsrc_u(static_cast<char*>(a.pack_out_v) + bg * a.top_k * RB, pbytes);
+      auto slot_of = [&](int l) {
+        const int slot = c0 + l - fixed;
+        return slot >= 0 && slot < sg.cnt && s_pos[l] >= 0 ? slot : -1;
+      };
+#pragma unroll
+      for (int tt = 0; tt < TILES; ++tt) {
+        const int slot = slot_of(w0 + 16 * tt + kr);
+#pragma unroll
+        for (int kk = 0; kk < A::kNL; ++kk)
+          buf_st16_stream(rpk, slot >= 0 ? static_cast<uint32_t>(slot) * RB + 64 * kk + 16 * kg : kOutOfRange, kb[tt][kk]);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int slot = slot_of(w0 + vr + A::kRPL * i);
+        buf_st16_stream(rpv, slot >= 0 ? static_cast<uint32_t>(slot) * RB + 16 * vp : kOutOfRange, vb[i]);
+      }
+    };
+    fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a,
+                                          static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk, pack_rows);
   }
-  fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a,
-                                        static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk);
 }
 
 // Fast step over the packed support: the selected rows were copied into a
@@ -1312,7 +1382,7 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
 // so all K/V loads are issued at once with no index lookups; only the end of
 // the selected rows (sel_cnt) masks the tail.
 template <typename E, int D, int G, int TILES, bool ONE>
-__global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
+__device__ __forceinline__ void fast_packed_body(const FastArgs& a, const FastSmem<E, D, G, TILES>& sm, int e) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
   constexpr int ROWS = TILES * 16;
@@ -1320,16 +1390,16 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   constexpr int NV = ROWS / A::kRPL;
 
   constexpr bool kMfma = fast_pv_mfma<E, TILES>();
-  __shared__ __attribute__((aligned(16))) float s_p[NW * ROWS * G];
-  __shared__ __attribute__((aligned(16))) float s_o[kMfma ? 4 : NW * A::kRowGroups * G * D];
-  __shared__ __attribute__((aligned(16))) char s_v[kMfma ? NW * ROWS * A::kRowBytes : 16];
-  __shared__ float s_m[NW * G], s_l[NW * G];
-  __shared__ FastTailSmem s_tail;
+  float* s_p = sm.p;
+  float* s_o = sm.o;
+  char* s_v = sm.v;
+  float* s_m = sm.m;
+  float* s_l = sm.l;
+  FastTailSmem& s_tail = *sm.tail;
 
   // the wave index as a scalar, so every test on a wave's rows is a scalar branch
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x;
-  const int e = ONE ? 0 : find_entry(a.tab, wg);
   const int local = ONE ? wg : wg - a.tab.wg_begin[e];
   const int nchunk = a.tab.ent[e].nsplit;
   const int g = local / nchunk;
@@ -1421,7 +1491,38 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
     }
   }
   fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a,
-                                        static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk);
+                                        static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk, [] {});
+}
+
+// ONE: a one-row launch, whose entry sits at fixed kernel-argument offsets
+// that load with the other arguments (no table search).
+template <typename E, int D, int G, int TILES, bool ONE>
+__global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
+  fast_packed_body<E, D, G, TILES, ONE>(a, fast_smem<E, D, G, TILES>(), ONE ? 0 : find_entry(a.tab, blockIdx.x));
+}
+
+// PACK: the variant of sfi_fast_step_pack, which also writes the selected rows
+// it loads to the packed buffers (a separate instantiation, so that the plain
+// fast step keeps its register budget)
+template <typename E, int D, int G, int TILES, bool ONE, bool PACK>
+__global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
+  fast_gather_body<E, D, G, TILES, ONE, PACK>(a, fast_smem<E, D, G, TILES>(),
+                                              ONE ? 0 : find_entry(a.tab, blockIdx.x));
+}
+
+// A launch of several sequences of which some gather and pack their selected
+// rows (bit e of pack_mask set for table entry e: the span's first fast step)
+// and the others read their packed support: each workgroup runs one of the two
+// paths for its entry, sharing one LDS layout.
+template <typename E, int D, int G, int TILES>
+__global__ __launch_bounds__(kFastThreads) void fast_mixed_kernel(FastArgs a) {
+  const FastSmem<E, D, G, TILES> sm = fast_smem<E, D, G, TILES>();
+  const int e = find_entry(a.tab, blockIdx.x);
+  if ((a.pack_mask >> e) & 1u) {
+    fast_gather_body<E, D, G, TILES, false, true>(a, sm, e);
+  } else {
+    fast_packed_body<E, D, G, TILES, false>(a, sm, e);
+  }
 }
 
 // Copies the selected K/V rows of each (sequence, KV head) into the packed
@@ -1614,12 +1715,17 @@ int fast_chunk_rows() { return (kFastThreads / 64) * fast_tiles() * 16; }
 template <typename E, int D, int G, int TILES>
 static void fast_partial_launch(const FastArgs& a, int grid, hipStream_t s) {
   const bool one = a.tab.n == 1;
-  if (a.packed_k != nullptr) {
+  if (a.packed_k != nullptr && a.pack_out_k != nullptr) {
+    launch(fast_mixed_kernel<E, D, G, TILES>, grid, kFastThreads, s, a);
+  } else if (a.packed_k != nullptr) {
     if (one) launch(fast_packed_kernel<E, D, G, TILES, true>, grid, kFastThreads, s, a);
     else launch(fast_packed_kernel<E, D, G, TILES, false>, grid, kFastThreads, s, a);
+  } else if (a.pack_out_k != nullptr) {
+    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, true>, grid, kFastThreads, s, a);
+    else launch(fast_partial_kernel<E, D, G, TILES, false, true>, grid, kFastThreads, s, a);
   } else {
-    if (one) launch(fast_partial_kernel<E, D, G, TILES, true>, grid, kFastThreads, s, a);
-    else launch(fast_partial_kernel<E, D, G, TILES, false>, grid, kFastThreads, s, a);
+    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, false>, grid, kFastThreads, s, a);
+    else launch(fast_partial_kernel<E, D, G, TILES, false, false>, grid, kFastThreads, s, a);
   }
 }
 

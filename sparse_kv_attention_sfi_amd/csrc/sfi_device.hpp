@@ -108,10 +108,14 @@ __device__ __forceinline__ uint4 buf_ld16_stream(__amdgpu_buffer_rsrc_t r, uint3
   return make_uint4(static_cast<uint32_t>(d.x), static_cast<uint32_t>(d.y), static_cast<uint32_t>(d.z),
                     static_cast<uint32_t>(d.w));
 }
-__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+// streaming (nt) store of 16 bytes: for rows written once and not read again
+// in the same kernel, the packed support rows (the fast step's packing
+// measured about 1 us faster with it than with plain stores, the Selector's
+// emission about 0.5 us).
+__device__ __forceinline__ void buf_st16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   typedef int i4 __attribute__((ext_vector_type(4)));
   const i4 d = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(d, r, static_cast<int32_t>(off), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, static_cast<int32_t>(off), 0, 2);
 }
 
 // s_waitcnt vmcnt(0): this wave's earlier vector memory accesses, stores

@@ -154,6 +154,13 @@ struct FastArgs {
   const void* q;
   const int32_t* sel_idx;
   const int32_t* sel_cnt;
+  // gather path only: also write the selected rows it reads into these packed
+  // buffers ([B][Hkv][top_k][D], at their selection slots), or nullptr
+  void* pack_out_k;
+  void* pack_out_v;
+  // with both packed_k and pack_out_k set (a mixed launch, the same buffers):
+  // bit e set = table entry e gathers and packs, clear = it reads packed_k
+  uint64_t pack_mask;
   // chunk states and counters are indexed by the row's entry in the launch
   // table (not its batch row), so they scale with kMaxSeqPerLaunch only
   float* part_ml;   // [entries][Hq][part_stride][2]

@@ -673,8 +673,8 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
         const int it = tid + kSelThreads * u;
         const int r = it >> lg, pc = it & (np - 1);
         const uint32_t off = r < n_pre ? slot_off(slot_of(s_pos[min(r, kStep - 1)] - i0), pc) : kOutOfRange;
-        buf_st16(rpk, off, pk[u]);
-        buf_st16(rpv, off, pv[u]);
+        buf_st16_stream(rpk, off, pk[u]);
+        buf_st16_stream(rpv, off, pv[u]);
       }
       // the kept rows of the threshold bin and the rows above it past the
       // prefetch: copied now
@@ -696,8 +696,8 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-          buf_st16(rpk, dst[u], kv[u]);
-          buf_st16(rpv, dst[u], vv[u]);
+          buf_st16_stream(rpk, dst[u], kv[u]);
+          buf_st16_stream(rpv, dst[u], vv[u]);
         }
       }
     }

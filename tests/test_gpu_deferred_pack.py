@@ -219,3 +219,38 @@ def test_uniform_flags_take_the_single_kind_kernels(flag):
     sp = S.support_params(8, 64, 512, 0.1)
     ws = S.alloc_workspace(kv, sp)
     _mixed_case(kv, sp, [0, 1, 2], q, [flag] * 3, ws)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.1, 1.0])
+def test_selection_does_not_depend_on_the_launch(lam):
+    """The Selector's output for a row does not depend on which rows share its
+    launch (a batch larger than one pass of the CUs, or the row alone) nor on
+    whether the refresh packs: bit for bit the same positions and counts."""
+    B = 12
+    ctx = [20000, 19000, 15000, 9000, 4500, 2400, 2300, 600, 20000, 11111, 8192, 16385]
+    kv, q = random_cache(B, 16, 8, 20000, 64, torch.bfloat16, ctx, seed=331, q_scale=2.0)
+    dev = kv.k.device
+    sp = S.support_params(16, 256, 2048, lam)
+    ws = S.alloc_workspace(kv, sp)
+    ids = list(range(B))
+    _, mass = run_slow(kv, q, ids, ws=ws)
+
+    def sel_of(rows, packed):
+        sel = torch.full((B, kv.n_kv_heads, sp.top_k), -7, dtype=torch.int32, device=dev)
+        cnt = torch.full((B, kv.n_kv_heads), -7, dtype=torch.int32, device=dev)
+        if packed:
+            pk, pv = _packed_pair(kv, sp, 0.0)
+            out = torch.empty(B, kv.n_q_heads, kv.head_dim, device=dev)
+            m2 = torch.empty_like(mass)
+            S.sfi_slow_step_select(kv, sp, rows, q, out, m2, sel, cnt, pk, pv, ws)
+        else:
+            S.sfi_select(kv, sp, rows, mass, sel, cnt, ws)
+        torch.cuda.synchronize()
+        return sel, cnt
+
+    batch_sel, batch_cnt = sel_of(ids, False)
+    pack_sel, pack_cnt = sel_of(ids, True)
+    assert torch.equal(batch_sel, pack_sel) and torch.equal(batch_cnt, pack_cnt)
+    for b in ids:
+        one_sel, one_cnt = sel_of([b], False)
+        assert torch.equal(one_sel[b], batch_sel[b]) and torch.equal(one_cnt[b], batch_cnt[b]), b

@@ -33,13 +33,25 @@ def _buffers(kv, sp):
 
 
 def _run_all(kv, sp, ids, q, ws):
+    """The refresh with packing and the fast steps over its support, then the
+    refresh without packing and the packing fast step over that support."""
     o = _buffers(kv, sp)
     S.sfi_slow_step_select(kv, sp, ids, q, o["out"], o["mass"], o["sel"], o["cnt"], o["pk"], o["pv"], ws)
     S.sfi_fast_step_packed(kv, sp, ids, q, o["pk"], o["pv"], o["cnt"], o["fast"], ws)
     S.sfi_fast_step(kv, sp, ids, q, o["sel"], o["cnt"], o["gath"], ws)
     S.sfi_slow_step(kv, ids, q, o["dense"], None, ws)
+    d = _buffers(kv, sp)
+    S.sfi_slow_step_select(kv, sp, ids, q, d["out"], d["mass"], d["sel"], d["cnt"], None, None, ws)
+    S.sfi_fast_step_pack(kv, sp, ids, q, d["sel"], d["cnt"], d["fast"], d["pk"], d["pv"], ws)
     torch.cuda.synchronize()
+    o.update({"d_" + key: d[key] for key in ("out", "mass", "sel", "cnt", "fast", "pk", "pv")})
     return o
+
+
+def _same_both_packings(o):
+    for key in ("out", "mass", "sel", "cnt", "pk", "pv"):
+        assert torch.equal(o[key], o["d_" + key]), key
+    assert torch.equal(o["d_fast"], o["gath"])
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -59,6 +71,7 @@ def test_device_lengths_with_exact_bounds_equal_host_lengths(dtype):
     got = _run_all(kvd, sp, ids, q, ws)
     for key in ref:
         assert torch.equal(ref[key], got[key]), key
+    _same_both_packings(ref)
 
 
 def test_device_lengths_below_their_bounds_match_the_oracle():
@@ -75,6 +88,7 @@ def test_device_lengths_below_their_bounds_match_the_oracle():
     ids = [0, 1, 2, 3]
     o = _run_all(kv, sp, ids, q, ws)
     assert torch.equal(o["fast"], o["gath"])
+    _same_both_packings(o)
     for b, T in enumerate(ctx):
         K64, V64 = np64(kv.k[b, :, :T]), np64(kv.v[b, :, :T])
         o_ref, P = O.dense_attention(np64(q[b]), K64, V64)
@@ -113,13 +127,16 @@ def test_append_advances_device_lengths_and_skips_full_rows():
     assert torch.equal(kv.k[0, :, 10], kn[0]) and torch.equal(kv.v[1, :, 63], vn[1])
 
 
-def test_growing_history_layer_captured_once_and_replayed():
+@pytest.mark.parametrize("packing", ["refresh", "deferred"])
+def test_growing_history_layer_captured_once_and_replayed(packing):
     """One layer of the 32-layer loop (batch 4, 128K context growing by one
     token a step, k = 4096, window 512, its own span schedules): every decode
-    step (append, refresh of the rows that open a span, packed fast step of
-    the others) is captured once per slow/fast pattern and replayed across 20
-    appends.  Each replayed step equals the same loop run eagerly, bit for
-    bit, and sequence 0 matches the oracle at the last steps."""
+    step (append, refresh of the rows that open a span, one fast launch for
+    the others) is captured once per row pattern and replayed across 20
+    appends.  With deferred packing the refresh only selects and the fast
+    launch packs the rows on their span's first fast step.  Each replayed
+    step equals the same loop run eagerly, bit for bit, and sequence 0
+    matches the oracle at the last steps."""
     w = synth.C5
     dev = torch.device("cuda:0")
     n_steps = 20
@@ -142,13 +159,22 @@ def test_growing_history_layer_captured_once_and_replayed():
     kn_buf, vn_buf = torch.empty_like(kn[0]), torch.empty_like(vn[0])
     ids = list(range(w.batch))
 
-    def step(slow, fast):
+    deferred = packing == "deferred"
+
+    def step(slow, fast, first=()):
         S.sfi_kv_append(kv, ids, kn_buf, vn_buf)
         if slow:
-            S.sfi_slow_step_select(kv, sp, list(slow), q_buf, o["out"], o["mass"], o["sel"], o["cnt"], o["pk"],
-                                   o["pv"], ws)
-        if fast:
+            S.sfi_slow_step_select(kv, sp, list(slow), q_buf, o["out"], o["mass"], o["sel"], o["cnt"],
+                                   None if deferred else o["pk"], None if deferred else o["pv"], ws)
+        if fast and deferred and first:
+            rows = sorted(fast)
+            S.sfi_fast_step_pack(kv, sp, rows, q_buf, o["sel"], o["cnt"], o["out"], o["pk"], o["pv"], ws,
+                                 pack_flags=[int(b in first) for b in rows])
+        elif fast:
             S.sfi_fast_step_packed(kv, sp, list(fast), q_buf, o["pk"], o["pv"], o["cnt"], o["out"], ws)
+
+    # rows on their span's first fast step (they refreshed the step before)
+    firsts = [tuple(b for b in plan[t][1] if t > 0 and b in plan[t - 1][0]) for t in range(n_steps)]
 
     def stage(t):
         q_buf.copy_(qs[t])
@@ -158,19 +184,19 @@ def test_growing_history_layer_captured_once_and_replayed():
     eager = []
     for t in range(n_steps):
         stage(t)
-        step(*plan[t])
+        step(*plan[t], firsts[t])
         eager.append(o["out"].clone())
     torch.cuda.synchronize()
     assert dev_ctx.tolist() == bound
     dev_ctx.copy_(torch.tensor(T0, dtype=torch.int32))
     graphs = {}
     for t in range(n_steps):
-        key = tuple(plan[t][0])
+        key = (tuple(plan[t][0]), firsts[t] if deferred else ())
         if key not in graphs:
             torch.cuda.synchronize()
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
-                step(*plan[t])
+                step(*plan[t], firsts[t])
             graphs[key] = gr
         stage(t)
         o["out"].fill_(float("nan"))

@@ -58,6 +58,16 @@ int main(void) {
                               NULL) == SFI_ERR_WORKSPACE);
   int32_t splits[2] = {0, 0};
   EXPECT(sfi_slow_plan(&d, ids, 2, 1, splits) == SFI_OK && splits[0] >= 1 && splits[1] >= 1);
+  /* the packing fast step: its packed buffers are required, and its workspace is the fast step's */
+  int32_t flags[2] = {1, 0};
+  size_t need_fast = sfi_workspace_bytes(&d, &sp, SFI_OP_FAST);
+  EXPECT(need_fast > 0);
+  EXPECT(sfi_fast_step_pack(&d, &sp, ids, 2, flags, (void*)0x30000, (int32_t*)0x70000, (int32_t*)0x80000,
+                            (float*)0x40000, NULL, NULL, (void*)0x50000, need_fast, NULL) == SFI_ERR_INVALID_ARG);
+  EXPECT(strstr(sfi_last_error(), "packed") != NULL);
+  EXPECT(sfi_fast_step_pack(&d, &sp, ids, 2, flags, (void*)0x30000, (int32_t*)0x70000, (int32_t*)0x80000,
+                            (float*)0x40000, (void*)0x90000, (void*)0xA0000, (void*)0x50000, need_fast - 1,
+                            NULL) == SFI_ERR_WORKSPACE);
 
   /* the scheduler: geometric spans of mean 18 for 3 sequences, seed 7 */
   sfi_sched* s = NULL;

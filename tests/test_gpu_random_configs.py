@@ -2,7 +2,8 @@
 (dtype, head dim, query/KV heads, ragged batch, sinks, window, top-k, lambda,
 query scale from 0, where every position ties, to 4, an unordered subset of
 rows) one fused refresh and one fast step
-of each kind run on the GPU and are checked against the oracle: dense output,
+of each kind (gather, packed, and gather with packing for a random subset of
+the rows) run on the GPU and are checked against the oracle: dense output,
 mass, support, packed rows, and the fast output over the GPU's own support
 (once that support has passed the support check).  A second, wider set adds
 contexts up to 300K rows, batches beyond one launch group and larger top-k."""
@@ -98,8 +99,20 @@ def _run(c, seed):
     out_g = torch.full_like(out, 7.0)
     S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out_p, ws)
     S.sfi_fast_step(kv, sp, ids, q, sel, cnt, out_g, ws)
+    # the packing fast step: some rows gather and pack, the others read the
+    # rows the refresh packed (one launch)
+    flags = [int(x) for x in np.random.default_rng(seed + 7).random(len(ids)) < 0.5]
+    pk_d, pv_d = torch.zeros_like(pk), torch.zeros_like(pv)
+    for b, f in zip(ids, flags):
+        if not f:
+            pk_d[b].copy_(pk[b])
+            pv_d[b].copy_(pv[b])
+    out_d = torch.full_like(out, 7.0)
+    S.sfi_fast_step_pack(kv, sp, ids, q, sel, cnt, out_d, pk_d, pv_d, ws, pack_flags=flags)
     torch.cuda.synchronize()
     assert torch.equal(out_p, out_g)
+    assert torch.equal(out_d, out_g)
+    assert torch.equal(pk_d, pk) and torch.equal(pv_d, pv)
     for b in range(B):
         if b not in ids:
             assert torch.all(out[b] == 7.0) and torch.all(cnt[b] == -7) and torch.all(mass[b] == -1.0)

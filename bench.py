@@ -601,7 +601,7 @@ def main():
         del kvs, q_steps, graphs, run
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        result["configs"] = config_block(dev, result, args.pack)
+        result["configs"] = config_block(dev, result, args.workload, args.pack)
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -876,24 +876,27 @@ def fast_batch_check(w, sp, batch, dev, ctx=32768, calls=20):
     return res
 
 
-def config_block(dev, headline, pack="deferred"):
+def config_block(dev, headline, name, pack="deferred"):
     """SFI against dense decode on every workload beside the headline: the
     32K layer (128 independent layer caches), the batch of 16 mixed contexts
     (8 cycled caches) and the 32-layer growing-history loop, each over its
-    whole span schedule, plus the 128K headline's own full-schedule figures."""
+    whole span schedule, plus the headline's own full-schedule figures under
+    its workload name `name` (which is then not measured a second time)."""
     import synth
     out = {}
     hs = headline.get("full_schedule") or {}
     if hs and headline.get("dense_steps_per_s_layer"):
-        out["C3"] = {"workload": headline["config"]["workload"], "steps": hs["steps"],
+        out[name] = {"workload": headline["config"]["workload"], "steps": hs["steps"],
                      "sfi_steps_per_s_layer": hs["blended_steps_per_s_layer"],
                      "dense_steps_per_s_layer": headline["dense_steps_per_s_layer"],
                      "speedup_vs_dense": hs["blended_steps_per_s_layer"] / headline["dense_steps_per_s_layer"],
                      "slow_row_fraction": hs["slow_fraction"]}
-    for name, w, layers in (("C2", synth.C2, 128), ("C4", synth.C4, 8), ("C5", synth.C5, synth.C5.n_layers)):
-        out[name] = measure_loop(w, dev, layers, dense_steps=64, warmup=8, pack=pack)
-        log(f"{name}: SFI {out[name]['sfi_steps_per_s_layer']:.0f} decode steps/s/layer, "
-            f"dense {out[name]['dense_steps_per_s_layer']:.0f}, speedup {out[name]['speedup_vs_dense']:.2f}")
+    for wname, w, layers in (("C2", synth.C2, 128), ("C4", synth.C4, 8), ("C5", synth.C5, synth.C5.n_layers)):
+        if wname in out:
+            continue
+        out[wname] = measure_loop(w, dev, layers, dense_steps=64, warmup=8, pack=pack)
+        log(f"{wname}: SFI {out[wname]['sfi_steps_per_s_layer']:.0f} decode steps/s/layer, "
+            f"dense {out[wname]['dense_steps_per_s_layer']:.0f}, speedup {out[wname]['speedup_vs_dense']:.2f}")
     return out
 
 

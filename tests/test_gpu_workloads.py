@@ -1,5 +1,6 @@
 """GPU parity on the five synthetic workloads, in the launch configuration the
-bench uses (the fused refresh with packing, the fast step over the packed
+bench uses (the fused refresh, which selects; the span's first fast step,
+which gathers and packs the support; the later fast steps over the packed
 support): the full 64-step loop of the tiny fp32 case, sampled steps of the
 larger ones (every output the oracle can afford is compared element by
 element; the rest is checked through properties that hold at any size), and
@@ -32,9 +33,11 @@ def _schedules(w, n_steps):
 
 class Runner:
     """Buffers and calls of one layer of a workload through the C ABI, in the
-    bench's configuration: the fused refresh (slow step + Selector + packing)
-    and the fast step over the packed support.  The separate calls and the
-    gather fast step serve as cross-checks."""
+    bench's configuration: the fused refresh (slow step + Selector), the
+    span's first fast step gathering its support and packing it
+    (sfi_fast_step_pack) and the later fast steps over the packed support.
+    The refresh that also packs, the separate calls and the gather fast step
+    serve as cross-checks."""
 
     def __init__(self, w, kv):
         dev = kv.k.device
@@ -47,23 +50,52 @@ class Runner:
         self.sel = torch.full((B, w.n_kv_heads, w.top_k), -1, dtype=torch.int32, device=dev)
         self.cnt = torch.zeros(B, w.n_kv_heads, dtype=torch.int32, device=dev)
         shape = (B, w.n_kv_heads, w.top_k, w.head_dim)
-        self.pk = torch.zeros(shape, dtype=kv.dtype, device=dev)
-        self.pv = torch.zeros(shape, dtype=kv.dtype, device=dev)
+        self.pk = torch.full(shape, float("nan"), dtype=kv.dtype, device=dev)
+        self.pv = torch.full(shape, float("nan"), dtype=kv.dtype, device=dev)
+        self.to_pack = set()   # rows whose next fast step is the first of their span
 
     def slow(self, ids, q):
         if ids:
+            S.sfi_slow_step_select(self.kv, self.sp, ids, q, self.out, self.mass, self.sel, self.cnt, None, None,
+                                   self.ws)
+            self.to_pack.update(ids)
+
+    def slow_packing(self, ids, q):
+        if ids:
             S.sfi_slow_step_select(self.kv, self.sp, ids, q, self.out, self.mass, self.sel, self.cnt, self.pk,
                                    self.pv, self.ws)
+            self.to_pack.difference_update(ids)
 
     def slow_separate(self, ids, q):
         if ids:
             S.sfi_slow_step(self.kv, ids, q, self.out, self.mass, self.ws)
             S.sfi_select(self.kv, self.sp, ids, self.mass, self.sel, self.cnt, self.ws)
             S.sfi_pack_support(self.kv, self.sp, ids, self.sel, self.cnt, self.pk, self.pv)
+            self.to_pack.difference_update(ids)
 
     def fast(self, ids, q):
-        if ids:
+        """One launch for the rows, as the bench makes it; returns the rows
+        that packed."""
+        ids = sorted(ids)
+        first = [b for b in ids if b in self.to_pack]
+        if first:
+            S.sfi_fast_step_pack(self.kv, self.sp, ids, q, self.sel, self.cnt, self.out, self.pk, self.pv, self.ws,
+                                 pack_flags=[int(b in self.to_pack) for b in ids])
+            self.to_pack.difference_update(first)
+        elif ids:
             S.sfi_fast_step_packed(self.kv, self.sp, ids, q, self.pk, self.pv, self.cnt, self.out, self.ws)
+        return first
+
+    def packed_rows_ok(self, b):
+        """The rows the first fast step packed for row b equal sfi_pack_support's."""
+        pk, pv = torch.zeros_like(self.pk), torch.zeros_like(self.pv)
+        S.sfi_pack_support(self.kv, self.sp, [b], self.sel, self.cnt, pk, pv)
+        torch.cuda.synchronize()
+        for g in range(self.w.n_kv_heads):
+            c = int(self.cnt[b, g])
+            if not (torch.equal(self.pk[b, g, :c], pk[b, g, :c]) and torch.equal(self.pv[b, g, :c], pv[b, g, :c])):
+                return False
+        return True
 
     def fast_gather(self, ids, q):
         if ids:
@@ -122,9 +154,15 @@ def test_tiny_fp32_full_loop():
             r.slow_separate([0], q[t])
             torch.cuda.synchronize()
             separate = r.state()
-            r.slow([0], q[t])
+            r.slow_packing([0], q[t])
             torch.cuda.synchronize()
             assert all(torch.equal(a, b) for a, b in zip(r.state(), separate))   # fused == separate calls
+            # the bench's refresh packs nothing: the span's first fast step does
+            r.pk.fill_(float("nan"))
+            r.pv.fill_(float("nan"))
+            r.slow([0], q[t])
+            torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip(r.state()[:4], separate[:4]))
             _, kinds = _check_slow(r, 0, np64(q[t, 0]), K64, V64, T)
             exact += kinds.count("exact")
             s_idx = span_ids[0][t]
@@ -132,7 +170,8 @@ def test_tiny_fp32_full_loop():
                 planted = set(c["planted"][0][g][s_idx].tolist())
                 recalls.append(len(planted & set(s.tolist())) / len(planted))
         else:
-            r.fast([0], q[t])
+            if r.fast([0], q[t]):
+                assert r.packed_rows_ok(0)
             torch.cuda.synchronize()
             ref = O.fast_step(np64(q[t, 0]), K64, V64, T, w.n_sink, w.n_recent, r.gpu_sel(0))
             assert np.max(np.abs(np64(r.out[0]) - ref)) < OUT_TOL
@@ -168,7 +207,8 @@ def test_8b_layer_sampled_steps(wname, n_fast):
             ora_sels = [O.select(f_ref[g], T, w.n_sink, w.n_recent, w.top_k, w.lam)[0]
                         for g in range(w.n_kv_heads)]
         else:
-            r.fast([0], q[t])
+            if r.fast([0], q[t]):
+                assert r.packed_rows_ok(0)
             torch.cuda.synchronize()
             gpu = np64(r.out[0])
             packed_out = r.out.clone()

@@ -70,8 +70,8 @@ def csrc_digest():
 
 def kernel_group(name):
     """Bench kernel name of a device kernel (the Selector's kernels form one group)."""
-    if "fast_partial_kernel<" in name and name.split(">")[0].endswith("true"):
-        return "fast_pack"  # the gather step's packing variant (last template argument)
+    if "fast_partial_kernel<" in name and name.split(">")[0].rsplit(",", 1)[-1].strip() not in ("0", "false"):
+        return "fast_pack"  # the gather step's packing variants (last template argument: when it packs)
     for key, group in (("slow_partial", "slow_partial"), ("slow_combine", "slow_combine"), ("select_", "select"),
                        ("pack_kernel", "pack"), ("fast_packed", "fast_partial"), ("fast_partial", "fast_partial"),
                        ("fast_merge", "fast_merge")):

@@ -1261,10 +1261,20 @@ __device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float
   late();
 }
 
+// When the fast step that gathers also packs (sfi_fast_step_pack), the
+// selected rows it loaded are stored either after the workgroup's ticket
+// (launches that merge in the kernel: neither the wait for the chunk-state
+// stores nor the last workgroup's merge waits behind them) or right after the
+// attention math (launches that merge in the second kernel: the loaded rows
+// then need not stay in registers through the tail, which keeps the register
+// count, and so the workgroups per CU, of the plain gather).
+constexpr int kPackNone = 0, kPackAfterTicket = 1, kPackAfterMath = 2;
+
 // Fast step over the support gathered through sel_idx: each workgroup first
 // resolves its chunk's support positions into LDS, then loads the rows.
-// PACK: also write the selected rows it loads to the packed buffers.
-template <typename E, int D, int G, int TILES, bool ONE, bool PACK>
+// PACK (kPack*): whether and when to write the selected rows it loads to the
+// packed buffers.
+template <typename E, int D, int G, int TILES, bool ONE, int PACK>
 __device__ __forceinline__ void fast_gather_body(const FastArgs& a, const FastSmem<E, D, G, TILES>& sm, int e) {
   using A = Attn<E, D, G>;
   constexpr int RB = A::kRowBytes;
@@ -1345,7 +1355,7 @@ __device__ __forceinline__ void fast_gather_body(const FastArgs& a, const FastSm
     // selected, or whose index is not a position of the context, get an
     // offset past the buffer and are dropped, as the packing pass skips them.
     auto pack_rows = [&] {
-      if constexpr (!PACK) return;
+      if constexpr (PACK == kPackNone) return;
       const int fixed = sg.ns_eff + sg.w_eff;
       const uint32_t pbytes = static_cast<uint32_t>(a.top_k) * RB;
       const __amdgpu_buffer_rsrc_t rpk =
@@ -1369,8 +1379,11 @@ __device__ __forceinline__ void fast_gather_body(const FastArgs& a, const FastSm
         buf_st16_stream(rpv, slot >= 0 ? static_cast<uint32_t>(slot) * RB + 16 * vp : kOutOfRange, vb[i]);
       }
     };
+    if constexpr (PACK == kPackAfterMath) pack_rows();
     fast_finish<A, D, G, NW, ROWS, kMfma>(st, s_m, s_l, s_o, s_v, s_tail, wave, lane, tid, a,
-                                          static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk, pack_rows);
+                                          static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk, [&] {
+                                            if constexpr (PACK == kPackAfterTicket) pack_rows();
+                                          });
   }
 }
 
@@ -1501,10 +1514,10 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
   fast_packed_body<E, D, G, TILES, ONE>(a, fast_smem<E, D, G, TILES>(), ONE ? 0 : find_entry(a.tab, blockIdx.x));
 }
 
-// PACK: the variant of sfi_fast_step_pack, which also writes the selected rows
-// it loads to the packed buffers (a separate instantiation, so that the plain
-// fast step keeps its register budget)
-template <typename E, int D, int G, int TILES, bool ONE, bool PACK>
+// PACK != kPackNone: the variants of sfi_fast_step_pack, which also write the
+// selected rows they load to the packed buffers (separate instantiations, so
+// that the plain fast step keeps its register budget)
+template <typename E, int D, int G, int TILES, bool ONE, int PACK>
 __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
   fast_gather_body<E, D, G, TILES, ONE, PACK>(a, fast_smem<E, D, G, TILES>(),
                                               ONE ? 0 : find_entry(a.tab, blockIdx.x));
@@ -1513,13 +1526,15 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
 // A launch of several sequences of which some gather and pack their selected
 // rows (bit e of pack_mask set for table entry e: the span's first fast step)
 // and the others read their packed support: each workgroup runs one of the two
-// paths for its entry, sharing one LDS layout.
+// paths for its entry, sharing one LDS layout.  Such launches hold several
+// rows and rarely fit the CUs in one pass, so the packing stores follow the
+// attention math.
 template <typename E, int D, int G, int TILES>
 __global__ __launch_bounds__(kFastThreads) void fast_mixed_kernel(FastArgs a) {
   const FastSmem<E, D, G, TILES> sm = fast_smem<E, D, G, TILES>();
   const int e = find_entry(a.tab, blockIdx.x);
   if ((a.pack_mask >> e) & 1u) {
-    fast_gather_body<E, D, G, TILES, false, true>(a, sm, e);
+    fast_gather_body<E, D, G, TILES, false, kPackAfterMath>(a, sm, e);
   } else {
     fast_packed_body<E, D, G, TILES, false>(a, sm, e);
   }
@@ -1720,12 +1735,15 @@ static void fast_partial_launch(const FastArgs& a, int grid, hipStream_t s) {
   } else if (a.packed_k != nullptr) {
     if (one) launch(fast_packed_kernel<E, D, G, TILES, true>, grid, kFastThreads, s, a);
     else launch(fast_packed_kernel<E, D, G, TILES, false>, grid, kFastThreads, s, a);
+  } else if (a.pack_out_k != nullptr && a.ticket != nullptr) {
+    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, kPackAfterTicket>, grid, kFastThreads, s, a);
+    else launch(fast_partial_kernel<E, D, G, TILES, false, kPackAfterTicket>, grid, kFastThreads, s, a);
   } else if (a.pack_out_k != nullptr) {
-    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, true>, grid, kFastThreads, s, a);
-    else launch(fast_partial_kernel<E, D, G, TILES, false, true>, grid, kFastThreads, s, a);
+    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, kPackAfterMath>, grid, kFastThreads, s, a);
+    else launch(fast_partial_kernel<E, D, G, TILES, false, kPackAfterMath>, grid, kFastThreads, s, a);
   } else {
-    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, false>, grid, kFastThreads, s, a);
-    else launch(fast_partial_kernel<E, D, G, TILES, false, false>, grid, kFastThreads, s, a);
+    if (one) launch(fast_partial_kernel<E, D, G, TILES, true, kPackNone>, grid, kFastThreads, s, a);
+    else launch(fast_partial_kernel<E, D, G, TILES, false, kPackNone>, grid, kFastThreads, s, a);
   }
 }
 

@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "sfi_device.hpp"
 #include "sfi_internal.hpp"
@@ -1060,11 +1061,14 @@ constexpr bool fast_pv_mfma() {
 }
 
 // Shared memory of the fast step's tail: the last workgroup of a head merges
-// the chunk states of its kFastThreads / (G * D / 4) slot subsets through it.
+// the chunk states of its kFastThreads / (G * D / 4) slot subsets through it
+// (subset 0 stays in registers, so only the other subsets take entries).
+template <int D, int G>
 struct FastTailSmem {
-  float m[kFastThreads];
-  float l[kFastThreads];
-  float4 o[kFastThreads];
+  static constexpr int kEntries = kFastThreads > G * D / 4 ? kFastThreads - G * D / 4 : 1;
+  float m[kEntries];
+  float l[kEntries];
+  float4 o[kEntries];
   int last;
 };
 
@@ -1082,7 +1086,7 @@ struct FastSmem {
   float* m;
   float* l;
   int* pos;
-  FastTailSmem* tail;
+  FastTailSmem<D, G>* tail;
 };
 template <typename E, int D, int G, int TILES>
 __device__ __forceinline__ FastSmem<E, D, G, TILES> fast_smem() {
@@ -1093,7 +1097,7 @@ __device__ __forceinline__ FastSmem<E, D, G, TILES> fast_smem() {
   __shared__ __attribute__((aligned(16))) char v[kMfma ? kWaves * kRows * Attn<E, D, G>::kRowBytes : 16];
   __shared__ float m[kWaves * G], l[kWaves * G];
   __shared__ int pos[kWaves * kRows];
-  __shared__ FastTailSmem tail;
+  __shared__ FastTailSmem<D, G> tail;
   return {p, o, v, m, l, pos, &tail};
 }
 
@@ -1108,7 +1112,7 @@ __device__ __forceinline__ FastSmem<E, D, G, TILES> fast_smem() {
 // threads, so they give the same bits.
 template <int D, int G, bool COHERENT>
 __device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t eg, int64_t qh0, int nchunk,
-                                                 FastTailSmem& sh, int tid) {
+                                                 FastTailSmem<D, G>& sh, int tid) {
   constexpr int C4 = D / 4;
   constexpr int NC = G * C4;  // column quads of the group: 16 ... 256
   constexpr int NSUB = kFastThreads / NC;
@@ -1162,21 +1166,24 @@ __device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t eg, 
     }
   }
   if constexpr (NSUB > 1) {
-    sh.m[tid] = M;
-    sh.l[tid] = L;
-    sh.o[tid] = acc;
+    static_assert(FastTailSmem<D, G>::kEntries == (NSUB - 1) * NC, "one entry per thread of subsets 1..");
+    if (sub != 0) {
+      sh.m[tid - NC] = M;
+      sh.l[tid - NC] = L;
+      sh.o[tid - NC] = acc;
+    }
     __syncthreads();
     if (sub != 0) return;
 #pragma unroll
     for (int u = 1; u < NSUB; ++u) {
-      const float mu = sh.m[u * NC + col];
+      const float mu = sh.m[(u - 1) * NC + col];
       if (mu == -INFINITY) continue;
       const float mn = fmaxf(M, mu);
       const float s_old = M == -INFINITY ? 0.f : fast_exp2(M - mn), s_new = fast_exp2(mu - mn);
-      const float4 ou = sh.o[u * NC + col];
+      const float4 ou = sh.o[(u - 1) * NC + col];
       acc.x = acc.x * s_old + ou.x * s_new; acc.y = acc.y * s_old + ou.y * s_new;
       acc.z = acc.z * s_old + ou.z * s_new; acc.w = acc.w * s_old + ou.w * s_new;
-      L = L * s_old + sh.l[u * NC + col] * s_new;
+      L = L * s_old + sh.l[(u - 1) * NC + col] * s_new;
       M = mn;
     }
   }
@@ -1203,9 +1210,9 @@ __device__ __forceinline__ void fast_merge_slots(const FastArgs& a, int64_t eg, 
 // stores does not also wait for them, and in the last workgroup after the
 // merge, whose loads would otherwise wait behind them.
 template <typename A, int D, int G, int NW, int ROWS, bool MFMA, typename Late>
-__device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v, FastTailSmem& sh,
-                                            int wave, int lane, int tid, const FastArgs& a, int64_t eg, int64_t qh0,
-                                            int chunk, int nchunk, Late&& late) {
+__device__ __forceinline__ void fast_finish(A& st, float* s_m, float* s_l, float* s_o, char* s_v,
+                                            FastTailSmem<D, G>& sh, int wave, int lane, int tid, const FastArgs& a,
+                                            int64_t eg, int64_t qh0, int chunk, int nchunk, Late&& late) {
   constexpr int kWaveBytes = ROWS * A::kRowBytes;
   if constexpr (MFMA) {
     wave_sync();
@@ -1290,7 +1297,7 @@ __device__ __forceinline__ void fast_gather_body(const FastArgs& a, const FastSm
   float* s_m = sm.m;
   float* s_l = sm.l;
   int* s_pos = sm.pos;
-  FastTailSmem& s_tail = *sm.tail;
+  FastTailSmem<D, G>& s_tail = *sm.tail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x;
@@ -1408,7 +1415,7 @@ __device__ __forceinline__ void fast_packed_body(const FastArgs& a, const FastSm
   char* s_v = sm.v;
   float* s_m = sm.m;
   float* s_l = sm.l;
-  FastTailSmem& s_tail = *sm.tail;
+  FastTailSmem<D, G>& s_tail = *sm.tail;
 
   // the wave index as a scalar, so every test on a wave's rows is a scalar branch
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1507,10 +1514,23 @@ __device__ __forceinline__ void fast_packed_body(const FastArgs& a, const FastSm
                                         static_cast<int64_t>(e) * a.n_kv_heads + g, qh0, chunk, nchunk, [] {});
 }
 
+// Waves per SIMD a fast-step kernel is compiled for.  Launches of several
+// rows hold more workgroups than the CUs, so more of them resident means more
+// loads in flight: for bf16 caches at two tiles per wave the code fits 128
+// VGPRs without spilling, which with its LDS (under 40 KB) lets four
+// workgroups share a CU instead of three.  One-row launches, which the
+// in-kernel merge serves one workgroup per CU, and the other shapes keep the
+// compiler's register choice.
+template <typename E, int TILES, bool ONE>
+constexpr int fast_waves_per_simd() {
+  return !ONE && std::is_same<E, BF16>::value && TILES == 2 ? 4 : 1;
+}
+
 // ONE: a one-row launch, whose entry sits at fixed kernel-argument offsets
 // that load with the other arguments (no table search).
 template <typename E, int D, int G, int TILES, bool ONE>
-__global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
+__global__ __launch_bounds__(kFastThreads, (fast_waves_per_simd<E, TILES, ONE>())) void
+fast_packed_kernel(FastArgs a) {
   fast_packed_body<E, D, G, TILES, ONE>(a, fast_smem<E, D, G, TILES>(), ONE ? 0 : find_entry(a.tab, blockIdx.x));
 }
 
@@ -1518,7 +1538,8 @@ __global__ __launch_bounds__(kFastThreads) void fast_packed_kernel(FastArgs a) {
 // selected rows they load to the packed buffers (separate instantiations, so
 // that the plain fast step keeps its register budget)
 template <typename E, int D, int G, int TILES, bool ONE, int PACK>
-__global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) {
+__global__ __launch_bounds__(kFastThreads, (fast_waves_per_simd<E, TILES, ONE || PACK == kPackAfterTicket>())) void
+fast_partial_kernel(FastArgs a) {
   fast_gather_body<E, D, G, TILES, ONE, PACK>(a, fast_smem<E, D, G, TILES>(),
                                               ONE ? 0 : find_entry(a.tab, blockIdx.x));
 }
@@ -1530,7 +1551,8 @@ __global__ __launch_bounds__(kFastThreads) void fast_partial_kernel(FastArgs a) 
 // rows and rarely fit the CUs in one pass, so the packing stores follow the
 // attention math.
 template <typename E, int D, int G, int TILES>
-__global__ __launch_bounds__(kFastThreads) void fast_mixed_kernel(FastArgs a) {
+__global__ __launch_bounds__(kFastThreads, (fast_waves_per_simd<E, TILES, false>())) void
+fast_mixed_kernel(FastArgs a) {
   const FastSmem<E, D, G, TILES> sm = fast_smem<E, D, G, TILES>();
   const int e = find_entry(a.tab, blockIdx.x);
   if ((a.pack_mask >> e) & 1u) {
@@ -1600,7 +1622,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 // heads, renormalised over the whole support.
 template <int D, int G, bool ONE>
 __global__ __launch_bounds__(kFastThreads) void fast_merge_kernel(FastArgs a) {
-  __shared__ FastTailSmem s_tail;
+  __shared__ FastTailSmem<D, G> s_tail;
   const int e = ONE ? 0 : blockIdx.x / a.n_kv_heads;
   const int g = ONE ? blockIdx.x : blockIdx.x - e * a.n_kv_heads;
   const int b = a.tab.ent[e].seq;

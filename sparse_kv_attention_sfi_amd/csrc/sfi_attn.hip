@@ -6,17 +6,22 @@
 //    K and V rows of one KV head exactly once and keeps the online-softmax
 //    state (running max, running sum, un-normalised output) of the G query
 //    heads that share the KV head.  It also stores the scaled logits so the
-//    merge kernel can turn them into per-position softmax mass.
+//    combine kernel can turn them into per-position softmax mass.
 //  * slow_combine: merges the split partials into the output and writes the
 //    Selector's evidence, the softmax mass averaged over the query group
 //    (2.B "Der Training-Free Selector").
-//  * fast_partial / fast_merge: attention restricted to sinks + recent window
-//    + selected memory (2.A, items 1-3), gathering K/V rows by index in
-//    chunks, then merging the chunk partials of each (sequence, KV head).
+//  * fast_packed / fast_partial / fast_mixed, fast_merge: attention
+//    restricted to sinks + recent window + selected memory (2.A, items 1-3)
+//    in chunks of the support, reading the selected rows from the packed
+//    buffers or gathering them by index (and, for the span's first fast
+//    step, packing them), then merging the chunk states of each (sequence,
+//    KV head): inside the kernel when the launch fits the CUs in one pass,
+//    else in fast_merge.
 //
-// Workgroups never hand data to each other inside a kernel: on gfx950 a
-// device-scope fence writes back and invalidates the XCD's L2, which is far
-// more expensive than the kernel boundary between a partial and a merge pass.
+// The in-kernel merge is the only place where workgroups of one kernel hand
+// data to each other.  It uses device-coherent (sc1) stores and loads and a
+// relaxed ticket, with no device-scope fence: on gfx950 such a fence writes
+// back and invalidates the XCD's L2, which costs more than a kernel boundary.
 //
 // Work layout inside a wave (64 lanes), per 16-row tile of K:
 //   logits   S[h][j] = q_h . k_j come from MFMA 16x16 (bf16: 16x16x32,
@@ -26,10 +31,12 @@
 //            logits of their row (lanes 16..31 heads 4..7 when G = 8).
 //   softmax  per-head block max over the tile rows with DPP row reductions,
 //            exp2 in the log2 domain, probabilities staged in LDS.
-//   P.V      VALU FMAs: lane l owns one 16-byte piece of V rows
+//   P.V      VALU FMAs (the slow partial, fp32 caches and one-tile fast
+//            steps): lane l owns one 16-byte piece of V rows
 //            (l / PPR) + RPL * i, so every V load instruction reads whole
 //            rows contiguously; partial outputs are reduced across lanes once
-//            at the end.
+//            at the end.  The bf16 fast step runs P.V on MFMA instead
+//            (consume_pv_mfma).
 #include <math.h>
 
 #include <algorithm>
@@ -1019,7 +1026,8 @@ __global__ __launch_bounds__(kCombineThreads) void slow_combine_kernel(CombineAr
 }
 
 // ---------------------------------------------------------------------------
-// fast step: sparse attention over the support in chunks, then a merge kernel
+// fast step: sparse attention over the support in chunks, then the merge of
+// the chunk states (in the kernel or in a merge kernel)
 // ---------------------------------------------------------------------------
 struct SupportGeom {
   int ns_eff, w_lo, w_eff, cnt, size;

@@ -17,14 +17,20 @@
 //      select_clear, or by the slow step's partial kernel in the fused call)
 //   1. histogram of the top 12 key bits, added into a per-head global
 //      histogram (select_hist, or the slow step's combine in the fused call).
-//   2. select_gather: every workgroup finds the bin d1 holding K*, counts its
-//      keys above d1 and appends its keys in d1 to a per-head list (one
-//      atomic per workgroup reserves its range).
+//   2. select_gather: every workgroup finds the bin d1 holding K*, lists the
+//      positions of its keys above d1 (all of them are kept) with their count,
+//      and appends its keys in d1 to a per-head list (one atomic per workgroup
+//      reserves its range).
 //   3. select_emit: every workgroup resolves K* inside the list in LDS (by
 //      direct ranking when the list is short, else 12 bits per level), derives
 //      how many kept keys precede its chunk, and writes the kept positions of
-//      its chunk in ascending order from there.  If d1 holds more keys than
-//      fit in LDS, K* comes from radix passes over all candidates instead.
+//      its chunk (its listed keys above d1 and its list keys at or above K*)
+//      in ascending order from there; when the refresh also packs, it copies
+//      their K and V rows into the packed buffers at the same slots.  If d1
+//      holds more keys than fit in LDS, K* comes from radix passes over all
+//      candidates instead.
+//  With the optional key-norm prior, Soft-NMS or exclusivity, select_score
+//  first writes the final scores, and the steps above rank those.
 // Resolving K* redundantly in every emitting workgroup costs less than a
 // kernel boundary.  Workgroups never hand data to each other inside a
 // kernel: on gfx950 a device-scope fence writes back and invalidates the

@@ -2,8 +2,9 @@
 or 4 tiles of 16 rows; the library reads it once per process).  bf16 waves of
 2 and 4 tiles take the MFMA P.V path (one or two 32-row groups), 1 tile and
 fp32 the VALU path.  Each setting runs in a child process (one at a time) on
-ragged batches and is checked against the oracle; packed and gather must stay
-bit-identical."""
+ragged batches and is checked against the oracle; packed, gather and the
+packing fast step (all rows packing, or mixed with rows reading packed rows)
+must stay bit-identical."""
 import os
 import subprocess
 import sys
@@ -43,6 +44,20 @@ for dtype, D, G in ((torch.bfloat16, 128, 4), (torch.bfloat16, 64, 8), (torch.bf
     out_g = torch.full_like(out, 7.0)
     S.sfi_fast_step_packed(kv, sp, ids, q, pk, pv, cnt, out_p, ws)
     S.sfi_fast_step(kv, sp, ids, q, sel, cnt, out_g, ws)
+    # the packing fast step: every row packing into empty buffers, then rows
+    # that pack beside rows reading the packed rows (one mixed launch); outputs
+    # equal the gather step's and the packed rows the refresh's bit for bit
+    for flags in ([1, 1, 1, 1], [1, 0, 0, 1]):
+        pk2 = pk.clone() if 0 in flags else torch.full_like(pk, float("nan"))
+        pv2 = pv.clone() if 0 in flags else torch.full_like(pv, float("nan"))
+        out_k = torch.full_like(out, 7.0)
+        S.sfi_fast_step_pack(kv, sp, ids, q, sel, cnt, out_k, pk2, pv2, ws, pack_flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(out_k, out_g), (dtype, D, G, flags)
+        for b in ids:
+            for g in range(Hkv):
+                c = int(cnt[b, g])
+                assert torch.equal(pk2[b, g, :c], pk[b, g, :c]) and torch.equal(pv2[b, g, :c], pv[b, g, :c])
     torch.cuda.synchronize()
     assert torch.equal(out_p, out_g), (dtype, D, G)
     for b in ids:

@@ -580,8 +580,12 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   const int n_ab = a.chunk_above[h.bg * kSelMaxChunks + h.c];
   const uint64_t* glist = a.list + h.bg * kSelListCap;
   const int32_t* gabove = a.above_pos + h.bg * a.t_cap + i0;
-  const uint64_t first = glist[tid];  // always inside the list; used if tid < cnt_d1
-  const int ab_first = i0 + tid < i1 ? gabove[tid] : 0;
+  // The first kPre entries of the threshold bin's list and of this chunk's
+  // keys above the bin are loaded before their counts are known; more are
+  // rare (a 128K row: 120-230 keys in the bin, 40-250 above it per chunk).
+  constexpr int kPre = 256;
+  const uint64_t first = tid < kPre ? glist[tid] : 0ull;  // inside the list; used if tid < cnt_d1
+  const int ab_first = tid < kPre && i0 + tid < i1 ? gabove[tid] : 0;
   // keys above the threshold bin in the chunks before this one (this
   // thread's share)
   int above_before = 0;
@@ -593,10 +597,10 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
 
   if (a.chunk <= kStep && cnt_d1 <= kSelListCap && (!PACK || a.rows32)) {
     const int len = i1 - i0, nw = (len + 31) >> 5;
-    s_list[tid] = first;
-    for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
-    if (tid < n_ab) s_pos[tid] = ab_first;
-    for (int r = kSelThreads + tid; r < n_ab; r += kSelThreads) s_pos[r] = gabove[r];
+    if (tid < kPre) s_list[tid] = first;
+    for (int i = kPre + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
+    if (tid < kPre && tid < n_ab) s_pos[tid] = ab_first;
+    for (int r = kPre + tid; r < n_ab; r += kSelThreads) s_pos[r] = gabove[r];
     if (tid < kWords) s_bits[tid] = 0u;
     if (tid == 0) s_nlate = 0;
     __syncthreads();
@@ -723,12 +727,12 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   uint64_t key[kRun];
 #pragma unroll
   for (int u = 0; u < kRun; ++u) key[u] = key_of(sp, i0 + tid * kRun + u, fv[u]);
-  s_list[tid] = first;
+  if (tid < kPre) s_list[tid] = first;
   uint64_t kstar;
   int before;  // kept keys of the chunks before this one (this thread's share)
   if (cnt_d1 <= kSelListCap) {
     before = above_before;  // plus the threshold-bin keys at or above K* before the chunk
-    for (int i = kSelThreads + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
+    for (int i = kPre + tid; i < cnt_d1; i += kSelThreads) s_list[i] = glist[i];
     __syncthreads();
     kstar = cnt_d1 <= kSelThreads
                 ? rank_select(s_list, cnt_d1, need, reinterpret_cast<int*>(s_hist), &s_kstar)

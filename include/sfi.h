@@ -57,8 +57,8 @@
  *    call that needs them): SFI_FAST_TILES = 1, 2 or 4 (default 2) sets the
  *    fast steps' rows per wave to 16 times that value (R = 64, 128, 256);
  *    SFI_SLOW_TARGET_WGS (default 1024, at least 64) is the number of
- *    split-K workgroups the slow step aims at (with mass, splits keep 512 to
- *    1024 rows where the context allows).  Results stay within the same
+ *    split-K workgroups the slow step aims at (splits keep at least 512
+ *    rows, and with mass at most 1024, where the context allows).  Results stay within the same
  *    tolerances for every setting; the defaults measured fastest on MI355X.
  */
 #ifndef SFI_H_

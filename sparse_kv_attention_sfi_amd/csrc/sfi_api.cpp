@@ -443,12 +443,13 @@ void plan_slow(const sfi_kv_desc* desc, const int32_t* ids, int32_t cnt, const v
     t_max = std::max<int64_t>(t_max, desc->ctx_len_host[ids[i]]);
   }
   // at most kMaxMergeSlots splits per head (the merge stages them in LDS);
-  // with mass, splits of kSlowMassMinRows to kLogitBufRows rows where those
-  // limits allow: the partial kernel buffers each split's logits, and shorter
-  // splits (a 32K row aimed at 1024 workgroups gets 256) cost more per row
-  // than they gain in workgroups (28.7 against 31.6 us on a 32K layer)
-  int64_t want = ceil_div(rows, target);
-  if (with_mass) want = std::min<int64_t>(std::max<int64_t>(want, kSlowMassMinRows), kLogitBufRows);
+  // splits of at least kSlowMinRows rows: shorter ones (a 32K row aimed at
+  // 1024 workgroups gets 256) cost more per row than they gain in workgroups
+  // (28.7 against 31.6 us with mass on a 32K layer, 30.9 against 33.2 us
+  // without); with mass at most kLogitBufRows where that limit allows, so
+  // that the partial kernel can buffer each split's logits
+  int64_t want = std::max<int64_t>(ceil_div(rows, target), kSlowMinRows);
+  if (with_mass) want = std::min<int64_t>(want, kLogitBufRows);
   const int64_t per = std::max(want, ceil_div(t_max, kMaxMergeSlots));
   a.split_rows = static_cast<int32_t>(std::max<int64_t>(unit, ceil_div(per, unit) * unit));
   a.tab.n = cnt;

@@ -31,7 +31,7 @@ constexpr int kFastThreads = 256;    // 4 waves, fast-step kernels
 constexpr int kMaxMergeSlots = 512;  // partial slots per (sequence, head) a merge accepts
 constexpr int kSlowTargetWgs = 1024;  // slow partial workgroups aimed at per launch
 constexpr int kLogitBufRows = 1024;   // slow partial: a split's logits are buffered in LDS up to this size
-constexpr int kSlowMassMinRows = 512; // slow partial with mass: splits of at least this many rows where possible
+constexpr int kSlowMinRows = 512;     // slow partial: splits of at least this many rows where possible
 constexpr int kTicketStride = 32;     // fast-step chunk counters, one per 128-byte line
 constexpr uint32_t kOutOfRange = 0xFFFFFFFFu;  // a buffer offset past every buffer: loads give 0, stores drop
 
